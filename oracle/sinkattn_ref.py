@@ -1,0 +1,200 @@
+"""Plain fp64 CPU oracle for sink-aware masked attention (forward and backward).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+run this module: only the tests, the smoke check and the CPU-baseline leg of
+the benchmark do.  It shares no code with the HIP library; the only thing the
+two have in common is the seeded input generator module (``workloads.py``),
+which holds no attention arithmetic.
+
+Sources (cited by page title and section):
+  [SUM]  "Efficient Reinforcement Learning for Long-Horizon Tool-Use Agentic
+         Tasks" (summary page), paragraph on the sink-aware FlexAttention path:
+         the mask M = 1[k <= q] AND 1[q - k <= w OR k < p], the attention call
+         returning the output and an auxiliary log-sum-exp, and the sink
+         scaling alpha = sigmoid(l - s) with l = log sum_i exp(q . k_i).
+  [S5]   arXiv 2608.10357, section 5 "Sink-aware FlexAttention", paragraph
+         "Zero-value sink equivalence": the explicit-sink output
+         O_sink = (sum_i exp(q.k_i) v_i + exp(s) * 0) / (sum_i exp(q.k_i) + exp(s)).
+  [RETRO] "GPT-OSS Agentic RL training: a practical retrospective", section on
+         the FlashAttention v3 implementation: a backward pass that produces the
+         gradient of the loss with respect to each head's sink logit S_h.
+
+What is computed is the plain dense definition.  Everything is fp64, one
+(sequence, query head) at a time, with the full score matrix of that head
+formed explicitly (that is exactly what the GPU path must never do, and is
+fine here).  Readings where the pages leave a step open:
+  * scores are ``scale * q . k`` (the pages write q . k; scale = 1 is theirs);
+  * the log-sum-exp runs over the visible keys only and is the content-only
+    ``l`` (no sink term); natural log;
+  * ``q - k <= w`` is inclusive, ``k < p`` strict; positions are local to each
+    packed sequence; the q-head h reads kv-head h // group;
+  * one fp32 sink logit per query head, shared by all rows and sequences.
+
+Backward (not printed on the pages; it is the chain rule through [S5]'s
+softmax with one extra zero-valued column of logit s):
+  L_i   = logaddexp(l_i, s)           (log of the sink-inclusive normaliser)
+  P'_ij = exp(S_ij - L_i)             (sink-inclusive probabilities, = alpha_i P_ij)
+  D_i   = dO_i . O_i
+  dS_ij = P'_ij (dO_i . v_j - D_i)    (the sink column has value 0, so it only
+                                       enters through D_i)
+  dq_i  = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i,
+  dv_j  = sum_i P'_ij dO_i,        ds   = -sum_i exp(s - L_i) D_i      [RETRO]
+dk and dv of a kv-head are summed over the query heads that read it, and ds
+over every row of every sequence.
+"""
+from __future__ import annotations
+
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+
+def visible_mask(n: int, window: int, prefix: int) -> np.ndarray:
+    """M[i, j] for one sequence of n tokens ([SUM], mask function)."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    return (j <= i) & ((i - j <= window) | (j < prefix))
+
+
+def attend_head(q, k, v, sink: float, window: int, prefix: int, scale: float):
+    """Forward for one sequence and one query head.
+
+    q [n, d], k [n, d], v [n, d] (any float type, used in fp64).
+    Returns (o [n, d], l [n]) with o = sigmoid(l - s) * softmax(S) v   ([SUM]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n = q.shape[0]
+    if n == 0:
+        return np.zeros_like(q), np.zeros((0,), np.float64)
+    m = visible_mask(n, window, prefix)
+    s_mat = scale * (q @ k.T)
+    s_mat = np.where(m, s_mat, -np.inf)
+    rowmax = s_mat.max(axis=1)
+    e = np.exp(s_mat - rowmax[:, None])
+    z = e.sum(axis=1)
+    l = rowmax + np.log(z)                       # content-only log-sum-exp
+    o_bar = (e @ v) / z[:, None]                 # plain masked softmax attention
+    alpha = 1.0 / (1.0 + np.exp(np.float64(sink) - l))   # sigmoid(l - s)
+    return alpha[:, None] * o_bar, l
+
+
+def attend_head_grad(q, k, v, sink: float, window: int, prefix: int, scale: float, do):
+    """Backward for one sequence and one query head.
+
+    Recomputes the forward, then applies the chain rule written in the module
+    docstring.  Returns (dq [n, d], dk [n, d], dv [n, d], dsink float).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n = q.shape[0]
+    if n == 0:
+        z = np.zeros_like(q)
+        return z, z.copy(), z.copy(), 0.0
+    o, l = attend_head(q, k, v, sink, window, prefix, scale)
+    m = visible_mask(n, window, prefix)
+    s_mat = np.where(m, scale * (q @ k.T), -np.inf)
+    big_l = np.logaddexp(l, np.float64(sink))
+    p_prime = np.exp(s_mat - big_l[:, None])     # 0 where masked
+    d_row = np.sum(do * o, axis=1)
+    dp = do @ v.T
+    ds_mat = p_prime * (dp - d_row[:, None])
+    dq = scale * (ds_mat @ k)
+    dk = scale * (ds_mat.T @ q)
+    dv = p_prime.T @ do
+    dsink = -float(np.sum(np.exp(np.float64(sink) - big_l) * d_row))
+    return dq, dk, dv, dsink
+
+
+def _sequences(q, cu_seqlens):
+    """Yield (batch_index_or_None, row_slice) for each sequence."""
+    if cu_seqlens is None:
+        for b in range(q.shape[0]):
+            yield b, slice(None)
+    else:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        for s in range(len(cu) - 1):
+            yield None, slice(int(cu[s]), int(cu[s + 1]))
+
+
+def _pick(x, b, rows, h):
+    return x[b, :, h, :] if b is not None else x[rows, h, :]
+
+
+def forward(q, k, v, sinks, window: int, prefix: int, scale: float,
+            cu_seqlens=None, heads: Optional[Iterable[int]] = None):
+    """Whole-call forward.
+
+    q [B,T,Hq,d] (or [N,Hq,d] with cu_seqlens int[G+1]); k, v [B,T,Hkv,d]
+    (or [N,Hkv,d]); sinks [Hq].  Returns (o like q, lse [B,Hq,T] or [Hq,N]),
+    fp64.  ``heads`` restricts the work to some query heads (the others are
+    left NaN), for spot checks at full size.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    sinks = np.asarray(sinks, dtype=np.float64)
+    hq = q.shape[-2]
+    group = hq // k.shape[-2]
+    heads = list(range(hq)) if heads is None else list(heads)
+    o = np.full(q.shape, np.nan, np.float64)
+    if cu_seqlens is None:
+        lse = np.full((q.shape[0], hq, q.shape[1]), np.nan, np.float64)
+    else:
+        lse = np.full((hq, q.shape[0]), np.nan, np.float64)
+    for b, rows in _sequences(q, cu_seqlens):
+        for h in heads:
+            oh, lh = attend_head(_pick(q, b, rows, h), _pick(k, b, rows, h // group),
+                                 _pick(v, b, rows, h // group), sinks[h], window,
+                                 prefix, scale)
+            if b is not None:
+                o[b, :, h, :] = oh
+                lse[b, h, :] = lh
+            else:
+                o[rows, h, :] = oh
+                lse[h, rows] = lh
+    return o, lse
+
+
+def backward(q, k, v, sinks, do, window: int, prefix: int, scale: float,
+             cu_seqlens=None, heads: Optional[Sequence[int]] = None):
+    """Whole-call backward.  Returns (dq, dk, dv, dsinks), fp64.
+
+    dk, dv of a kv-head sum the contributions of every query head in
+    ``heads`` that reads it (complete only when ``heads`` covers the group);
+    dsinks[h] sums over all rows of all sequences.  Heads left out are NaN in
+    dq and dsinks.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    do = np.asarray(do)
+    sinks = np.asarray(sinks, dtype=np.float64)
+    hq = q.shape[-2]
+    group = hq // k.shape[-2]
+    heads = list(range(hq)) if heads is None else list(heads)
+    dq = np.full(q.shape, np.nan, np.float64)
+    dk = np.zeros(k.shape, np.float64)
+    dv = np.zeros(v.shape, np.float64)
+    dsinks = np.full((hq,), np.nan, np.float64)
+    for h in heads:
+        dsinks[h] = 0.0
+    for b, rows in _sequences(q, cu_seqlens):
+        for h in heads:
+            kv = h // group
+            g_q, g_k, g_v, g_s = attend_head_grad(
+                _pick(q, b, rows, h), _pick(k, b, rows, kv), _pick(v, b, rows, kv),
+                sinks[h], window, prefix, scale, _pick(do, b, rows, h))
+            if b is not None:
+                dq[b, :, h, :] = g_q
+                dk[b, :, kv, :] += g_k
+                dv[b, :, kv, :] += g_v
+            else:
+                dq[rows, h, :] = g_q
+                dk[rows, kv, :] += g_k
+                dv[rows, kv, :] += g_v
+            dsinks[h] += g_s
+    return dq, dk, dv, dsinks

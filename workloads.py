@@ -1,0 +1,172 @@
+"""Seeded synthetic inputs for sink-aware masked attention.
+
+This module holds no attention arithmetic.  It only names the workloads and
+draws their tensors, so that the fp64 oracle (``oracle/``) and the HIP path
+(``sink_aware_masked_sinkattn_amd``) can be fed the very same values without
+sharing any code of the method itself.
+
+Recipe (the same for every workload):
+  * one ``torch.Generator`` (CPU) per workload, seeded with ``1000 + index``;
+  * draws in this order per layer: Q, K, V, dO (each ``std * N(0, 1)`` in fp32),
+    then the per-head sink logits ``s_h ~ N(0, 1)`` (fp32);
+  * for bf16 workloads Q, K, V and dO are rounded once to bf16 (round to
+    nearest even, torch's ``.to(torch.bfloat16)``); sinks stay fp32;
+  * varlen workloads draw their G sequence lengths first, uniform on the
+    closed range [lo, hi], and pack the sequences back to back
+    (``cu_seqlens`` is the exclusive prefix sum of the lengths).
+
+Layouts: Q, O, dO ``[B, T, Hq, d]`` (varlen ``[N, Hq, d]``); K, V
+``[B, T, Hkv, d]`` (varlen ``[N, Hkv, d]``); sinks ``[Hq]``.  The q-head ``h``
+reads kv-head ``h // (Hq // Hkv)``.
+
+The shapes follow the attention layers of the workloads described for the
+SinkFlex-RL method (64 query heads, 8 kv heads, head dim 64, alternating
+128-token sliding-window and full-causal layers, GRPO groups of rollouts of
+1k-8k tokens).  The pages measure on tau^2-Bench retail trajectories with an
+unnamed MoE model; neither is available, so these seeded draws stand in for
+their attention inputs.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import torch
+
+# Window value meaning "no window limit" (plain causal plus prefix).  The C
+# ABI uses the same value (INT32_MAX).
+WINDOW_INF = 2**31 - 1
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int                      # seed = 1000 + index
+    dtype: str                      # "bf16" or "fp32"
+    batch: int                      # B (ignored for varlen)
+    seqlen: int                     # T (max length for varlen)
+    heads_q: int
+    heads_kv: int
+    head_dim: int
+    std: float                      # Q, K, V, dO ~ std * N(0, 1)
+    layers: Tuple[Tuple[int, int], ...]   # (window, prefix) per layer
+    varlen: Optional[Tuple[int, int, int]] = None  # (G, lo, hi)
+
+    @property
+    def group(self) -> int:
+        return self.heads_q // self.heads_kv
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_fp32", 0, "fp32", 1, 128, 2, 2, 32, 1.0, ((16, 4),)),
+        Workload("gqa_swa_4096", 1, "bf16", 1, 4096, 64, 8, 64, 0.5, ((128, 0),)),
+        Workload("gqa_causal_4096", 2, "bf16", 1, 4096, 64, 8, 64, 0.5, ((WINDOW_INF, 0),)),
+        Workload("long_8192", 3, "bf16", 1, 8192, 64, 8, 64, 0.5,
+                 ((128, 4), (WINDOW_INF, 0))),
+        Workload("varlen_grpo_g8", 4, "bf16", 1, 8192, 64, 8, 64, 0.5, ((128, 16),),
+                 varlen=(8, 1024, 8192)),
+    ]
+}
+
+
+@dataclass
+class Inputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    do: torch.Tensor
+    sinks: torch.Tensor
+    window: int
+    prefix: int
+    scale: float
+    group: int
+    cu_seqlens: Optional[torch.Tensor] = None   # int32 [G+1] or None
+    lengths: Optional[Tuple[int, ...]] = None
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def max_seqlen(self) -> int:
+        if self.lengths is not None:
+            return max(self.lengths) if self.lengths else 0
+        return self.q.shape[1]
+
+
+def _storage(dtype: str) -> torch.dtype:
+    return {"bf16": torch.bfloat16, "fp32": torch.float32}[dtype]
+
+
+def draw(gen: torch.Generator, shape, std: float, dtype: str) -> torch.Tensor:
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32) * std
+    return x.to(_storage(dtype))
+
+
+def draw_lengths(gen: torch.Generator, count: int, lo: int, hi: int) -> Tuple[int, ...]:
+    return tuple(int(x) for x in torch.randint(lo, hi + 1, (count,), generator=gen))
+
+
+def make_inputs(*, batch: int, seqlen: int, heads_q: int, heads_kv: int, head_dim: int,
+                window: int, prefix: int, seed: int, std: float = 1.0,
+                dtype: str = "bf16", lengths: Optional[Tuple[int, ...]] = None,
+                sink_values: Optional[Tuple[float, ...]] = None,
+                gen: Optional[torch.Generator] = None) -> Inputs:
+    """Draw one attention call's inputs.
+
+    ``lengths`` given means varlen packing (``batch``/``seqlen`` ignored).
+    ``sink_values`` overrides the drawn sinks (edge cases such as -inf).
+    """
+    if gen is None:
+        gen = torch.Generator().manual_seed(seed)
+    if lengths is not None:
+        n = int(sum(lengths))
+        qs, ks = (n, heads_q, head_dim), (n, heads_kv, head_dim)
+    else:
+        qs = (batch, seqlen, heads_q, head_dim)
+        ks = (batch, seqlen, heads_kv, head_dim)
+    q = draw(gen, qs, std, dtype)
+    k = draw(gen, ks, std, dtype)
+    v = draw(gen, ks, std, dtype)
+    do = draw(gen, qs, std, dtype)
+    sinks = torch.randn(heads_q, generator=gen, dtype=torch.float32)
+    if sink_values is not None:
+        sinks = torch.tensor(sink_values, dtype=torch.float32)
+        assert sinks.numel() == heads_q
+    cu = None
+    if lengths is not None:
+        offs = [0]
+        for L in lengths:
+            offs.append(offs[-1] + int(L))
+        cu = torch.tensor(offs, dtype=torch.int32)
+    return Inputs(q=q, k=k, v=v, do=do, sinks=sinks, window=int(window),
+                  prefix=int(prefix), scale=1.0 / math.sqrt(head_dim),
+                  group=heads_q // heads_kv, cu_seqlens=cu,
+                  lengths=tuple(int(x) for x in lengths) if lengths is not None else None,
+                  meta={"seed": seed, "std": std, "dtype": dtype})
+
+
+def workload_inputs(name: str) -> list:
+    """All layers' inputs of a named workload, drawn from its own generator."""
+    wl = WORKLOADS[name]
+    gen = torch.Generator().manual_seed(wl.seed)
+    lengths = None
+    if wl.varlen is not None:
+        g, lo, hi = wl.varlen
+        lengths = draw_lengths(gen, g, lo, hi)
+    out = []
+    for (w, p) in wl.layers:
+        out.append(make_inputs(batch=wl.batch, seqlen=wl.seqlen, heads_q=wl.heads_q,
+                               heads_kv=wl.heads_kv, head_dim=wl.head_dim, window=w,
+                               prefix=p, seed=wl.seed, std=wl.std, dtype=wl.dtype,
+                               lengths=lengths, gen=gen))
+        out[-1].meta["workload"] = name
+    return out
