@@ -1,0 +1,148 @@
+/*
+ * sinkattn.h -- C ABI of a gfx950 (MI355X) library for exact sink-aware
+ * masked attention, forward and backward.
+ *
+ * What it computes (sources cited by page title and section):
+ *
+ *   Mask.  M[q,k] = 1[k <= q] AND 1[q - k <= w OR k < p]: causal, limited to a
+ *   local window of w keys behind the query, except that the first p keys of
+ *   the sequence stay visible to every later query.  ("Efficient
+ *   Reinforcement Learning for Long-Horizon Tool-Use Agentic Tasks", summary
+ *   page, paragraph on the sink-aware FlexAttention path.)  The window test
+ *   is inclusive (a query sees w + 1 window keys including itself), the
+ *   prefix test strict.  Positions are local to each sequence.
+ *
+ *   Forward.  With S[q,k] = softmax_scale * (q . k) over visible keys,
+ *   l[q] = log sum_k exp(S[q,k]) (natural log, content keys only) and
+ *   O[q] = sigmoid(l[q] - s_h) * sum_k softmax_k(S[q,:]) v_k,
+ *   which equals attention with one extra key of logit s_h and value 0
+ *   (arXiv 2608.10357, section 5 "Sink-aware FlexAttention", paragraph
+ *   "Zero-value sink equivalence").  One learned sink logit s_h per query
+ *   head.  The call returns O and l (same summary-page paragraph: the
+ *   attention call returns the output and an auxiliary log-sum-exp).
+ *
+ *   Backward.  Given dO, returns dQ, dK, dV and dL/ds_h (the per-head sink
+ *   gradient of "GPT-OSS Agentic RL training: a practical retrospective",
+ *   section on the FlashAttention v3 implementation).  With
+ *   L = logaddexp(l, s_h), P' = exp(S - L), D = rowsum(dO * O):
+ *     dS = P' * (dO V^T - D),  dQ = scale dS K,  dK = scale dS^T Q,
+ *     dV = P'^T dO,            ds_h = -sum_rows exp(s_h - L) D.
+ *   dK and dV of a kv-head are summed over the query heads that read it;
+ *   ds_h is summed over every row of every sequence.  No O(T^2) buffer is
+ *   ever formed.
+ *
+ * Tensor layouts (all contiguous, last dimension unit-stride, row-major):
+ *   fixed length (cu_seqlens == NULL)      varlen (cu_seqlens != NULL)
+ *   q, o, dout, dq : [B, T, Hq, d]          [N, Hq, d]
+ *   k, v, dk, dv   : [B, T, Hkv, d]         [N, Hkv, d]
+ *   lse            : [B, Hq, T]  fp32       [Hq, N]  fp32
+ *   sinks, dsinks  : [Hq]        fp32       [Hq]     fp32
+ * Element type of q, k, v, o, dout, dq, dk, dv: problem.dtype (bf16 or fp32).
+ * Query head h reads kv head h / (Hq / Hkv) (contiguous groups).
+ *
+ * Conventions:
+ *   - Every pointer argument is a DEVICE pointer, except `problem` (host).
+ *     The caller owns all memory; the library allocates none.
+ *   - Every tensor pointer must be 16-byte aligned (SINKATTN_ERR_MISALIGNED).
+ *   - All argument checks run on the host before any HIP call, so an invalid
+ *     call returns an error status without touching the device.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  No call synchronises.  A launch failure is reported as
+ *     SINKATTN_ERR_HIP.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - cu_seqlens contents are a caller contract, not checked: cu[0] = 0,
+ *     non-decreasing, cu[batch] = total_tokens, every length <= seqlen.
+ *   - No global mutable state: concurrent calls on different streams are safe.
+ *   - Results of the backward are not bitwise reproducible run to run (float
+ *     atomics in dQ and ds_h); they are reproducible to rounding.
+ */
+#ifndef SINKATTN_H
+#define SINKATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SINKATTN_OK = 0,
+  SINKATTN_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  SINKATTN_ERR_BAD_SHAPE = 2,    /* negative size, Hq % Hkv != 0, N < 0 ... */
+  SINKATTN_ERR_BAD_MASK = 3,     /* window < 0 or prefix < 0 */
+  SINKATTN_ERR_UNSUPPORTED = 4,  /* dtype / head_dim combination not built */
+  SINKATTN_ERR_MISALIGNED = 5,   /* a tensor pointer is not 16-byte aligned */
+  SINKATTN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than required */
+  SINKATTN_ERR_HIP = 7           /* a HIP runtime call or launch failed */
+} sinkattn_status;
+
+typedef enum { SINKATTN_BF16 = 0, SINKATTN_FP32 = 1 } sinkattn_dtype;
+
+/* window value meaning "no window limit": plain causal (plus prefix) */
+#define SINKATTN_WINDOW_INF INT32_MAX
+
+typedef struct {
+  int32_t dtype;         /* sinkattn_dtype of q, k, v, o, dout, dq, dk, dv */
+  int32_t batch;         /* B; or G, the number of packed sequences, if cu_seqlens */
+  int32_t seqlen;        /* T; or the maximum sequence length, if cu_seqlens */
+  int32_t total_tokens;  /* N, rows of the packed tensors, if cu_seqlens; else ignored */
+  int32_t heads_q;       /* Hq >= 1 */
+  int32_t heads_kv;      /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;      /* d: 64 for bf16; 32 or 64 for fp32 */
+  int32_t window;        /* w >= 0, or SINKATTN_WINDOW_INF */
+  int32_t prefix;        /* p >= 0 */
+  float softmax_scale;   /* scale on q . k (1/sqrt(d) in the usual setting) */
+  const int32_t *cu_seqlens; /* device int32[batch + 1], or NULL (fixed length) */
+} sinkattn_problem;
+
+/*
+ * Forward.  Reads q, k, v, sinks; writes o and (if lse != NULL) lse.
+ * lse may be NULL when no backward will follow (inference).
+ */
+sinkattn_status sinkattn_fwd(const sinkattn_problem *problem, const void *q,
+                             const void *k, const void *v, const float *sinks,
+                             void *o, float *lse, void *stream);
+
+/* Bytes of device workspace sinkattn_bwd needs for `problem` (0 if invalid). */
+size_t sinkattn_bwd_workspace_size(const sinkattn_problem *problem);
+
+/*
+ * Backward.  Reads q, k, v, sinks, o and lse (both exactly as written by
+ * sinkattn_fwd for the same inputs) and dout; writes dq, dk, dv and dsinks.
+ * `workspace` is caller-owned device memory of at least
+ * sinkattn_bwd_workspace_size(problem) bytes, 256-byte aligned; its contents
+ * on entry do not matter and on return are unspecified.
+ */
+sinkattn_status sinkattn_bwd(const sinkattn_problem *problem, const void *q,
+                             const void *k, const void *v, const float *sinks,
+                             const void *o, const float *lse, const void *dout,
+                             void *dq, void *dk, void *dv, float *dsinks,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *sinkattn_status_string(sinkattn_status status);
+
+/*
+ * Host-only helpers exposing the tile schedule the kernels use, so it can be
+ * checked against brute-force enumeration of the mask without a GPU.
+ *
+ * sinkattn_tile_class: for query rows [q0, q1] and key columns [k0, k1]
+ * (inclusive, positions local to one sequence) returns 0 if no (q, k) pair
+ * in the block is visible, 1 if every pair is visible, 2 otherwise.
+ *
+ * sinkattn_key_tile_segments: the key tiles of width block_k that query rows
+ * [q0, q1] must visit, as at most two half-open tile-index ranges written to
+ * out[0..3] (begin0, end0, begin1, end1).  Returns the number of ranges.
+ * Every tile holding a visible pair is listed exactly once.
+ */
+int32_t sinkattn_tile_class(int32_t q0, int32_t q1, int32_t k0, int32_t k1,
+                            int32_t window, int32_t prefix);
+int32_t sinkattn_key_tile_segments(int32_t q0, int32_t q1, int32_t window,
+                                   int32_t prefix, int32_t block_k, int32_t *out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKATTN_H */

@@ -1,0 +1,14 @@
+"""Sink-aware masked attention for MI355X (gfx950): forward and backward.
+
+The computation lives in ``libsinkattn.so`` (hand-written HIP kernels behind
+the C ABI of ``include/sinkattn.h``); this package only binds it.
+"""
+from .binding import (WINDOW_INF, Problem, SinkAttnError, load_library, make_problem,
+                      sinkattn_bwd, sinkattn_bwd_workspace_size, sinkattn_fwd,
+                      sinkattn_key_tile_segments, sinkattn_tile_class)
+
+__all__ = [
+    "WINDOW_INF", "Problem", "SinkAttnError", "load_library", "make_problem",
+    "sinkattn_fwd", "sinkattn_bwd", "sinkattn_bwd_workspace_size",
+    "sinkattn_tile_class", "sinkattn_key_tile_segments",
+]

@@ -1,0 +1,239 @@
+// C ABI of the sink-aware masked attention library (declared in
+// include/sinkattn.h): argument validation (host only, before any HIP call),
+// workspace layout, and dispatch to the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/sinkattn.h"
+#include "mask_tiles.h"
+
+typedef __bf16 bf16;
+
+hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const float* sinks,
+                               bf16* o, float* lse, const int* cu_seqlens, int batch, int seqlen,
+                               int total_tokens, int heads_q, int heads_kv, int window,
+                               int prefix, float scale, hipStream_t stream);
+hipError_t launch_bwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
+                               const float* l_ws, const float* d_ws, float* dq_acc, float* dk_acc,
+                               float* dv_acc, const int* cu_seqlens, int batch, int seqlen,
+                               int rows_total, int heads_q, int heads_kv, int window, int prefix,
+                               float scale, int heads_per_wg, hipStream_t stream);
+hipError_t launch_fwd_f32(int head_dim, const float* q, const float* k, const float* v,
+                          const float* sinks, float* o, float* lse, const int* cu_seqlens,
+                          int batch, int seqlen, int total_tokens, int heads_q, int heads_kv,
+                          int window, int prefix, float scale, hipStream_t stream);
+hipError_t launch_bwd_f32(int head_dim, const float* q, const float* k, const float* v,
+                          const float* dout, const float* l_ws, const float* d_ws, float* dq,
+                          float* dk, float* dv, const int* cu_seqlens, int batch, int seqlen,
+                          int total_tokens, int heads_q, int heads_kv, int window, int prefix,
+                          float scale, hipStream_t stream);
+hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const void* dout,
+                          const float* lse, const float* sinks, const int* cu_seqlens,
+                          float* dsinks, float* d_ws, float* l_ws, float* dq_acc, float* dk_acc,
+                          float* dv_acc, int batch, int seqlen, int rows_total, int heads_q,
+                          int heads_kv, int lse_head_stride, hipStream_t stream);
+hipError_t launch_convert(int dtype_is_f32, const float* dq_acc, const float* dk_acc,
+                          const float* dv_acc, void* dq, void* dk, void* dv, long long n_q,
+                          long long n_kv, float scale, hipStream_t stream);
+hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Dims {
+  long long rows;      // B*T or N
+  bool varlen;
+};
+
+// Shape / mask / dtype checks shared by fwd and bwd.  No HIP calls.
+sinkattn_status check_problem(const sinkattn_problem* pb, Dims* dims) {
+  if (!pb) return SINKATTN_ERR_NULL_POINTER;
+  if (pb->dtype != SINKATTN_BF16 && pb->dtype != SINKATTN_FP32) return SINKATTN_ERR_UNSUPPORTED;
+  if (pb->batch < 0 || pb->seqlen < 0 || pb->heads_q <= 0 || pb->heads_kv <= 0 ||
+      pb->head_dim <= 0)
+    return SINKATTN_ERR_BAD_SHAPE;
+  if (pb->heads_q % pb->heads_kv != 0) return SINKATTN_ERR_BAD_SHAPE;
+  if (pb->window < 0 || pb->prefix < 0) return SINKATTN_ERR_BAD_MASK;
+  if (pb->dtype == SINKATTN_BF16 && pb->head_dim != 64) return SINKATTN_ERR_UNSUPPORTED;
+  if (pb->dtype == SINKATTN_FP32 && pb->head_dim != 32 && pb->head_dim != 64)
+    return SINKATTN_ERR_UNSUPPORTED;
+  if (!(pb->softmax_scale > 0.0f) || pb->softmax_scale > 1.0e30f) return SINKATTN_ERR_BAD_SHAPE;
+  dims->varlen = pb->cu_seqlens != nullptr;
+  if (dims->varlen) {
+    if (pb->total_tokens < 0) return SINKATTN_ERR_BAD_SHAPE;
+    if (pb->batch > 0 && pb->seqlen == 0 && pb->total_tokens > 0) return SINKATTN_ERR_BAD_SHAPE;
+    dims->rows = pb->total_tokens;
+  } else {
+    dims->rows = (long long)pb->batch * pb->seqlen;
+  }
+  // 32-bit element offsets are used for row * stride products inside kernels
+  // only after widening to size_t; the per-row element count must fit int.
+  if ((long long)pb->heads_q * pb->head_dim > (1LL << 30)) return SINKATTN_ERR_BAD_SHAPE;
+  if (dims->rows > (1LL << 31) - 1) return SINKATTN_ERR_BAD_SHAPE;
+  return SINKATTN_OK;
+}
+
+struct Workspace {
+  size_t d_off, l_off, dq_off, dk_off, dv_off, total;
+};
+
+Workspace workspace_layout(const sinkattn_problem* pb, const Dims& dims) {
+  Workspace w;
+  const size_t rows = (size_t)dims.rows;
+  const size_t stat = round_up(rows * (size_t)pb->heads_q * sizeof(float));
+  const bool accum = pb->dtype == SINKATTN_BF16;   // fp32 path writes outputs directly
+  const size_t qacc = accum ? round_up(rows * pb->heads_q * pb->head_dim * sizeof(float)) : 0;
+  const size_t kvacc = accum ? round_up(rows * pb->heads_kv * pb->head_dim * sizeof(float)) : 0;
+  w.d_off = 0;
+  w.l_off = stat;
+  w.dq_off = 2 * stat;
+  w.dk_off = w.dq_off + qacc;
+  w.dv_off = w.dk_off + kvacc;
+  w.total = w.dv_off + kvacc;
+  return w;
+}
+
+sinkattn_status hip_status(hipError_t e) { return e == hipSuccess ? SINKATTN_OK : SINKATTN_ERR_HIP; }
+
+// query heads per backward workgroup: the whole GQA group unless that leaves
+// too few workgroups to fill the chip
+int choose_heads_per_wg(const sinkattn_problem* pb) {
+  const int group = pb->heads_q / pb->heads_kv;
+  const long long kblocks = ((long long)pb->seqlen + 127) / 128;
+  int hpw = group;
+  while (hpw > 1 && (hpw % 2 == 0) &&
+         (long long)pb->batch * pb->heads_kv * (group / hpw) * kblocks < 2048)
+    hpw /= 2;
+  return hpw;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sinkattn_status_string(sinkattn_status s) {
+  switch (s) {
+    case SINKATTN_OK: return "ok";
+    case SINKATTN_ERR_NULL_POINTER: return "null pointer argument";
+    case SINKATTN_ERR_BAD_SHAPE: return "invalid shape";
+    case SINKATTN_ERR_BAD_MASK: return "invalid mask parameters (window and prefix must be >= 0)";
+    case SINKATTN_ERR_UNSUPPORTED: return "unsupported dtype / head_dim combination";
+    case SINKATTN_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
+    case SINKATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case SINKATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t sinkattn_tile_class(int32_t q0, int32_t q1, int32_t k0, int32_t k1, int32_t window,
+                            int32_t prefix) {
+  return sa_tile_class(q0, q1, k0, k1, window, prefix);
+}
+
+int32_t sinkattn_key_tile_segments(int32_t q0, int32_t q1, int32_t window, int32_t prefix,
+                                   int32_t block_k, int32_t* out) {
+  if (!out || block_k <= 0 || q0 < 0 || q1 < q0 || window < 0 || prefix < 0) return -1;
+  int tmp[4];
+  const int n = sa_key_tile_segments(q0, q1, window, prefix, block_k, tmp);
+  for (int i = 0; i < 4; ++i) out[i] = tmp[i];
+  return n;
+}
+
+size_t sinkattn_bwd_workspace_size(const sinkattn_problem* pb) {
+  Dims dims;
+  if (check_problem(pb, &dims) != SINKATTN_OK) return 0;
+  return workspace_layout(pb, dims).total;
+}
+
+sinkattn_status sinkattn_fwd(const sinkattn_problem* pb, const void* q, const void* k,
+                             const void* v, const float* sinks, void* o, float* lse,
+                             void* stream) {
+  Dims dims;
+  sinkattn_status st = check_problem(pb, &dims);
+  if (st != SINKATTN_OK) return st;
+  if (dims.rows == 0 || pb->batch == 0) return SINKATTN_OK;
+  if (!q || !k || !v || !sinks || !o) return SINKATTN_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned16(lse)) || !aligned16(sinks))
+    return SINKATTN_ERR_MISALIGNED;
+  const int window = pb->window > pb->seqlen ? pb->seqlen : pb->window;   // same mask
+  const int prefix = pb->prefix > pb->seqlen ? pb->seqlen : pb->prefix;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pb->dtype == SINKATTN_BF16) {
+    return hip_status(launch_fwd_bf16_d64(
+        (const bf16*)q, (const bf16*)k, (const bf16*)v, sinks, (bf16*)o, lse, pb->cu_seqlens,
+        pb->batch, pb->seqlen, (int)dims.rows, pb->heads_q, pb->heads_kv, window, prefix,
+        pb->softmax_scale, s));
+  }
+  return hip_status(launch_fwd_f32(pb->head_dim, (const float*)q, (const float*)k,
+                                   (const float*)v, sinks, (float*)o, lse, pb->cu_seqlens,
+                                   pb->batch, pb->seqlen, (int)dims.rows, pb->heads_q,
+                                   pb->heads_kv, window, prefix, pb->softmax_scale, s));
+}
+
+sinkattn_status sinkattn_bwd(const sinkattn_problem* pb, const void* q, const void* k,
+                             const void* v, const float* sinks, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, float* dsinks,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  Dims dims;
+  sinkattn_status st = check_problem(pb, &dims);
+  if (st != SINKATTN_OK) return st;
+  if (!sinks || !dsinks) return SINKATTN_ERR_NULL_POINTER;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool empty = dims.rows == 0 || pb->batch == 0;
+  if (!empty) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+      return SINKATTN_ERR_NULL_POINTER;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        !aligned16(sinks) || !aligned16(dsinks))
+      return SINKATTN_ERR_MISALIGNED;
+    const Workspace wl = workspace_layout(pb, dims);
+    if (!workspace || workspace_bytes < wl.total) return SINKATTN_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SINKATTN_ERR_MISALIGNED;
+  }
+  // ---- validation done; device work from here on
+  hipError_t e = launch_zero_f32(dsinks, pb->heads_q, s);
+  if (e != hipSuccess || empty) return hip_status(e);
+  const Workspace wl = workspace_layout(pb, dims);
+  char* ws = static_cast<char*>(workspace);
+  float* d_ws = (float*)(ws + wl.d_off);
+  float* l_ws = (float*)(ws + wl.l_off);
+  const bool is_f32 = pb->dtype == SINKATTN_FP32;
+  float* dq_acc = is_f32 ? nullptr : (float*)(ws + wl.dq_off);
+  float* dk_acc = is_f32 ? nullptr : (float*)(ws + wl.dk_off);
+  float* dv_acc = is_f32 ? nullptr : (float*)(ws + wl.dv_off);
+  const int window = pb->window > pb->seqlen ? pb->seqlen : pb->window;
+  const int prefix = pb->prefix > pb->seqlen ? pb->seqlen : pb->prefix;
+  const int rows = (int)dims.rows;
+  const int lse_stride = dims.varlen ? rows : pb->seqlen;
+  e = launch_bwd_pre(is_f32, pb->head_dim, o, dout, lse, sinks, pb->cu_seqlens, dsinks, d_ws, l_ws,
+                     dq_acc, dk_acc, dv_acc, pb->batch, pb->seqlen, rows, pb->heads_q,
+                     pb->heads_kv, lse_stride, s);
+  if (e != hipSuccess) return hip_status(e);
+  if (is_f32) {
+    return hip_status(launch_bwd_f32(pb->head_dim, (const float*)q, (const float*)k,
+                                     (const float*)v, (const float*)dout, l_ws, d_ws, (float*)dq,
+                                     (float*)dk, (float*)dv, pb->cu_seqlens, pb->batch,
+                                     pb->seqlen, rows, pb->heads_q, pb->heads_kv, window, prefix,
+                                     pb->softmax_scale, s));
+  }
+  e = launch_bwd_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, l_ws,
+                          d_ws, dq_acc, dk_acc, dv_acc, pb->cu_seqlens, pb->batch, pb->seqlen,
+                          rows, pb->heads_q, pb->heads_kv, window, prefix, pb->softmax_scale,
+                          choose_heads_per_wg(pb), s);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_convert(0, dq_acc, dk_acc, dv_acc, dq, dk, dv,
+                                   (long long)rows * pb->heads_q * pb->head_dim,
+                                   (long long)rows * pb->heads_kv * pb->head_dim,
+                                   pb->softmax_scale, s));
+}
+
+}  // extern "C"

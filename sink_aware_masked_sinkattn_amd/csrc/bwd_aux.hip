@@ -1,0 +1,198 @@
+// Backward helpers around the main kernel: the row preprocessing pass and the
+// accumulator conversion pass.  Both are HBM-bound streaming kernels.
+//
+// Preprocessing, per (row i, query head h) -- the sink gradient of "GPT-OSS
+// Agentic RL training: a practical retrospective" (FlashAttention v3
+// implementation section), written out with the sink as a zero-value key
+// (arXiv 2608.10357, section 5):
+//   D_i = sum_c dO_ic O_ic
+//   L_i = logaddexp(l_i, s_h)                (sink-inclusive log-normaliser)
+//   ds_h -= exp(s_h - L_i) D_i               (summed over all rows)
+// D and L go to the workspace for the main kernel.  The ds_h partial sums of
+// a wave are reduced with cross-lane shuffles, then added with one float
+// atomic per wave.  The same pass zeroes the fp32 accumulators of dQ (and,
+// from the first query head of each group, of dK and dV), so no separate
+// memset is needed.
+#include "common.h"
+
+namespace {
+
+// 16 bytes of a row per lane: lanes-per-row = D / (16 / sizeof(T)).
+template <typename T, int D>
+struct RowSplit {
+  static constexpr int kElems = 16 / (int)sizeof(T);
+  static constexpr int kLanesPerRow = D / kElems;
+  static constexpr int kRowsPerPass = 64 / kLanesPerRow;
+};
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+struct PreArgs {
+  const void* o;
+  const void* dout;
+  const float* lse;
+  const float* sinks;
+  const int* cu_seqlens;
+  float* dsinks;
+  float* d_ws;        // [Hq, rows] : D_i
+  float* l_ws;        // [Hq, rows] : L_i (natural log)
+  float* dq_acc;      // [rows, Hq, D] fp32, zeroed here (may be null)
+  float* dk_acc;      // [rows, Hkv, D] fp32, zeroed here (may be null)
+  float* dv_acc;
+  int seqlen, heads_q, heads_kv, group, rows_total;
+  int lse_head_stride;
+  int rows_per_wave;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void sinkattn_bwd_pre(PreArgs a) {
+  using RS = RowSplit<T, D>;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + wave;
+  if (h >= a.heads_q) return;
+  const int z = blockIdx.z;
+  const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
+  const int r_begin = blockIdx.x * a.rows_per_wave;
+  const int r_end = min(r_begin + a.rows_per_wave, sv.len);
+  const float s = a.sinks[h];
+  const int sub = lane % RS::kLanesPerRow;        // which 16-byte chunk of the row
+  const int rsub = lane / RS::kLanesPerRow;       // which row of the pass
+  const T* o = (const T*)a.o;
+  const T* dout = (const T*)a.dout;
+  const bool zero_kv = (a.dk_acc != nullptr) && (h % a.group == 0);
+  const int kvh = h / a.group;
+  float ds_part = 0.0f;
+  for (int r0 = r_begin; r0 < r_end; r0 += RS::kRowsPerPass) {
+    const int r = r0 + rsub;
+    float dot = 0.0f;
+    const size_t row = (size_t)sv.row_base + r;
+    if (r < r_end) {
+      const size_t off = (row * a.heads_q + h) * D + sub * RS::kElems;
+      const T* po = o + off;
+      const T* pd = dout + off;
+#pragma unroll
+      for (int e = 0; e < RS::kElems; ++e) dot += to_f32(po[e]) * to_f32(pd[e]);
+      if (a.dq_acc) {
+        float4* pz = (float4*)(a.dq_acc + off);
+#pragma unroll
+        for (int e = 0; e < RS::kElems / 4; ++e) pz[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      if (zero_kv) {
+        const size_t koff = (row * a.heads_kv + kvh) * D + sub * RS::kElems;
+        float4* pk = (float4*)(a.dk_acc + koff);
+        float4* pv = (float4*)(a.dv_acc + koff);
+#pragma unroll
+        for (int e = 0; e < RS::kElems / 4; ++e) {
+          pk[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+          pv[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
+#pragma unroll
+    for (int w = 1; w < RS::kLanesPerRow; w <<= 1) dot += __shfl_xor(dot, w);
+    if (r < r_end && sub == 0) {
+      const float l = a.lse[sv.lse_base + (size_t)h * a.lse_head_stride + r];
+      const float mx = fmaxf(l, s);
+      const float big_l = (s == -INFINITY) ? l : mx + log1pf(expf(-fabsf(l - s)));
+      const size_t wi = (size_t)h * a.rows_total + row;
+      a.d_ws[wi] = dot;
+      a.l_ws[wi] = big_l;
+      ds_part -= expf(s - big_l) * dot;
+    }
+  }
+#pragma unroll
+  for (int w = 1; w < 64; w <<= 1) ds_part += __shfl_xor(ds_part, w);
+  if (lane == 0 && r_end > r_begin) unsafeAtomicAdd(a.dsinks + h, ds_part);
+}
+
+__global__ void sinkattn_zero_f32(float* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+// fp32 accumulators -> output dtype, with the softmax scale folded into dQ
+// and dK here (the main kernel accumulates dS K and dS^T Q unscaled).
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float4 v);
+template <>
+__device__ __forceinline__ void store4<bf16>(bf16* dst, float4 v) {
+  *(bf16x4*)dst = to_bf16x4(v.x, v.y, v.z, v.w);
+}
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, float4 v) {
+  *(float4*)dst = v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void sinkattn_convert(const float* dq_acc, const float* dk_acc,
+                                                        const float* dv_acc, T* dq, T* dk, T* dv,
+                                                        long long n_q4, long long n_kv4, float scale) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n_q4; i += stride) {
+    float4 x = ((const float4*)dq_acc)[i];
+    x.x *= scale; x.y *= scale; x.z *= scale; x.w *= scale;
+    store4<T>(dq + 4 * i, x);
+  }
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n_kv4; i += stride) {
+    float4 x = ((const float4*)dk_acc)[i];
+    x.x *= scale; x.y *= scale; x.z *= scale; x.w *= scale;
+    store4<T>(dk + 4 * i, x);
+    store4<T>(dv + 4 * i, ((const float4*)dv_acc)[i]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_zero_f32(float* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sinkattn_zero_f32, dim3((n + 255) / 256), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const void* dout,
+                          const float* lse, const float* sinks, const int* cu_seqlens,
+                          float* dsinks, float* d_ws, float* l_ws, float* dq_acc, float* dk_acc,
+                          float* dv_acc, int batch, int seqlen, int rows_total, int heads_q,
+                          int heads_kv, int lse_head_stride, hipStream_t stream) {
+  PreArgs a;
+  a.o = o; a.dout = dout; a.lse = lse; a.sinks = sinks; a.cu_seqlens = cu_seqlens;
+  a.dsinks = dsinks; a.d_ws = d_ws; a.l_ws = l_ws;
+  a.dq_acc = dq_acc; a.dk_acc = dk_acc; a.dv_acc = dv_acc;
+  a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
+  a.group = heads_q / heads_kv; a.rows_total = rows_total;
+  a.lse_head_stride = lse_head_stride;
+  a.rows_per_wave = 256;
+  dim3 grid((seqlen + a.rows_per_wave - 1) / a.rows_per_wave, (heads_q + 3) / 4, batch);
+  if (grid.x == 0 || batch == 0) return hipSuccess;
+  if (!dtype_is_f32 && head_dim == 64) {
+    hipLaunchKernelGGL((sinkattn_bwd_pre<bf16, 64>), grid, dim3(256), 0, stream, a);
+  } else if (dtype_is_f32 && head_dim == 64) {
+    hipLaunchKernelGGL((sinkattn_bwd_pre<float, 64>), grid, dim3(256), 0, stream, a);
+  } else if (dtype_is_f32 && head_dim == 32) {
+    hipLaunchKernelGGL((sinkattn_bwd_pre<float, 32>), grid, dim3(256), 0, stream, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_convert(int dtype_is_f32, const float* dq_acc, const float* dk_acc,
+                          const float* dv_acc, void* dq, void* dk, void* dv, long long n_q,
+                          long long n_kv, float scale, hipStream_t stream) {
+  const long long n4 = (n_q / 4 > n_kv / 4) ? n_q / 4 : n_kv / 4;
+  if (n4 == 0) return hipSuccess;
+  long long blocks = (n4 + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (dtype_is_f32) {
+    hipLaunchKernelGGL(sinkattn_convert<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       dq_acc, dk_acc, dv_acc, (float*)dq, (float*)dk, (float*)dv, n_q / 4,
+                       n_kv / 4, scale);
+  } else {
+    hipLaunchKernelGGL(sinkattn_convert<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       dq_acc, dk_acc, dv_acc, (bf16*)dq, (bf16*)dk, (bf16*)dv, n_q / 4,
+                       n_kv / 4, scale);
+  }
+  return hipGetLastError();
+}

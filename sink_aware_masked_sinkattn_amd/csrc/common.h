@@ -1,0 +1,98 @@
+// Device-side building blocks for the gfx950 (CDNA4) kernels: vector types,
+// MFMA wrappers, LDS transpose reads, cross-half-wave reductions.
+//
+// MFMA lane layouts (v_mfma_f32_32x32x16_bf16, wave64), checked on the device:
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) + j, j = 0..7
+//   B (16 x 32): lane l holds col l%32, k = 8*(l/32) + j
+//   C (32 x 32): lane l holds col l%32, rows 8*(i/4) + 4*(l/32) + i%4, i = 0..15
+// Any permutation of k applied identically to A and B leaves C unchanged,
+// which is how probabilities produced in C layout feed the next MFMA directly.
+//
+// ds_read_tr16_b64 (LDS transpose read), per 16-lane group: lane i receives,
+// as element j (0..3), the 16-bit value at (address of lane 4j + i/4) + i%4.
+// Pointing lane L at row r0 + L/4, column c0 + 4*(L%4) of a row-major [row][col]
+// bf16 array makes lane i hold column c0 + i, rows r0 .. r0+3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define SA_LOG2E 1.4426950408889634f
+#define SA_LN2 0.6931471805599453f
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed 4 x 16-bit read from LDS (see header comment).
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Reduce across the two 32-lane halves of the wave (lanes l and l^32).
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// 8 fp32 -> 8 bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3, float a4,
+                                            float a5, float a6, float a7) {
+  f32x2 p0 = {a0, a1}, p1 = {a2, a3}, p2 = {a4, a5}, p3 = {a6, a7};
+  bf16x2 b0 = __builtin_convertvector(p0, bf16x2);
+  bf16x2 b1 = __builtin_convertvector(p1, bf16x2);
+  bf16x2 b2 = __builtin_convertvector(p2, bf16x2);
+  bf16x2 b3 = __builtin_convertvector(p3, bf16x2);
+  bf16x4 lo = __builtin_shufflevector(b0, b1, 0, 1, 2, 3);
+  bf16x4 hi = __builtin_shufflevector(b2, b3, 0, 1, 2, 3);
+  return cat8(lo, hi);
+}
+__device__ __forceinline__ bf16x4 to_bf16x4(float a0, float a1, float a2, float a3) {
+  f32x2 p0 = {a0, a1}, p1 = {a2, a3};
+  bf16x2 b0 = __builtin_convertvector(p0, bf16x2);
+  bf16x2 b1 = __builtin_convertvector(p1, bf16x2);
+  return __builtin_shufflevector(b0, b1, 0, 1, 2, 3);
+}
+
+// Where a sequence lives in the packed/batched tensors.
+struct SeqView {
+  int row_base;  // first token row of the sequence in [B*T] or [N]
+  int len;       // its length
+  int lse_base;  // offset of (head 0, token 0) in the lse tensor, minus head stride
+};
+
+__device__ __forceinline__ SeqView seq_view(const int* cu_seqlens, int z, int seqlen, int heads_q) {
+  SeqView s;
+  if (cu_seqlens) {
+    s.row_base = cu_seqlens[z];
+    s.len = cu_seqlens[z + 1] - s.row_base;
+    s.lse_base = s.row_base;            // lse [Hq, N]: h * N + row
+  } else {
+    s.row_base = z * seqlen;
+    s.len = seqlen;
+    s.lse_base = z * heads_q * seqlen;  // lse [B, Hq, T]: (z*Hq + h)*T + t
+  }
+  return s;
+}

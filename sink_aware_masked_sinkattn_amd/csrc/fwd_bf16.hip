@@ -1,0 +1,309 @@
+// Forward of sink-aware masked attention, bf16 in / bf16 out, head dim 64,
+// on gfx950 MFMA.
+//
+// What it computes: for each query row q of head h, over the keys that the
+// mask M[q,k] = 1[k<=q] AND 1[q-k<=w OR k<p] leaves visible,
+//   l[q] = log sum_k exp(scale q.k)           (content-only log-sum-exp)
+//   O[q] = sigmoid(l[q] - s_h) * softmax(scale q.K) V
+// ("Efficient Reinforcement Learning for Long-Horizon Tool-Use Agentic
+// Tasks", summary page, sink-aware FlexAttention paragraph; the equivalence
+// with an explicit zero-value sink column is arXiv 2608.10357 section 5,
+// "Zero-value sink equivalence").  The score matrix is never stored: key tiles
+// stream through LDS and an online softmax (running max m, running sum r)
+// keeps fp32 state per row, in the blockwise exact form the same section cites
+// (FlashAttention).  Because
+//   sigmoid(l - s) * Obar = acc / (r + exp(s - m)) when acc = sum exp(S - m) v,
+// the sink scaling costs one extra exponential per row in the epilogue.
+//
+// Work decomposition (one workgroup = 4 waves = 256 query rows of one head):
+//   * each wave owns 64 query rows (two 32-row MFMA blocks) whose Q fragments
+//     stay in registers for the whole kernel;
+//   * key tiles of 64 rows are listed per workgroup from the mask (prefix
+//     tiles + window tiles, each once), double-buffered in LDS: K row-major,
+//     V row-major and read transposed with ds_read_tr16_b64;
+//   * S^T = K Q^T puts one query per lane (C layout), so the row max / sum
+//     need only a 32-lane swap, and the probabilities convert in registers
+//     into the B operand of O^T += V^T P^T;
+//   * each wave classifies every key tile against its own rows: skipped
+//     tiles cost nothing, full tiles run mask-free, partial tiles apply the
+//     element predicate;
+//   * grid z runs from the last query tile to the first (longest rows start
+//     first); grid x maps the heads so that one kv-group's query heads share
+//     an XCD and its L2 (consecutive workgroups go to consecutive XCDs).
+#include "common.h"
+#include "mask_tiles.h"
+
+namespace {
+
+constexpr int D = 64;
+constexpr int QB = 2;                    // 32-row query blocks per wave
+constexpr int WAVES = 4;
+constexpr int BQ = WAVES * QB * 32;      // 256 query rows per workgroup
+constexpr int BK = 64;                   // key rows per LDS tile
+constexpr int LROW = D + 8;              // padded LDS row (bf16 elements, 144 B)
+constexpr int TILE_ELEMS = BK * LROW;
+
+struct FwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const float* sinks;
+  bf16* o;
+  float* lse;                // may be null
+  const int* cu_seqlens;     // null for fixed length
+  int seqlen, heads_q, heads_kv, group, window, prefix;
+  int lse_head_stride;       // T (fixed) or N (varlen)
+  int num_q_tiles;
+  float scale_log2;          // softmax_scale * log2(e)
+};
+
+__device__ __forceinline__ int map_head(int x, int heads_q) {
+  // consecutive workgroups land on consecutive XCDs (8): give XCD c the
+  // contiguous head range [c*Hq/8, (c+1)*Hq/8) so a kv-group stays in one L2
+  if ((heads_q & 7) == 0) return (x & 7) * (heads_q >> 3) + (x >> 3);
+  return x;
+}
+
+__global__ __launch_bounds__(256, 2) void sinkattn_fwd_bf16_d64(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE_ELEMS];  // K0 V0 K1 V1
+
+  const int h = map_head(blockIdx.x, a.heads_q);
+  const int z = blockIdx.y;
+  const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
+  const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
+  const int q_start = qt * BQ;
+  if (q_start >= sv.len) return;
+  const int q_last = min(q_start + BQ - 1, sv.len - 1);
+  const int kvh = h / a.group;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int qw0 = q_start + wave * (QB * 32);
+  const bool wave_active = qw0 < sv.len;
+  const int qw1 = min(qw0 + QB * 32 - 1, sv.len - 1);
+
+  const int q_row_stride = a.heads_q * D;
+  const int kv_row_stride = a.heads_kv * D;
+  const bf16* qbase = a.q + (size_t)sv.row_base * q_row_stride + (size_t)h * D;
+  const bf16* kbase = a.k + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
+  const bf16* vbase = a.v + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds query l32 of each
+  // block, head-dim chunk 16s + 8g .. +7.
+  bf16x8 qf[QB][4];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + qb * 32 + l32;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (row < sv.len) {
+        qf[qb][s] = *(const bf16x8*)(qbase + (size_t)row * q_row_stride + 16 * s + 8 * g);
+      } else {
+        qf[qb][s] = bf16x8{};
+      }
+    }
+  }
+
+  int seg[4];
+  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BK, seg);
+  const int n0 = seg[1] - seg[0];
+  const int ntiles = n0 + (nseg > 1 ? seg[3] - seg[2] : 0);
+
+  // cooperative tile load: 512 chunks of 16 B per tensor, 2 per thread
+  const int ld_row0 = tid >> 3;          // 0..31 (and +32)
+  const int ld_col = (tid & 7) * 8;
+  uint4 kreg[2], vreg[2];
+  auto load_tile = [&](int t) {
+    const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = kt * BK + ld_row0 + 32 * i;
+      if (r < sv.len) {
+        kreg[i] = *(const uint4*)(kbase + (size_t)r * kv_row_stride + ld_col);
+        vreg[i] = *(const uint4*)(vbase + (size_t)r * kv_row_stride + ld_col);
+      } else {
+        kreg[i] = make_uint4(0, 0, 0, 0);
+        vreg[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+    bf16* ks = smem + (2 * buf) * TILE_ELEMS;
+    bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *(uint4*)(ks + (ld_row0 + 32 * i) * LROW + ld_col) = kreg[i];
+      *(uint4*)(vs + (ld_row0 + 32 * i) * LROW + ld_col) = vreg[i];
+    }
+  };
+
+  f32x16 acc[QB][2];
+  float m_run[QB], r_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    acc[qb][0] = f32x16{};
+    acc[qb][1] = f32x16{};
+    m_run[qb] = -1.0e30f;   // finite start: exp2(S - m) never sees (-inf) - (-inf)
+    r_run[qb] = 0.0f;
+  }
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
+    const int k0 = kt * BK;
+    const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
+                                : SA_TILE_SKIP;
+    if (cls != SA_TILE_SKIP) {
+      const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
+      const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
+      // ---- S^T = K Q^T: [kb][qb], lane = query, 16 keys in registers
+      f32x16 st[2][QB];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) st[kb][qb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 kf = *(const bf16x8*)(ks + (kb * 32 + l32) * LROW + 16 * s + 8 * g);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) st[kb][qb] = mfma32x32x16(kf, qf[qb][s], st[kb][qb]);
+        }
+      }
+      if (cls == SA_TILE_PARTIAL) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          const int qrow = qw0 + qb * 32 + l32;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+              if (!sa_visible(qrow, key, a.window, a.prefix)) st[kb][qb][i] = -INFINITY;
+            }
+        }
+      }
+      // ---- online softmax (log2 domain), probabilities to bf16
+      bf16x8 pf[2][QB][2];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb][qb][i]);
+        mx = halves_max(mx);
+        const float m_new = fmaxf(m_run[qb], mx * a.scale_log2);
+        const float corr = fast_exp2(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        float rs = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float p[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            p[i] = fast_exp2(fmaf(st[kb][qb][i], a.scale_log2, -m_new));
+            rs += p[i];
+          }
+          pf[kb][qb][0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+          pf[kb][qb][1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+        }
+        r_run[qb] = r_run[qb] * corr + rs;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[qb][db][i] *= corr;
+      }
+      // ---- O^T += V^T P^T (A = V^T via LDS transpose reads)
+      const int grp = lane >> 4;           // 16-lane group 0..3
+      const int li = lane & 15;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r0 = kb * 32 + 16 * hh + 4 * g + (li >> 2);
+            const bf16x4 lo = lds_read_tr4(vs + r0 * LROW + c0);
+            const bf16x4 hi = lds_read_tr4(vs + (r0 + 8) * LROW + c0);
+            const bf16x8 vf = cat8(lo, hi);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(vf, pf[kb][qb][hh], acc[qb][db]);
+          }
+      }
+    }
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / (r + exp(s - m)), l = ln(2) * (m + log2 r)
+  // Stage each wave's 64 x 64 output through LDS for row-contiguous stores.
+  bf16* os = smem + wave * (QB * 32) * LROW;   // 64 rows x LROW per wave (fits in 4 tiles)
+  const float sink_l2 = a.sinks[h] * SA_LOG2E;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float r_tot = halves_sum(r_run[qb]);
+    const float denom = r_tot + fast_exp2(sink_l2 - m_run[qb]);
+    const float inv = 1.0f / denom;
+    const int qrow = qw0 + qb * 32 + l32;
+    if (a.lse && wave_active && g == 0 && qrow < sv.len) {
+      a.lse[sv.lse_base + (size_t)h * a.lse_head_stride + qrow] = (m_run[qb] + fast_log2(r_tot)) * SA_LN2;
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = db * 32 + 8 * i4 + 4 * g;
+        *(bf16x4*)(os + (qb * 32 + l32) * LROW + d) =
+            to_bf16x4(acc[qb][db][4 * i4] * inv, acc[qb][db][4 * i4 + 1] * inv,
+                      acc[qb][db][4 * i4 + 2] * inv, acc[qb][db][4 * i4 + 3] * inv);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  if (wave_active) {
+    bf16* obase = a.o + (size_t)sv.row_base * q_row_stride + (size_t)h * D;
+#pragma unroll
+    for (int it = 0; it < (QB * 32 * D) / (64 * 8); ++it) {   // 8 iterations of 64 lanes x 16 B
+      const int chunk = it * 64 + lane;
+      const int r = chunk >> 3;
+      const int c = (chunk & 7) * 8;
+      const int qrow = qw0 + r;
+      if (qrow < sv.len) {
+        *(uint4*)(obase + (size_t)qrow * q_row_stride + c) = *(const uint4*)(os + r * LROW + c);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Host-side launcher (called from the C ABI after validation).
+hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const float* sinks,
+                               bf16* o, float* lse, const int* cu_seqlens, int batch, int seqlen,
+                               int total_tokens, int heads_q, int heads_kv, int window,
+                               int prefix, float scale, hipStream_t stream) {
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.o = o; a.lse = lse;
+  a.cu_seqlens = cu_seqlens;
+  a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
+  a.group = heads_q / heads_kv;
+  a.window = window; a.prefix = prefix;
+  a.lse_head_stride = cu_seqlens ? total_tokens : seqlen;
+  a.num_q_tiles = (seqlen + BQ - 1) / BQ;
+  a.scale_log2 = scale * SA_LOG2E;
+  if (a.num_q_tiles == 0 || batch == 0 || heads_q == 0) return hipSuccess;
+  dim3 grid(heads_q, batch, a.num_q_tiles);
+  hipLaunchKernelGGL(sinkattn_fwd_bf16_d64, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}

@@ -1,0 +1,77 @@
+// Tile-level view of the sink-aware mask
+//   M[q,k] = 1[k <= q] AND 1[q - k <= w OR k < p]
+// ("Efficient Reinforcement Learning for Long-Horizon Tool-Use Agentic Tasks",
+// summary page, sink-aware FlexAttention paragraph).  Positions are local to
+// one sequence.  Host- and device-callable, integer only.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define SA_HD __host__ __device__ __forceinline__
+#else
+#define SA_HD static inline
+#endif
+
+enum { SA_TILE_SKIP = 0, SA_TILE_FULL = 1, SA_TILE_PARTIAL = 2 };
+
+// Element predicate.  w may be INT32_MAX; q - k never overflows for
+// non-negative positions.
+SA_HD bool sa_visible(int q, int k, int w, int p) {
+  return (k <= q) && ((q - k <= w) || (k < p));
+}
+
+SA_HD int sa_max(int a, int b) { return a > b ? a : b; }
+SA_HD int sa_min(int a, int b) { return a < b ? a : b; }
+
+// Classify the block of query rows [q0, q1] x key columns [k0, k1]
+// (inclusive, q0 <= q1, k0 <= k1).
+//  skip:  no key is causal for any row (k0 > q1), or every key is past the
+//         prefix and even the closest pair (q0, k1) is beyond the window;
+//  full:  every key is causal for every row (k1 <= q0) and every key that is
+//         not a prefix key lies within the window of the farthest row q1;
+//  partial otherwise (the element predicate decides).
+SA_HD int sa_tile_class(int q0, int q1, int k0, int k1, int w, int p) {
+  if (k0 > q1) return SA_TILE_SKIP;
+  if (k0 >= p && q0 - k1 > w) return SA_TILE_SKIP;
+  if (k1 <= q0) {
+    if (k1 < p) return SA_TILE_FULL;
+    if (q1 - sa_max(k0, p) <= w) return SA_TILE_FULL;
+  }
+  return SA_TILE_PARTIAL;
+}
+
+// Key tiles (width bk) that query rows [q0, q1] must visit: the prefix tiles
+// [0, ceil(min(p, q1+1)/bk)) and the window tiles
+// [floor(max(0, q0-w)/bk), floor(q1/bk)], merged when they touch.  A tile is
+// listed iff it holds at least one visible pair, and at most once.
+// Writes up to two half-open ranges to out[0..3]; returns their number.
+SA_HD int sa_key_tile_segments(int q0, int q1, int w, int p, int bk, int* out) {
+  const long long wlo = (long long)q0 - (long long)w;
+  const int win_begin = (int)((wlo > 0 ? wlo : 0) / bk);
+  const int win_end = q1 / bk + 1;
+  const int pre_keys = sa_min(p, q1 + 1);
+  const int pre_end = (pre_keys + bk - 1) / bk;
+  if (pre_end <= 0 || pre_end >= win_begin) {
+    out[0] = pre_end > 0 ? 0 : win_begin;
+    out[1] = win_end;
+    out[2] = out[3] = 0;
+    return 1;
+  }
+  out[0] = 0;
+  out[1] = pre_end;
+  out[2] = win_begin;
+  out[3] = win_end;
+  return 2;
+}
+
+// Query rows that key columns [k0, k1] are visible to, within a sequence of
+// n tokens: rows [k0, qmax] with qmax = n-1 if any key is a prefix key, else
+// min(n-1, k1 + w).  Returns false if no row sees them.
+SA_HD bool sa_query_range(int k0, int k1, int n, int w, int p, int* qlo, int* qhi) {
+  if (k0 >= n) return false;
+  long long hi = (k0 < p) ? (long long)(n - 1) : (long long)k1 + (long long)w;
+  if (hi > n - 1) hi = n - 1;
+  *qlo = k0;
+  *qhi = (int)hi;
+  return *qlo <= *qhi;
+}

@@ -1,0 +1,130 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/sinkattn.h declares, and rejects invalid calls on the host
+(before any HIP call) with the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sink_aware_masked_sinkattn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sinkattn.h")
+
+# fake device addresses: never dereferenced, validation fails before any HIP call
+A = 0x7F0000000000
+
+
+def _lib():
+    return binding.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sinkattn_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    names = _declared_functions()
+    assert set(names) >= {"sinkattn_fwd", "sinkattn_bwd", "sinkattn_bwd_workspace_size",
+                          "sinkattn_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = _lib()
+    for code in range(8):
+        s = lib.sinkattn_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.sinkattn_status_string(99).decode() == "unknown status"
+
+
+def _problem(**kw):
+    pb = binding.Problem()
+    pb.dtype = kw.get("dtype", binding.SINKATTN_BF16)
+    pb.batch = kw.get("batch", 1)
+    pb.seqlen = kw.get("seqlen", 256)
+    pb.total_tokens = kw.get("total_tokens", 256)
+    pb.heads_q = kw.get("heads_q", 8)
+    pb.heads_kv = kw.get("heads_kv", 2)
+    pb.head_dim = kw.get("head_dim", 64)
+    pb.window = kw.get("window", 128)
+    pb.prefix = kw.get("prefix", 4)
+    pb.softmax_scale = kw.get("softmax_scale", 0.125)
+    pb.cu_seqlens = kw.get("cu_seqlens", None)
+    return pb
+
+
+def _fwd(pb, q=A, k=A, v=A, s=A, o=A, lse=A):
+    return _lib().sinkattn_fwd(ctypes.byref(pb), q, k, v, s, o, lse, None)
+
+
+def _bwd(pb, ws=A, ws_bytes=1 << 40, **ptrs):
+    p = {n: ptrs.get(n, A) for n in ("q", "k", "v", "s", "o", "lse", "do", "dq", "dk", "dv", "ds")}
+    return _lib().sinkattn_bwd(ctypes.byref(pb), p["q"], p["k"], p["v"], p["s"], p["o"],
+                               p["lse"], p["do"], p["dq"], p["dk"], p["dv"], p["ds"], ws,
+                               ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(heads_q=6, heads_kv=4), 2),
+    (dict(heads_kv=0), 2),
+    (dict(batch=-1), 2),
+    (dict(seqlen=-5), 2),
+    (dict(softmax_scale=0.0), 2),
+    (dict(softmax_scale=float("nan")), 2),
+    (dict(window=-1), 3),
+    (dict(prefix=-2), 3),
+    (dict(head_dim=128), 4),
+    (dict(dtype=7), 4),
+    (dict(dtype=binding.SINKATTN_FP32, head_dim=48), 4),
+])
+def test_invalid_problem_rejected(kw, code):
+    pb = _problem(**kw)
+    assert _fwd(pb) == code
+    assert _bwd(pb) == code
+    assert _lib().sinkattn_bwd_workspace_size(ctypes.byref(pb)) == 0
+
+
+def test_null_and_misaligned_pointers():
+    pb = _problem()
+    assert _lib().sinkattn_fwd(None, A, A, A, A, A, A, None) == 1
+    for name in ("q", "k", "v", "s", "o"):
+        assert _fwd(pb, **{name: None}) == 1, name
+        assert _fwd(pb, **{name: A + 2}) == 5, name
+    assert _fwd(pb, lse=A + 4) == 5
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert _bwd(pb, **{name: None}) == 1, name
+        assert _bwd(pb, **{name: A + 8}) == 5, name
+    assert _bwd(pb, ds=None) == 1
+    assert _bwd(pb, s=None) == 1
+
+
+def test_workspace_checks():
+    pb = _problem()
+    need = _lib().sinkattn_bwd_workspace_size(ctypes.byref(pb))
+    rows, hq, hkv, d = 256, 8, 2, 64
+    # D and L stats, fp32 dQ accumulator, fp32 dK and dV accumulators
+    assert need >= 4 * (2 * rows * hq + rows * hq * d + 2 * rows * hkv * d)
+    assert _bwd(pb, ws=None) == 6
+    assert _bwd(pb, ws_bytes=need - 1) == 6
+    assert _bwd(pb, ws=A + 16, ws_bytes=need) == 5          # workspace must be 256-B aligned
+    f32 = _problem(dtype=binding.SINKATTN_FP32, head_dim=32)
+    need32 = _lib().sinkattn_bwd_workspace_size(ctypes.byref(f32))
+    assert need32 >= 4 * 2 * rows * hq
+    pb_var = _problem(cu_seqlens=A, batch=3, total_tokens=1000, seqlen=600)
+    need_var = _lib().sinkattn_bwd_workspace_size(ctypes.byref(pb_var))
+    assert need_var >= 4 * (2 * 1000 * hq + 1000 * hq * d + 2 * 1000 * hkv * d)
+    bad_var = _problem(cu_seqlens=A, batch=3, total_tokens=-1)
+    assert _fwd(bad_var) == 2
+
+
+def test_empty_forward_is_a_no_op():
+    # zero rows: valid, returns OK without touching the device
+    assert _fwd(_problem(batch=0)) == 0
+    assert _fwd(_problem(seqlen=0)) == 0
+    assert _fwd(_problem(batch=0), q=None, k=None, v=None, s=None, o=None, lse=None) == 0

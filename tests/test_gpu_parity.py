@@ -1,0 +1,216 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
+the same seeded inputs.  Tolerances are in tests/parity_util.py.
+
+Small cases span several query tiles (256 rows forward, 64 backward) and key
+tiles (64 forward, 128 backward) with ragged tails, every mask regime
+(plain causal, window, prefix, window+prefix, w=0, prefix past the end), GQA
+and varlen packing with empty, single-token and tile-edge lengths.  The
+named workloads run at their full sizes, compared on whole GQA groups.
+"""
+import numpy as np
+import pytest
+import torch
+
+from parity_util import compare, log, run_gpu, run_oracle
+from workloads import WINDOW_INF, WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+SMALL = [
+    # B, T, Hq, Hkv, w, p, std
+    (2, 300, 8, 2, WINDOW_INF, 0, 0.5),
+    (1, 333, 4, 1, 128, 0, 1.0),
+    (2, 300, 8, 2, 128, 4, 0.5),
+    (1, 257, 4, 4, 0, 0, 1.0),
+    (1, 257, 4, 2, 1, 0, 1.0),
+    (1, 400, 4, 2, 63, 1, 0.5),
+    (1, 400, 4, 2, 64, 5, 0.5),
+    (1, 300, 4, 2, 200, 300, 0.5),
+    (1, 520, 4, 2, 5, 130, 0.5),
+    (1, 64, 2, 1, 16, 4, 1.0),
+    (3, 129, 16, 2, 31, 2, 0.5),
+    (1, 1, 2, 1, 0, 0, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}_T{}_H{}x{}_w{}_p{}_s{}".format(*c))
+def test_bf16_small(case):
+    b, t, hq, hkv, w, p, std = case
+    inp = make_inputs(batch=b, seqlen=t, heads_q=hq, heads_kv=hkv, head_dim=64, window=w,
+                      prefix=p, seed=hash(case) % 100000, std=std, dtype="bf16")
+    log(f"case {case}")
+    compare(run_gpu(inp), run_oracle(inp), "bf16", inp, label=str(case), scaled=True)
+
+
+@pytest.mark.parametrize("lengths,w,p", [
+    ((1, 63, 65, 255, 257, 300), 20, 3),
+    ((0, 5, 0, 130), 4, 2),
+    ((512, 1, 77), WINDOW_INF, 0),
+    ((200, 300), 128, 16),
+])
+def test_bf16_varlen_small(lengths, w, p):
+    inp = make_inputs(batch=0, seqlen=0, heads_q=8, heads_kv=2, head_dim=64, window=w, prefix=p,
+                      seed=sum(lengths) + w, std=0.5, dtype="bf16", lengths=lengths)
+    log(f"varlen {lengths} w={w} p={p}")
+    compare(run_gpu(inp), run_oracle(inp), "bf16", inp, label=f"varlen{lengths}", scaled=True)
+
+
+@pytest.mark.parametrize("sinks", [(float("-inf"), -10.0, 0.0, 10.0)])
+def test_bf16_sink_extremes(sinks):
+    inp = make_inputs(batch=1, seqlen=200, heads_q=4, heads_kv=2, head_dim=64, window=30,
+                      prefix=2, seed=5, std=1.0, dtype="bf16", sink_values=sinks)
+    compare(run_gpu(inp), run_oracle(inp), "bf16", inp, label="sinks", scaled=True)
+
+
+@pytest.mark.parametrize("d,case", [(32, (1, 128, 2, 2, 16, 4)), (32, (2, 200, 4, 2, 7, 0)),
+                                    (64, (1, 150, 4, 1, WINDOW_INF, 0)),
+                                    (32, (1, 90, 2, 1, 0, 50))])
+def test_fp32_small(d, case):
+    b, t, hq, hkv, w, p = case
+    inp = make_inputs(batch=b, seqlen=t, heads_q=hq, heads_kv=hkv, head_dim=d, window=w,
+                      prefix=p, seed=d + t, std=1.0, dtype="fp32")
+    compare(run_gpu(inp), run_oracle(inp), "fp32", inp, label=f"fp32 d{d} {case}")
+
+
+def test_fp32_varlen():
+    inp = make_inputs(batch=0, seqlen=0, heads_q=2, heads_kv=1, head_dim=32, window=9, prefix=3,
+                      seed=3, std=1.0, dtype="fp32", lengths=(17, 0, 64, 1))
+    compare(run_gpu(inp), run_oracle(inp), "fp32", inp, label="fp32 varlen")
+
+
+# ------------------------------------------------------------ named workloads
+
+def test_workload_tiny_fp32():
+    (inp,) = workload_inputs("tiny_fp32")
+    compare(run_gpu(inp), run_oracle(inp), "fp32", inp, label="tiny_fp32")
+
+
+def _group_heads(inp, kv):
+    return list(range(kv * inp.group, (kv + 1) * inp.group))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,layer,kv", [("gqa_swa_4096", 0, 3), ("gqa_causal_4096", 0, 5),
+                                           ("long_8192", 0, 1), ("long_8192", 1, 6)])
+def test_workload_full_size(name, layer, kv):
+    """Full-size run of the workload (every head computed on the GPU, in the
+    same launch configuration the benchmark times); the oracle recomputes one
+    whole GQA group (8 query heads + their kv head) for the comparison."""
+    inp = workload_inputs(name)[layer]
+    heads = _group_heads(inp, kv)
+    log(f"{name} layer {layer}: GPU run")
+    gpu = run_gpu(inp)
+    log(f"{name} layer {layer}: oracle on heads {heads}")
+    ref = run_oracle(inp, heads=heads)
+    compare(gpu, ref, "bf16", inp, heads=heads, label=f"{name}[{layer}] kv{kv}")
+
+
+_VARLEN = {}
+
+
+def _varlen_state():
+    if "inp" not in _VARLEN:
+        (inp,) = workload_inputs("varlen_grpo_g8")
+        _VARLEN["inp"] = inp
+        log(f"varlen_grpo_g8 lengths {inp.lengths}: GPU run")
+        _VARLEN["gpu"] = run_gpu(inp)
+        _VARLEN["ds_parts"] = {}
+    return _VARLEN
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("seq", list(range(8)))
+def test_workload_varlen_per_sequence(seq):
+    """Packed GRPO group (8 rollouts): the whole pack runs on the GPU in one
+    call; the oracle checks one sequence per test on GQA group kv=2."""
+    st = _varlen_state()
+    inp = st["inp"]
+    kv = 2
+    heads = _group_heads(inp, kv)
+    cu = inp.cu_seqlens.numpy()
+    r = slice(int(cu[seq]), int(cu[seq + 1]))
+    sub = make_inputs(batch=1, seqlen=int(cu[seq + 1] - cu[seq]), heads_q=inp.q.shape[1],
+                      heads_kv=inp.k.shape[1], head_dim=64, window=inp.window, prefix=inp.prefix,
+                      seed=0, dtype="bf16")
+    sub.q, sub.k, sub.v, sub.do = (t[r].unsqueeze(0) for t in (inp.q, inp.k, inp.v, inp.do))
+    sub.sinks = inp.sinks
+    ref = run_oracle(sub, heads=heads)
+    gpu = st["gpu"]
+    g = {"o": gpu["o"][r][None], "dq": gpu["dq"][r][None], "dk": gpu["dk"][r][None],
+         "dv": gpu["dv"][r][None], "lse": gpu["lse"][:, r][None]}
+    compare(g, ref, "bf16", sub, heads=heads, what=("o", "lse", "dq", "dk", "dv"),
+            label=f"varlen seq {seq} (len {r.stop - r.start})")
+    st["ds_parts"][seq] = ref["ds"]
+    if len(st["ds_parts"]) == 8:
+        ds_ref = sum(st["ds_parts"].values())[heads]
+        ds_gpu = gpu["ds"][heads]
+        err = float(np.max(np.abs(ds_gpu - ds_ref)) / np.max(np.abs(ds_ref)))
+        log(f"  varlen ds (all sequences) norm-wise rel error {err:.3g}")
+        assert err <= 2e-2
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_varlen_equals_separate_calls():
+    lengths = (70, 300, 129)
+    inp = make_inputs(batch=0, seqlen=0, heads_q=8, heads_kv=2, head_dim=64, window=40, prefix=3,
+                      seed=17, std=0.5, dtype="bf16", lengths=lengths)
+    full = run_gpu(inp)
+    cu = inp.cu_seqlens.numpy()
+    ds_sum = np.zeros_like(full["ds"])
+    for i, L in enumerate(lengths):
+        r = slice(int(cu[i]), int(cu[i + 1]))
+        one = make_inputs(batch=1, seqlen=L, heads_q=8, heads_kv=2, head_dim=64, window=40,
+                          prefix=3, seed=0, dtype="bf16")
+        one.q, one.k, one.v, one.do = (t[r].unsqueeze(0) for t in (inp.q, inp.k, inp.v, inp.do))
+        one.sinks = inp.sinks
+        sep = run_gpu(one)
+        np.testing.assert_array_equal(full["o"][r], sep["o"][0])
+        np.testing.assert_array_equal(full["lse"][:, r], sep["lse"][0])
+        for n in ("dq", "dk", "dv"):
+            np.testing.assert_allclose(full[n][r], sep[n][0], atol=1e-2)
+        ds_sum += sep["ds"]
+    np.testing.assert_allclose(full["ds"], ds_sum, rtol=1e-3, atol=1e-3)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    inp = make_inputs(batch=1, seqlen=300, heads_q=8, heads_kv=2, head_dim=64, window=100,
+                      prefix=2, seed=23, std=0.5, dtype="bf16")
+    gqa = run_gpu(inp)
+    mha = make_inputs(batch=1, seqlen=300, heads_q=8, heads_kv=8, head_dim=64, window=100,
+                      prefix=2, seed=0, dtype="bf16")
+    mha.q, mha.do, mha.sinks = inp.q, inp.do, inp.sinks
+    mha.k = inp.k.repeat_interleave(4, dim=2).contiguous()
+    mha.v = inp.v.repeat_interleave(4, dim=2).contiguous()
+    rep = run_gpu(mha)
+    np.testing.assert_array_equal(gqa["o"], rep["o"])
+    np.testing.assert_array_equal(gqa["lse"], rep["lse"])
+    np.testing.assert_allclose(gqa["dq"], rep["dq"], atol=1e-2)
+    for n in ("dk", "dv"):
+        summed = rep[n].reshape(1, 300, 2, 4, 64).sum(axis=3)
+        np.testing.assert_allclose(gqa[n], summed, atol=2e-2)
+
+
+def test_memory_grows_linearly():
+    """Peak device memory of fwd+bwd (workspace included) is O(T)."""
+    peaks = {}
+    for t in (2048, 4096, 8192):
+        inp = make_inputs(batch=1, seqlen=t, heads_q=64, heads_kv=8, head_dim=64,
+                          window=WINDOW_INF, prefix=0, seed=1, std=0.5, dtype="bf16")
+        dev = torch.device("cuda:0")
+        q, k, v, do = (x.to(dev) for x in (inp.q, inp.k, inp.v, inp.do))
+        s = inp.sinks.to(dev)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        base = torch.cuda.memory_allocated()
+        from sink_aware_masked_sinkattn_amd import sinkattn_bwd, sinkattn_fwd
+        o, lse = sinkattn_fwd(q, k, v, s, inp.window, inp.prefix, inp.scale)
+        grads = sinkattn_bwd(q, k, v, s, o, lse, do, inp.window, inp.prefix, inp.scale)
+        torch.cuda.synchronize()
+        peaks[t] = torch.cuda.max_memory_allocated() - base
+        del o, lse, grads, q, k, v, do
+        log(f"  T={t}: peak extra {peaks[t] / 2**20:.1f} MiB")
+    # doubling T must not more than double (plus slack) the extra memory
+    assert peaks[4096] <= 2.1 * peaks[2048]
+    assert peaks[8192] <= 2.1 * peaks[4096]
