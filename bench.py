@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of sink-aware masked attention, forward + backward, on one GPU.
+
+One step = one full pass of the hot path over the long-context workload
+(B=1, Hq=64, Hkv=8, d=64, T=8192, two attention layers: a 128-token
+sliding window with 4 prefix keys, and full causal): per layer the forward
+kernel, then the backward's prepare / main / finish phases.  Inputs are
+seeded synthetic bf16 tensors already resident in device memory; outputs
+and workspace are preallocated.
+
+Printed: one JSON line with useful (unmasked) TFLOP/s of the whole step
+(4d FLOP per visible (q, k) pair forward, 10d backward), the fraction of
+the bf16 dense MFMA peak, the roofline of the dominant kernel (timed live
+with HIP events on the library's stream), peak device memory, and the fp64
+oracle timed on a bounded sample on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sink-attn fwd+bwd useful TFLOP/s and % bf16 MFMA peak at T=8192"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+WINDOW_INF = 2**31 - 1
+CPU_SAMPLE_HEADS = 4
+
+KERNEL_SOURCES = {
+    "sinkattn_fwd_bf16_d64": ["fwd_bf16.hip", "common.h", "mask_tiles.h"],
+    "sinkattn_bwd_bf16_d64": ["bwd_bf16.hip", "common.h", "mask_tiles.h"],
+}
+
+
+def visible_pairs_per_head(n: int, window: int, prefix: int) -> int:
+    """Number of (q, k) pairs the mask leaves visible in one sequence of n
+    tokens: row i sees min(i + 1, w + p + 1) keys."""
+    c = min(window, n) + min(prefix, n) + 1
+    if c >= n:
+        return n * (n + 1) // 2
+    return c * (c + 1) // 2 + (n - c) * c
+
+
+def useful_pairs(inp) -> int:
+    hq = inp.q.shape[-2]
+    if inp.lengths is not None:
+        per = sum(visible_pairs_per_head(n, inp.window, inp.prefix) for n in inp.lengths)
+        return per * hq
+    b, t = inp.q.shape[0], inp.q.shape[1]
+    return b * hq * visible_pairs_per_head(t, inp.window, inp.prefix)
+
+
+def kernel_source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "sink_aware_masked_sinkattn_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not sha or not val or sha.group(1) != kernel_source_sha(kernel):
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(layers, head_dim: int):
+    """The fp64 oracle as it stands, timed on a bounded sample: the first
+    four query heads of each layer (forward + backward over the full
+    sequence; about 10 s on 16 host cores)."""
+    import numpy as np  # noqa: F401
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    flops = 0.0
+    t0 = time.perf_counter()
+    for inp in layers:
+        sl = slice(0, CPU_SAMPLE_HEADS)
+        q = inp.q[:, :, sl].to(torch.float64).numpy()
+        k = inp.k[:, :, sl].to(torch.float64).numpy()
+        v = inp.v[:, :, sl].to(torch.float64).numpy()
+        do = inp.do[:, :, sl].to(torch.float64).numpy()
+        s = inp.sinks[sl].to(torch.float64).numpy()
+        oracle.forward(q, k, v, s, inp.window, inp.prefix, inp.scale)
+        oracle.backward(q, k, v, s, do, inp.window, inp.prefix, inp.scale)
+        flops += (14 * head_dim * CPU_SAMPLE_HEADS *
+                  visible_pairs_per_head(inp.q.shape[1], inp.window, inp.prefix))
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{CPU_SAMPLE_HEADS} of 64 query heads per layer (both layers, T=8192), "
+                      "fwd+bwd in fp64; "
+                      f"{dt:.1f} s",
+            "seconds": round(dt, 3)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): "
+              "the sink-attention path here is a single-GPU kernel library; multi-GPU sharding "
+              "is described in the design notes but not built.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from sink_aware_masked_sinkattn_amd import (load_library, sinkattn_bwd_finish,
+                                                sinkattn_bwd_main, sinkattn_bwd_prepare,
+                                                sinkattn_bwd_workspace_size, sinkattn_fwd,
+                                                make_problem)
+    from workloads import WORKLOADS, workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    load_library()
+    wl = WORKLOADS[args.workload]
+    layers = workload_inputs(args.workload)
+    dev = torch.device("cuda:0")
+
+    runs = []
+    for inp in layers:
+        r = {"inp": inp}
+        r["q"], r["k"], r["v"], r["do"] = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.do))
+        r["s"] = inp.sinks.to(dev)
+        r["cu"] = inp.cu_seqlens.to(dev) if inp.cu_seqlens is not None else None
+        r["ms"] = inp.max_seqlen if inp.cu_seqlens is not None else None
+        runs.append(r)
+    torch.cuda.synchronize()
+    # device memory beyond the resident inputs: outputs, lse, workspace, transients
+    base_alloc = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    for r in runs:
+        inp = r["inp"]
+        r["o"] = torch.empty_like(r["q"])
+        pb = make_problem(r["q"], r["k"], inp.window, inp.prefix, inp.scale, r["cu"], r["ms"])
+        lse_shape = (pb.heads_q, pb.total_tokens) if r["cu"] is not None else \
+            (pb.batch, pb.heads_q, pb.seqlen)
+        r["lse"] = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+        r["grads"] = (torch.empty_like(r["q"]), torch.empty_like(r["k"]),
+                      torch.empty_like(r["v"]), torch.empty_like(r["s"]))
+        r["ws"] = torch.empty(sinkattn_bwd_workspace_size(pb), dtype=torch.uint8, device=dev)
+        r["pairs"] = useful_pairs(inp)
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for li, r in enumerate(runs):
+            inp = r["inp"]
+            a = (r["q"], r["k"], r["v"], r["s"])
+            ev = events[li] if events is not None else None
+            if ev:
+                ev[0].record()
+            sinkattn_fwd(*a, inp.window, inp.prefix, inp.scale, r["cu"], r["ms"], out=r["o"],
+                         lse=r["lse"])
+            if ev:
+                ev[1].record()
+            bargs = (*a, r["o"], r["lse"], r["do"], inp.window, inp.prefix, inp.scale, r["cu"],
+                     r["ms"])
+            sinkattn_bwd_prepare(*bargs, workspace=r["ws"], grads=r["grads"])
+            if ev:
+                ev[2].record()
+            sinkattn_bwd_main(*bargs, workspace=r["ws"], grads=r["grads"])
+            if ev:
+                ev[3].record()
+            sinkattn_bwd_finish(*bargs, workspace=r["ws"], grads=r["grads"])
+            if ev:
+                ev[4].record()
+
+    step()
+    torch.cuda.synchronize()
+    peak_mem = torch.cuda.max_memory_allocated()
+    inputs_bytes = sum(sum(t.numel() * t.element_size()
+                           for t in (r["q"], r["k"], r["v"], r["do"], r["s"])) for r in runs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in runs]
+              for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+
+    d = wl.head_dim
+    per_layer = []
+    for li, r in enumerate(runs):
+        ph = [sum(events[i][li][j].elapsed_time(events[i][li][j + 1]) for i in range(K)) / K
+              for j in range(4)]
+        per_layer.append({"window": r["inp"].window, "prefix": r["inp"].prefix,
+                          "pairs": r["pairs"], "fwd_ms": ph[0], "bwd_prepare_ms": ph[1],
+                          "bwd_main_ms": ph[2], "bwd_finish_ms": ph[3]})
+    total_flops = sum(14 * d * r["pairs"] for r in runs)
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the one with the largest total time per step
+    kern_time = {"sinkattn_fwd_bf16_d64": sum(p["fwd_ms"] for p in per_layer),
+                 "sinkattn_bwd_bf16_d64": sum(p["bwd_main_ms"] for p in per_layer)}
+    kern_flops = {"sinkattn_fwd_bf16_d64": sum(4 * d * p["pairs"] for p in per_layer),
+                  "sinkattn_bwd_bf16_d64": sum(10 * d * p["pairs"] for p in per_layer)}
+    dom = max(kern_time, key=kern_time.get)
+    launches = len(per_layer)
+    avg_ms = kern_time[dom] / launches
+    achieved = kern_flops[dom] / launches / (avg_ms * 1e-3) / 1e12
+    traffic = committed_traffic(dom, args.workload)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": dom, "avg_launch_ms": round(avg_ms, 4),
+                "algorithmic_flop_per_launch": kern_flops[dom] / launches}
+
+    # the full-causal layer alone (the target configuration)
+    causal = [p for p in per_layer if p["window"] >= 8192 and p["prefix"] == 0]
+    causal_info = None
+    if causal:
+        p = causal[0]
+        t_ms = p["fwd_ms"] + p["bwd_prepare_ms"] + p["bwd_main_ms"] + p["bwd_finish_ms"]
+        tf = 14 * d * p["pairs"] / (t_ms * 1e-3) / 1e12
+        causal_info = {"ms": round(t_ms, 4), "useful_tflops": round(tf, 2),
+                       "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                       "fwd_tflops": round(4 * d * p["pairs"] / (p["fwd_ms"] * 1e-3) / 1e12, 2),
+                       "bwd_main_tflops": round(10 * d * p["pairs"] / (p["bwd_main_ms"] * 1e-3)
+                                                / 1e12, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers, d)
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": wl.batch, "seq_len": wl.seqlen,
+                   "heads_q": wl.heads_q, "heads_kv": wl.heads_kv, "head_dim": wl.head_dim,
+                   "layers": [{"window": w if w < WINDOW_INF else "inf", "prefix": p}
+                              for (w, p) in wl.layers],
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "useful_flop_per_step": total_flops,
+        "full_causal_layer": causal_info,
+        "per_layer_ms": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}
+                         for p in per_layer],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "peak_mem_bytes": int(peak_mem - base_alloc),
+        "peak_mem_including_inputs_bytes": int(peak_mem - base_alloc + inputs_bytes),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -120,6 +120,37 @@ sinkattn_status sinkattn_bwd(const sinkattn_problem *problem, const void *q,
                              void *dq, void *dk, void *dv, float *dsinks,
                              void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The same backward as three stream-ordered phases, for callers that want to
+ * place work (or timing events) between them.  Each takes exactly the
+ * arguments of sinkattn_bwd, validates them the same way, and must be called
+ * in this order, on one stream, with the same arguments and workspace:
+ *   prepare: clears dsinks, then the row pass D = rowsum(dout * o),
+ *            L = logaddexp(lse, s_h), dsinks (the sink gradient of "GPT-OSS
+ *            Agentic RL training: a practical retrospective", FlashAttention
+ *            v3 implementation section), and clears the accumulators;
+ *   main:    dQ, dK, dV from the recomputed probabilities exp(S - L)
+ *            (into the workspace accumulators for bf16, into dq/dk/dv for fp32);
+ *   finish:  scales and converts the accumulators into dq, dk, dv (bf16; a
+ *            no-op for fp32).
+ * sinkattn_bwd == prepare; main; finish.
+ */
+sinkattn_status sinkattn_bwd_prepare(const sinkattn_problem *problem, const void *q,
+                                     const void *k, const void *v, const float *sinks,
+                                     const void *o, const float *lse, const void *dout,
+                                     void *dq, void *dk, void *dv, float *dsinks,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+sinkattn_status sinkattn_bwd_main(const sinkattn_problem *problem, const void *q,
+                                  const void *k, const void *v, const float *sinks,
+                                  const void *o, const float *lse, const void *dout,
+                                  void *dq, void *dk, void *dv, float *dsinks,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+sinkattn_status sinkattn_bwd_finish(const sinkattn_problem *problem, const void *q,
+                                    const void *k, const void *v, const float *sinks,
+                                    const void *o, const float *lse, const void *dout,
+                                    void *dq, void *dk, void *dv, float *dsinks,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *sinkattn_status_string(sinkattn_status status);
 

@@ -75,8 +75,11 @@ def load_library(path: str = LIB_PATH):
     pp = ctypes.POINTER(Problem)
     lib.sinkattn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
     lib.sinkattn_fwd.restype = ctypes.c_int
-    lib.sinkattn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.sinkattn_bwd.restype = ctypes.c_int
+    for name in ("sinkattn_bwd", "sinkattn_bwd_prepare", "sinkattn_bwd_main",
+                 "sinkattn_bwd_finish"):
+        fn = getattr(lib, name)
+        fn.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        fn.restype = ctypes.c_int
     lib.sinkattn_bwd_workspace_size.argtypes = [pp]
     lib.sinkattn_bwd_workspace_size.restype = sz
     lib.sinkattn_status_string.argtypes = [ctypes.c_int]
@@ -167,11 +170,8 @@ def sinkattn_fwd(q, k, v, sinks, window: int, prefix: int, softmax_scale=None,
     return out, lse
 
 
-def sinkattn_bwd(q, k, v, sinks, o, lse, dout, window: int, prefix: int, softmax_scale=None,
-                 cu_seqlens=None, max_seqlen=None, workspace=None, grads=None):
-    """Backward: returns (dq, dk, dv, dsinks).  ``workspace`` (uint8 GPU
-    tensor) is allocated here when not given; ``grads`` may pass preallocated
-    (dq, dk, dv, dsinks)."""
+def _bwd_call(entry: str, q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale,
+              cu_seqlens, max_seqlen, workspace, grads):
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (sinks, "sinks"), (o, "o"), (lse, "lse"),
                  (dout, "dout")):
@@ -185,12 +185,41 @@ def sinkattn_bwd(q, k, v, sinks, o, lse, dout, window: int, prefix: int, softmax
     need = int(lib.sinkattn_bwd_workspace_size(ctypes.byref(pb)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = lib.sinkattn_bwd(ctypes.byref(pb), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o),
-                          _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks),
-                          _ptr(workspace), workspace.numel(), _stream())
+    st = getattr(lib, entry)(ctypes.byref(pb), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o),
+                             _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks),
+                             _ptr(workspace), workspace.numel(), _stream())
     if st != 0:
-        raise SinkAttnError(st, "sinkattn_bwd", lib)
+        raise SinkAttnError(st, entry, lib)
     return dq, dk, dv, dsinks
+
+
+def sinkattn_bwd(q, k, v, sinks, o, lse, dout, window: int, prefix: int, softmax_scale=None,
+                 cu_seqlens=None, max_seqlen=None, workspace=None, grads=None):
+    """Backward: returns (dq, dk, dv, dsinks).  ``workspace`` (uint8 GPU
+    tensor) is allocated here when not given; ``grads`` may pass preallocated
+    (dq, dk, dv, dsinks)."""
+    return _bwd_call("sinkattn_bwd", q, k, v, sinks, o, lse, dout, window, prefix,
+                     softmax_scale, cu_seqlens, max_seqlen, workspace, grads)
+
+
+def sinkattn_bwd_prepare(q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale=None,
+                         cu_seqlens=None, max_seqlen=None, *, workspace, grads):
+    """First backward phase (same arguments as sinkattn_bwd; workspace and
+    grads must be given and reused by the later phases)."""
+    return _bwd_call("sinkattn_bwd_prepare", q, k, v, sinks, o, lse, dout, window, prefix,
+                     softmax_scale, cu_seqlens, max_seqlen, workspace, grads)
+
+
+def sinkattn_bwd_main(q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale=None,
+                      cu_seqlens=None, max_seqlen=None, *, workspace, grads):
+    return _bwd_call("sinkattn_bwd_main", q, k, v, sinks, o, lse, dout, window, prefix,
+                     softmax_scale, cu_seqlens, max_seqlen, workspace, grads)
+
+
+def sinkattn_bwd_finish(q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale=None,
+                        cu_seqlens=None, max_seqlen=None, *, workspace, grads):
+    return _bwd_call("sinkattn_bwd_finish", q, k, v, sinks, o, lse, dout, window, prefix,
+                     softmax_scale, cu_seqlens, max_seqlen, workspace, grads)
 
 
 def sinkattn_tile_class(q0: int, q1: int, k0: int, k1: int, window: int, prefix: int) -> int:

@@ -178,10 +178,13 @@ sinkattn_status sinkattn_fwd(const sinkattn_problem* pb, const void* q, const vo
                                    pb->heads_kv, window, prefix, pb->softmax_scale, s));
 }
 
-sinkattn_status sinkattn_bwd(const sinkattn_problem* pb, const void* q, const void* k,
-                             const void* v, const float* sinks, const void* o, const float* lse,
-                             const void* dout, void* dq, void* dk, void* dv, float* dsinks,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+enum { PHASE_PREPARE = 1, PHASE_MAIN = 2, PHASE_FINISH = 4, PHASE_ALL = 7 };
+
+static sinkattn_status bwd_phases(int phases, const sinkattn_problem* pb, const void* q,
+                                  const void* k, const void* v, const float* sinks, const void* o,
+                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                  float* dsinks, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   Dims dims;
   sinkattn_status st = check_problem(pb, &dims);
   if (st != SINKATTN_OK) return st;
@@ -200,8 +203,12 @@ sinkattn_status sinkattn_bwd(const sinkattn_problem* pb, const void* q, const vo
     if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SINKATTN_ERR_MISALIGNED;
   }
   // ---- validation done; device work from here on
-  hipError_t e = launch_zero_f32(dsinks, pb->heads_q, s);
-  if (e != hipSuccess || empty) return hip_status(e);
+  hipError_t e = hipSuccess;
+  if (phases & PHASE_PREPARE) {
+    e = launch_zero_f32(dsinks, pb->heads_q, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (empty) return SINKATTN_OK;
   const Workspace wl = workspace_layout(pb, dims);
   char* ws = static_cast<char*>(workspace);
   float* d_ws = (float*)(ws + wl.d_off);
@@ -214,26 +221,52 @@ sinkattn_status sinkattn_bwd(const sinkattn_problem* pb, const void* q, const vo
   const int prefix = pb->prefix > pb->seqlen ? pb->seqlen : pb->prefix;
   const int rows = (int)dims.rows;
   const int lse_stride = dims.varlen ? rows : pb->seqlen;
-  e = launch_bwd_pre(is_f32, pb->head_dim, o, dout, lse, sinks, pb->cu_seqlens, dsinks, d_ws, l_ws,
-                     dq_acc, dk_acc, dv_acc, pb->batch, pb->seqlen, rows, pb->heads_q,
-                     pb->heads_kv, lse_stride, s);
-  if (e != hipSuccess) return hip_status(e);
-  if (is_f32) {
-    return hip_status(launch_bwd_f32(pb->head_dim, (const float*)q, (const float*)k,
-                                     (const float*)v, (const float*)dout, l_ws, d_ws, (float*)dq,
-                                     (float*)dk, (float*)dv, pb->cu_seqlens, pb->batch,
-                                     pb->seqlen, rows, pb->heads_q, pb->heads_kv, window, prefix,
-                                     pb->softmax_scale, s));
+  if (phases & PHASE_PREPARE) {
+    e = launch_bwd_pre(is_f32, pb->head_dim, o, dout, lse, sinks, pb->cu_seqlens, dsinks, d_ws,
+                       l_ws, dq_acc, dk_acc, dv_acc, pb->batch, pb->seqlen, rows, pb->heads_q,
+                       pb->heads_kv, lse_stride, s);
+    if (e != hipSuccess) return hip_status(e);
   }
-  e = launch_bwd_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout, l_ws,
-                          d_ws, dq_acc, dk_acc, dv_acc, pb->cu_seqlens, pb->batch, pb->seqlen,
-                          rows, pb->heads_q, pb->heads_kv, window, prefix, pb->softmax_scale,
-                          choose_heads_per_wg(pb), s);
-  if (e != hipSuccess) return hip_status(e);
-  return hip_status(launch_convert(0, dq_acc, dk_acc, dv_acc, dq, dk, dv,
-                                   (long long)rows * pb->heads_q * pb->head_dim,
-                                   (long long)rows * pb->heads_kv * pb->head_dim,
-                                   pb->softmax_scale, s));
+  if (phases & PHASE_MAIN) {
+    if (is_f32) {
+      e = launch_bwd_f32(pb->head_dim, (const float*)q, (const float*)k, (const float*)v,
+                         (const float*)dout, l_ws, d_ws, (float*)dq, (float*)dk, (float*)dv,
+                         pb->cu_seqlens, pb->batch, pb->seqlen, rows, pb->heads_q, pb->heads_kv,
+                         window, prefix, pb->softmax_scale, s);
+    } else {
+      e = launch_bwd_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
+                              l_ws, d_ws, dq_acc, dk_acc, dv_acc, pb->cu_seqlens, pb->batch,
+                              pb->seqlen, rows, pb->heads_q, pb->heads_kv, window, prefix,
+                              pb->softmax_scale, choose_heads_per_wg(pb), s);
+    }
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if ((phases & PHASE_FINISH) && !is_f32) {
+    e = launch_convert(0, dq_acc, dk_acc, dv_acc, dq, dk, dv,
+                       (long long)rows * pb->heads_q * pb->head_dim,
+                       (long long)rows * pb->heads_kv * pb->head_dim, pb->softmax_scale, s);
+  }
+  return hip_status(e);
+}
+
+#define SINKATTN_BWD_ARGS                                                                   \
+  const sinkattn_problem *pb, const void *q, const void *k, const void *v,                 \
+      const float *sinks, const void *o, const float *lse, const void *dout, void *dq,     \
+      void *dk, void *dv, float *dsinks, void *workspace, size_t workspace_bytes,          \
+      void *stream
+#define SINKATTN_BWD_PASS q, k, v, sinks, o, lse, dout, dq, dk, dv, dsinks, workspace, workspace_bytes, stream
+
+sinkattn_status sinkattn_bwd(SINKATTN_BWD_ARGS) {
+  return bwd_phases(PHASE_ALL, pb, SINKATTN_BWD_PASS);
+}
+sinkattn_status sinkattn_bwd_prepare(SINKATTN_BWD_ARGS) {
+  return bwd_phases(PHASE_PREPARE, pb, SINKATTN_BWD_PASS);
+}
+sinkattn_status sinkattn_bwd_main(SINKATTN_BWD_ARGS) {
+  return bwd_phases(PHASE_MAIN, pb, SINKATTN_BWD_PASS);
+}
+sinkattn_status sinkattn_bwd_finish(SINKATTN_BWD_ARGS) {
+  return bwd_phases(PHASE_FINISH, pb, SINKATTN_BWD_PASS);
 }
 
 }  // extern "C"

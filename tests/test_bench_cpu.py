@@ -1,0 +1,36 @@
+"""Host-side logic of the benchmark (no GPU): the useful-pair count that
+the TFLOP/s figures are built on, against brute-force counting of the
+oracle's mask, and the single-GPU guard."""
+import numpy as np
+import pytest
+
+import bench
+import oracle
+from workloads import WINDOW_INF, make_inputs
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 64, 130])
+@pytest.mark.parametrize("w,p", [(0, 0), (3, 0), (0, 4), (16, 4), (128, 16), (WINDOW_INF, 0),
+                                 (200, 0), (2, 300)])
+def test_visible_pairs_closed_form(n, w, p):
+    assert bench.visible_pairs_per_head(n, w, p) == int(oracle.visible_mask(n, w, p).sum())
+
+
+def test_useful_pairs_varlen_and_batched():
+    inp = make_inputs(batch=0, seqlen=0, heads_q=4, heads_kv=2, head_dim=8, window=5, prefix=2,
+                      seed=1, dtype="fp32", lengths=(3, 0, 17))
+    want = 4 * sum(int(oracle.visible_mask(n, 5, 2).sum()) for n in (3, 0, 17))
+    assert bench.useful_pairs(inp) == want
+    inp = make_inputs(batch=3, seqlen=20, heads_q=2, heads_kv=1, head_dim=8, window=WINDOW_INF,
+                      prefix=0, seed=1, dtype="fp32")
+    assert bench.useful_pairs(inp) == 3 * 2 * 20 * 21 // 2
+
+
+def test_target_workload_flop_count():
+    # T=8192 full causal, Hq=64, d=64: 2,147,745,792 visible pairs, 896 FLOP each
+    assert 64 * bench.visible_pairs_per_head(8192, WINDOW_INF, 0) == 2_147_745_792
+    assert 64 * bench.visible_pairs_per_head(8192, 128, 4) == 69_168_512
+
+
+def test_multi_gpu_request_refused():
+    assert bench.main(["--gpus", "2"]) == 2
