@@ -38,8 +38,13 @@ CPU_SAMPLE_HEADS = 4
 
 KERNEL_SOURCES = {
     "sinkattn_fwd_bf16_d64": ["fwd_bf16.hip", "common.h", "mask_tiles.h"],
-    "sinkattn_bwd_bf16_d64": ["bwd_bf16.hip", "common.h", "mask_tiles.h"],
+    "sinkattn_bwd_dkdv_bf16_d64": ["bwd_bf16.hip", "common.h", "mask_tiles.h"],
+    "sinkattn_bwd_dq_bf16_d64": ["bwd_dq_bf16.hip", "common.h", "mask_tiles.h"],
 }
+# useful FLOP per visible pair of each kernel (d = head dim): forward QK^T and PV;
+# dK/dV kernel S, dP, dV, dK; dQ kernel dQ (its recomputed S and dP are not useful work)
+KERNEL_FLOP_PER_PAIR = {"sinkattn_fwd_bf16_d64": 4, "sinkattn_bwd_dkdv_bf16_d64": 8,
+                        "sinkattn_bwd_dq_bf16_d64": 2}
 
 
 def visible_pairs_per_head(n: int, window: int, prefix: int) -> int:
@@ -134,10 +139,9 @@ def main(argv=None):
 
     import torch
 
-    from sink_aware_masked_sinkattn_amd import (load_library, sinkattn_bwd_finish,
-                                                sinkattn_bwd_main, sinkattn_bwd_prepare,
-                                                sinkattn_bwd_workspace_size, sinkattn_fwd,
-                                                make_problem)
+    from sink_aware_masked_sinkattn_amd import (BWD_DKDV, BWD_DQ, BWD_FINISH, BWD_PREPARE,
+                                                load_library, make_problem, sinkattn_bwd_phases,
+                                                sinkattn_bwd_workspace_size, sinkattn_fwd)
     from workloads import WORKLOADS, workload_inputs
 
     if not torch.cuda.is_available():
@@ -186,15 +190,10 @@ def main(argv=None):
                 ev[1].record()
             bargs = (*a, r["o"], r["lse"], r["do"], inp.window, inp.prefix, inp.scale, r["cu"],
                      r["ms"])
-            sinkattn_bwd_prepare(*bargs, workspace=r["ws"], grads=r["grads"])
-            if ev:
-                ev[2].record()
-            sinkattn_bwd_main(*bargs, workspace=r["ws"], grads=r["grads"])
-            if ev:
-                ev[3].record()
-            sinkattn_bwd_finish(*bargs, workspace=r["ws"], grads=r["grads"])
-            if ev:
-                ev[4].record()
+            for j, ph in enumerate((BWD_PREPARE, BWD_DKDV, BWD_DQ, BWD_FINISH)):
+                sinkattn_bwd_phases(ph, *bargs, workspace=r["ws"], grads=r["grads"])
+                if ev:
+                    ev[2 + j].record()
 
     step()
     torch.cuda.synchronize()
@@ -207,7 +206,7 @@ def main(argv=None):
     torch.cuda.synchronize()
 
     K = args.steps
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in runs]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in runs]
               for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -221,18 +220,19 @@ def main(argv=None):
     per_layer = []
     for li, r in enumerate(runs):
         ph = [sum(events[i][li][j].elapsed_time(events[i][li][j + 1]) for i in range(K)) / K
-              for j in range(4)]
+              for j in range(5)]
         per_layer.append({"window": r["inp"].window, "prefix": r["inp"].prefix,
                           "pairs": r["pairs"], "fwd_ms": ph[0], "bwd_prepare_ms": ph[1],
-                          "bwd_main_ms": ph[2], "bwd_finish_ms": ph[3]})
+                          "bwd_dkdv_ms": ph[2], "bwd_dq_ms": ph[3], "bwd_finish_ms": ph[4]})
     total_flops = sum(14 * d * r["pairs"] for r in runs)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
     # dominant kernel: the one with the largest total time per step
-    kern_time = {"sinkattn_fwd_bf16_d64": sum(p["fwd_ms"] for p in per_layer),
-                 "sinkattn_bwd_bf16_d64": sum(p["bwd_main_ms"] for p in per_layer)}
-    kern_flops = {"sinkattn_fwd_bf16_d64": sum(4 * d * p["pairs"] for p in per_layer),
-                  "sinkattn_bwd_bf16_d64": sum(10 * d * p["pairs"] for p in per_layer)}
+    phase_of = {"sinkattn_fwd_bf16_d64": "fwd_ms", "sinkattn_bwd_dkdv_bf16_d64": "bwd_dkdv_ms",
+                "sinkattn_bwd_dq_bf16_d64": "bwd_dq_ms"}
+    kern_time = {k: sum(p[ph] for p in per_layer) for k, ph in phase_of.items()}
+    kern_flops = {k: sum(KERNEL_FLOP_PER_PAIR[k] * d * p["pairs"] for p in per_layer)
+                  for k in phase_of}
     dom = max(kern_time, key=kern_time.get)
     launches = len(per_layer)
     avg_ms = kern_time[dom] / launches
@@ -248,13 +248,14 @@ def main(argv=None):
     causal_info = None
     if causal:
         p = causal[0]
-        t_ms = p["fwd_ms"] + p["bwd_prepare_ms"] + p["bwd_main_ms"] + p["bwd_finish_ms"]
+        t_ms = (p["fwd_ms"] + p["bwd_prepare_ms"] + p["bwd_dkdv_ms"] + p["bwd_dq_ms"] +
+                p["bwd_finish_ms"])
+        t_bwd = t_ms - p["fwd_ms"]
         tf = 14 * d * p["pairs"] / (t_ms * 1e-3) / 1e12
         causal_info = {"ms": round(t_ms, 4), "useful_tflops": round(tf, 2),
                        "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                        "fwd_tflops": round(4 * d * p["pairs"] / (p["fwd_ms"] * 1e-3) / 1e12, 2),
-                       "bwd_main_tflops": round(10 * d * p["pairs"] / (p["bwd_main_ms"] * 1e-3)
-                                                / 1e12, 2)}
+                       "bwd_tflops": round(10 * d * p["pairs"] / (t_bwd * 1e-3) / 1e12, 2)}
 
     cpu = None
     if not args.no_cpu_baseline:

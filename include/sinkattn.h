@@ -53,8 +53,9 @@
  *   - cu_seqlens contents are a caller contract, not checked: cu[0] = 0,
  *     non-decreasing, cu[batch] = total_tokens, every length <= seqlen.
  *   - No global mutable state: concurrent calls on different streams are safe.
- *   - Results of the backward are not bitwise reproducible run to run (float
- *     atomics in dQ and ds_h); they are reproducible to rounding.
+ *   - The forward and dQ are bitwise reproducible.  ds_h (float atomics over
+ *     waves) and, for long key ranges, dK/dV (float atomics over work chunks)
+ *     are reproducible to rounding, not bitwise.
  */
 #ifndef SINKATTN_H
 #define SINKATTN_H
@@ -121,35 +122,36 @@ sinkattn_status sinkattn_bwd(const sinkattn_problem *problem, const void *q,
                              void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * The same backward as three stream-ordered phases, for callers that want to
- * place work (or timing events) between them.  Each takes exactly the
- * arguments of sinkattn_bwd, validates them the same way, and must be called
- * in this order, on one stream, with the same arguments and workspace:
- *   prepare: clears dsinks, then the row pass D = rowsum(dout * o),
- *            L = logaddexp(lse, s_h), dsinks (the sink gradient of "GPT-OSS
- *            Agentic RL training: a practical retrospective", FlashAttention
- *            v3 implementation section), and clears the accumulators;
- *   main:    dQ, dK, dV from the recomputed probabilities exp(S - L)
- *            (into the workspace accumulators for bf16, into dq/dk/dv for fp32);
- *   finish:  scales and converts the accumulators into dq, dk, dv (bf16; a
- *            no-op for fp32).
- * sinkattn_bwd == prepare; main; finish.
+ * The same backward in stream-ordered phases, for callers that want to place
+ * work (or timing events) between them.  `phases` is a non-empty OR of the
+ * flags below (other bits: SINKATTN_ERR_BAD_SHAPE); the other arguments are
+ * exactly those of sinkattn_bwd and are validated the same way.  Phases must
+ * run in flag order across calls on one stream, with the same arguments and
+ * workspace; DKDV and DQ depend only on PREPARE, FINISH on DKDV.
+ *   PREPARE: clears dsinks, then the row pass D = rowsum(dout * o),
+ *            L = logaddexp(lse, s_h) and dsinks (the sink gradient of
+ *            "GPT-OSS Agentic RL training: a practical retrospective",
+ *            FlashAttention v3 implementation section); clears accumulators;
+ *   DKDV:    dK, dV from the recomputed probabilities exp(S - L) (bf16: into
+ *            fp32 workspace accumulators; fp32: into dk, dv);
+ *   DQ:      dQ, written to dq;
+ *   FINISH:  scales and converts the dK/dV accumulators into dk, dv (bf16;
+ *            nothing to do for fp32).
+ * sinkattn_bwd(...) == sinkattn_bwd_phases(SINKATTN_BWD_ALL, ...).
  */
-sinkattn_status sinkattn_bwd_prepare(const sinkattn_problem *problem, const void *q,
-                                     const void *k, const void *v, const float *sinks,
-                                     const void *o, const float *lse, const void *dout,
-                                     void *dq, void *dk, void *dv, float *dsinks,
-                                     void *workspace, size_t workspace_bytes, void *stream);
-sinkattn_status sinkattn_bwd_main(const sinkattn_problem *problem, const void *q,
-                                  const void *k, const void *v, const float *sinks,
-                                  const void *o, const float *lse, const void *dout,
-                                  void *dq, void *dk, void *dv, float *dsinks,
-                                  void *workspace, size_t workspace_bytes, void *stream);
-sinkattn_status sinkattn_bwd_finish(const sinkattn_problem *problem, const void *q,
-                                    const void *k, const void *v, const float *sinks,
-                                    const void *o, const float *lse, const void *dout,
-                                    void *dq, void *dk, void *dv, float *dsinks,
-                                    void *workspace, size_t workspace_bytes, void *stream);
+enum {
+  SINKATTN_BWD_PREPARE = 1,
+  SINKATTN_BWD_DKDV = 2,
+  SINKATTN_BWD_DQ = 4,
+  SINKATTN_BWD_FINISH = 8,
+  SINKATTN_BWD_ALL = 15
+};
+sinkattn_status sinkattn_bwd_phases(uint32_t phases, const sinkattn_problem *problem,
+                                    const void *q, const void *k, const void *v,
+                                    const float *sinks, const void *o, const float *lse,
+                                    const void *dout, void *dq, void *dk, void *dv,
+                                    float *dsinks, void *workspace, size_t workspace_bytes,
+                                    void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *sinkattn_status_string(sinkattn_status status);

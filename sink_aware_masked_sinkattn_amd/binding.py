@@ -22,6 +22,13 @@ WINDOW_INF = 2**31 - 1          # SINKATTN_WINDOW_INF
 SINKATTN_BF16 = 0
 SINKATTN_FP32 = 1
 
+# backward phase flags (sinkattn_bwd_phases)
+BWD_PREPARE = 1
+BWD_DKDV = 2
+BWD_DQ = 4
+BWD_FINISH = 8
+BWD_ALL = 15
+
 STATUS = {
     0: "SINKATTN_OK",
     1: "SINKATTN_ERR_NULL_POINTER",
@@ -75,11 +82,11 @@ def load_library(path: str = LIB_PATH):
     pp = ctypes.POINTER(Problem)
     lib.sinkattn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp]
     lib.sinkattn_fwd.restype = ctypes.c_int
-    for name in ("sinkattn_bwd", "sinkattn_bwd_prepare", "sinkattn_bwd_main",
-                 "sinkattn_bwd_finish"):
-        fn = getattr(lib, name)
-        fn.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        fn.restype = ctypes.c_int
+    lib.sinkattn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sinkattn_bwd.restype = ctypes.c_int
+    lib.sinkattn_bwd_phases.argtypes = [ctypes.c_uint32, pp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        vp, vp, vp, sz, vp]
+    lib.sinkattn_bwd_phases.restype = ctypes.c_int
     lib.sinkattn_bwd_workspace_size.argtypes = [pp]
     lib.sinkattn_bwd_workspace_size.restype = sz
     lib.sinkattn_status_string.argtypes = [ctypes.c_int]
@@ -170,8 +177,8 @@ def sinkattn_fwd(q, k, v, sinks, window: int, prefix: int, softmax_scale=None,
     return out, lse
 
 
-def _bwd_call(entry: str, q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale,
-              cu_seqlens, max_seqlen, workspace, grads):
+def _bwd_call(phases: Optional[int], q, k, v, sinks, o, lse, dout, window, prefix,
+              softmax_scale, cu_seqlens, max_seqlen, workspace, grads):
     lib = load_library()
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (sinks, "sinks"), (o, "o"), (lse, "lse"),
                  (dout, "dout")):
@@ -185,9 +192,13 @@ def _bwd_call(entry: str, q, k, v, sinks, o, lse, dout, window, prefix, softmax_
     need = int(lib.sinkattn_bwd_workspace_size(ctypes.byref(pb)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = getattr(lib, entry)(ctypes.byref(pb), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o),
-                             _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks),
-                             _ptr(workspace), workspace.numel(), _stream())
+    args = (ctypes.byref(pb), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(o), _ptr(lse),
+            _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dsinks), _ptr(workspace),
+            workspace.numel(), _stream())
+    if phases is None:
+        st, entry = lib.sinkattn_bwd(*args), "sinkattn_bwd"
+    else:
+        st, entry = lib.sinkattn_bwd_phases(phases, *args), "sinkattn_bwd_phases"
     if st != 0:
         raise SinkAttnError(st, entry, lib)
     return dq, dk, dv, dsinks
@@ -198,28 +209,18 @@ def sinkattn_bwd(q, k, v, sinks, o, lse, dout, window: int, prefix: int, softmax
     """Backward: returns (dq, dk, dv, dsinks).  ``workspace`` (uint8 GPU
     tensor) is allocated here when not given; ``grads`` may pass preallocated
     (dq, dk, dv, dsinks)."""
-    return _bwd_call("sinkattn_bwd", q, k, v, sinks, o, lse, dout, window, prefix,
-                     softmax_scale, cu_seqlens, max_seqlen, workspace, grads)
+    return _bwd_call(None, q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale,
+                     cu_seqlens, max_seqlen, workspace, grads)
 
 
-def sinkattn_bwd_prepare(q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale=None,
-                         cu_seqlens=None, max_seqlen=None, *, workspace, grads):
-    """First backward phase (same arguments as sinkattn_bwd; workspace and
-    grads must be given and reused by the later phases)."""
-    return _bwd_call("sinkattn_bwd_prepare", q, k, v, sinks, o, lse, dout, window, prefix,
-                     softmax_scale, cu_seqlens, max_seqlen, workspace, grads)
-
-
-def sinkattn_bwd_main(q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale=None,
-                      cu_seqlens=None, max_seqlen=None, *, workspace, grads):
-    return _bwd_call("sinkattn_bwd_main", q, k, v, sinks, o, lse, dout, window, prefix,
-                     softmax_scale, cu_seqlens, max_seqlen, workspace, grads)
-
-
-def sinkattn_bwd_finish(q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale=None,
-                        cu_seqlens=None, max_seqlen=None, *, workspace, grads):
-    return _bwd_call("sinkattn_bwd_finish", q, k, v, sinks, o, lse, dout, window, prefix,
-                     softmax_scale, cu_seqlens, max_seqlen, workspace, grads)
+def sinkattn_bwd_phases(phases: int, q, k, v, sinks, o, lse, dout, window, prefix,
+                        softmax_scale=None, cu_seqlens=None, max_seqlen=None, *, workspace,
+                        grads):
+    """Run some phases of the backward (OR of BWD_PREPARE, BWD_DKDV, BWD_DQ,
+    BWD_FINISH); the workspace and grads must be the same across the calls
+    that make up one backward."""
+    return _bwd_call(int(phases), q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale,
+                     cu_seqlens, max_seqlen, workspace, grads)
 
 
 def sinkattn_tile_class(q0: int, q1: int, k0: int, k1: int, window: int, prefix: int) -> int:

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libsinkattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "bwd_aux.hip", "fp32_kernels.hip"]
+SOURCES = ["api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "bwd_dq_bf16.hip", "bwd_aux.hip",
+           "fp32_kernels.hip"]
 
 ARCH = "gfx950"
 COMMON = [

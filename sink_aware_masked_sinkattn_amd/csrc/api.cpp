@@ -15,11 +15,17 @@ hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, cons
                                bf16* o, float* lse, const int* cu_seqlens, int batch, int seqlen,
                                int total_tokens, int heads_q, int heads_kv, int window,
                                int prefix, float scale, hipStream_t stream);
-hipError_t launch_bwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
-                               const float* l_ws, const float* d_ws, float* dq_acc, float* dk_acc,
-                               float* dv_acc, const int* cu_seqlens, int batch, int seqlen,
-                               int rows_total, int heads_q, int heads_kv, int window, int prefix,
-                               float scale, int heads_per_wg, hipStream_t stream);
+hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
+                                    const bf16* dout, const float* l_ws, const float* d_ws,
+                                    float* dk_acc, float* dv_acc, const int* cu_seqlens,
+                                    int batch, int seqlen, int rows_total, int heads_q,
+                                    int heads_kv, int window, int prefix, float scale,
+                                    hipStream_t stream);
+hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
+                                  const float* l_ws, const float* d_ws, bf16* dq,
+                                  const int* cu_seqlens, int batch, int seqlen, int rows_total,
+                                  int heads_q, int heads_kv, int window, int prefix, float scale,
+                                  hipStream_t stream);
 hipError_t launch_fwd_f32(int head_dim, const float* q, const float* k, const float* v,
                           const float* sinks, float* o, float* lse, const int* cu_seqlens,
                           int batch, int seqlen, int total_tokens, int heads_q, int heads_kv,
@@ -28,15 +34,14 @@ hipError_t launch_bwd_f32(int head_dim, const float* q, const float* k, const fl
                           const float* dout, const float* l_ws, const float* d_ws, float* dq,
                           float* dk, float* dv, const int* cu_seqlens, int batch, int seqlen,
                           int total_tokens, int heads_q, int heads_kv, int window, int prefix,
-                          float scale, hipStream_t stream);
+                          float scale, bool do_dq, bool do_dkdv, hipStream_t stream);
 hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const void* dout,
                           const float* lse, const float* sinks, const int* cu_seqlens,
-                          float* dsinks, float* d_ws, float* l_ws, float* dq_acc, float* dk_acc,
-                          float* dv_acc, int batch, int seqlen, int rows_total, int heads_q,
-                          int heads_kv, int lse_head_stride, hipStream_t stream);
-hipError_t launch_convert(int dtype_is_f32, const float* dq_acc, const float* dk_acc,
-                          const float* dv_acc, void* dq, void* dk, void* dv, long long n_q,
-                          long long n_kv, float scale, hipStream_t stream);
+                          float* dsinks, float* d_ws, float* l_ws, float* dk_acc, float* dv_acc,
+                          int batch, int seqlen, int rows_total, int heads_q, int heads_kv,
+                          int lse_head_stride, hipStream_t stream);
+hipError_t launch_convert(int dtype_is_f32, const float* dk_acc, const float* dv_acc, void* dk,
+                          void* dv, long long n_kv, float scale, hipStream_t stream);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
 
 namespace {
@@ -81,7 +86,7 @@ sinkattn_status check_problem(const sinkattn_problem* pb, Dims* dims) {
 }
 
 struct Workspace {
-  size_t d_off, l_off, dq_off, dk_off, dv_off, total;
+  size_t d_off, l_off, dk_off, dv_off, total;
 };
 
 Workspace workspace_layout(const sinkattn_problem* pb, const Dims& dims) {
@@ -89,30 +94,16 @@ Workspace workspace_layout(const sinkattn_problem* pb, const Dims& dims) {
   const size_t rows = (size_t)dims.rows;
   const size_t stat = round_up(rows * (size_t)pb->heads_q * sizeof(float));
   const bool accum = pb->dtype == SINKATTN_BF16;   // fp32 path writes outputs directly
-  const size_t qacc = accum ? round_up(rows * pb->heads_q * pb->head_dim * sizeof(float)) : 0;
   const size_t kvacc = accum ? round_up(rows * pb->heads_kv * pb->head_dim * sizeof(float)) : 0;
   w.d_off = 0;
   w.l_off = stat;
-  w.dq_off = 2 * stat;
-  w.dk_off = w.dq_off + qacc;
+  w.dk_off = 2 * stat;
   w.dv_off = w.dk_off + kvacc;
   w.total = w.dv_off + kvacc;
   return w;
 }
 
 sinkattn_status hip_status(hipError_t e) { return e == hipSuccess ? SINKATTN_OK : SINKATTN_ERR_HIP; }
-
-// query heads per backward workgroup: the whole GQA group unless that leaves
-// too few workgroups to fill the chip
-int choose_heads_per_wg(const sinkattn_problem* pb) {
-  const int group = pb->heads_q / pb->heads_kv;
-  const long long kblocks = ((long long)pb->seqlen + 127) / 128;
-  int hpw = group;
-  while (hpw > 1 && (hpw % 2 == 0) &&
-         (long long)pb->batch * pb->heads_kv * (group / hpw) * kblocks < 2048)
-    hpw /= 2;
-  return hpw;
-}
 
 }  // namespace
 
@@ -178,9 +169,8 @@ sinkattn_status sinkattn_fwd(const sinkattn_problem* pb, const void* q, const vo
                                    pb->heads_kv, window, prefix, pb->softmax_scale, s));
 }
 
-enum { PHASE_PREPARE = 1, PHASE_MAIN = 2, PHASE_FINISH = 4, PHASE_ALL = 7 };
 
-static sinkattn_status bwd_phases(int phases, const sinkattn_problem* pb, const void* q,
+static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, const void* q,
                                   const void* k, const void* v, const float* sinks, const void* o,
                                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
                                   float* dsinks, void* workspace, size_t workspace_bytes,
@@ -204,7 +194,7 @@ static sinkattn_status bwd_phases(int phases, const sinkattn_problem* pb, const 
   }
   // ---- validation done; device work from here on
   hipError_t e = hipSuccess;
-  if (phases & PHASE_PREPARE) {
+  if (phases & SINKATTN_BWD_PREPARE) {
     e = launch_zero_f32(dsinks, pb->heads_q, s);
     if (e != hipSuccess) return hip_status(e);
   }
@@ -214,37 +204,43 @@ static sinkattn_status bwd_phases(int phases, const sinkattn_problem* pb, const 
   float* d_ws = (float*)(ws + wl.d_off);
   float* l_ws = (float*)(ws + wl.l_off);
   const bool is_f32 = pb->dtype == SINKATTN_FP32;
-  float* dq_acc = is_f32 ? nullptr : (float*)(ws + wl.dq_off);
   float* dk_acc = is_f32 ? nullptr : (float*)(ws + wl.dk_off);
   float* dv_acc = is_f32 ? nullptr : (float*)(ws + wl.dv_off);
   const int window = pb->window > pb->seqlen ? pb->seqlen : pb->window;
   const int prefix = pb->prefix > pb->seqlen ? pb->seqlen : pb->prefix;
   const int rows = (int)dims.rows;
   const int lse_stride = dims.varlen ? rows : pb->seqlen;
-  if (phases & PHASE_PREPARE) {
+  if (phases & SINKATTN_BWD_PREPARE) {
     e = launch_bwd_pre(is_f32, pb->head_dim, o, dout, lse, sinks, pb->cu_seqlens, dsinks, d_ws,
-                       l_ws, dq_acc, dk_acc, dv_acc, pb->batch, pb->seqlen, rows, pb->heads_q,
+                       l_ws, dk_acc, dv_acc, pb->batch, pb->seqlen, rows, pb->heads_q,
                        pb->heads_kv, lse_stride, s);
     if (e != hipSuccess) return hip_status(e);
   }
-  if (phases & PHASE_MAIN) {
-    if (is_f32) {
-      e = launch_bwd_f32(pb->head_dim, (const float*)q, (const float*)k, (const float*)v,
-                         (const float*)dout, l_ws, d_ws, (float*)dq, (float*)dk, (float*)dv,
-                         pb->cu_seqlens, pb->batch, pb->seqlen, rows, pb->heads_q, pb->heads_kv,
-                         window, prefix, pb->softmax_scale, s);
-    } else {
-      e = launch_bwd_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
-                              l_ws, d_ws, dq_acc, dk_acc, dv_acc, pb->cu_seqlens, pb->batch,
-                              pb->seqlen, rows, pb->heads_q, pb->heads_kv, window, prefix,
-                              pb->softmax_scale, choose_heads_per_wg(pb), s);
-    }
+  if (is_f32 && (phases & (SINKATTN_BWD_DKDV | SINKATTN_BWD_DQ))) {
+    // the fp32 path computes dQ and dK/dV in one call (both into the outputs)
+    e = launch_bwd_f32(pb->head_dim, (const float*)q, (const float*)k, (const float*)v,
+                       (const float*)dout, l_ws, d_ws, (float*)dq, (float*)dk, (float*)dv,
+                       pb->cu_seqlens, pb->batch, pb->seqlen, rows, pb->heads_q, pb->heads_kv,
+                       window, prefix, pb->softmax_scale, (phases & SINKATTN_BWD_DQ) != 0,
+                       (phases & SINKATTN_BWD_DKDV) != 0, s);
     if (e != hipSuccess) return hip_status(e);
   }
-  if ((phases & PHASE_FINISH) && !is_f32) {
-    e = launch_convert(0, dq_acc, dk_acc, dv_acc, dq, dk, dv,
-                       (long long)rows * pb->heads_q * pb->head_dim,
-                       (long long)rows * pb->heads_kv * pb->head_dim, pb->softmax_scale, s);
+  if (!is_f32 && (phases & SINKATTN_BWD_DKDV)) {
+    e = launch_bwd_dkdv_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v,
+                                 (const bf16*)dout, l_ws, d_ws, dk_acc, dv_acc, pb->cu_seqlens,
+                                 pb->batch, pb->seqlen, rows, pb->heads_q, pb->heads_kv, window,
+                                 prefix, pb->softmax_scale, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (!is_f32 && (phases & SINKATTN_BWD_DQ)) {
+    e = launch_bwd_dq_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
+                               l_ws, d_ws, (bf16*)dq, pb->cu_seqlens, pb->batch, pb->seqlen, rows,
+                               pb->heads_q, pb->heads_kv, window, prefix, pb->softmax_scale, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if ((phases & SINKATTN_BWD_FINISH) && !is_f32) {
+    e = launch_convert(0, dk_acc, dv_acc, dk, dv, (long long)rows * pb->heads_kv * pb->head_dim,
+                       pb->softmax_scale, s);
   }
   return hip_status(e);
 }
@@ -257,16 +253,12 @@ static sinkattn_status bwd_phases(int phases, const sinkattn_problem* pb, const 
 #define SINKATTN_BWD_PASS q, k, v, sinks, o, lse, dout, dq, dk, dv, dsinks, workspace, workspace_bytes, stream
 
 sinkattn_status sinkattn_bwd(SINKATTN_BWD_ARGS) {
-  return bwd_phases(PHASE_ALL, pb, SINKATTN_BWD_PASS);
+  return bwd_phases(SINKATTN_BWD_ALL, pb, SINKATTN_BWD_PASS);
 }
-sinkattn_status sinkattn_bwd_prepare(SINKATTN_BWD_ARGS) {
-  return bwd_phases(PHASE_PREPARE, pb, SINKATTN_BWD_PASS);
-}
-sinkattn_status sinkattn_bwd_main(SINKATTN_BWD_ARGS) {
-  return bwd_phases(PHASE_MAIN, pb, SINKATTN_BWD_PASS);
-}
-sinkattn_status sinkattn_bwd_finish(SINKATTN_BWD_ARGS) {
-  return bwd_phases(PHASE_FINISH, pb, SINKATTN_BWD_PASS);
+
+sinkattn_status sinkattn_bwd_phases(uint32_t phases, SINKATTN_BWD_ARGS) {
+  if (phases == 0 || (phases & ~(uint32_t)SINKATTN_BWD_ALL) != 0) return SINKATTN_ERR_BAD_SHAPE;
+  return bwd_phases(phases, pb, SINKATTN_BWD_PASS);
 }
 
 }  // extern "C"

@@ -1,5 +1,5 @@
-// Backward helpers around the main kernel: the row preprocessing pass and the
-// accumulator conversion pass.  Both are HBM-bound streaming kernels.
+// Backward helpers around the dK/dV and dQ kernels: the row preprocessing
+// pass and the dK/dV conversion pass.  Both are HBM-bound streaming kernels.
 //
 // Preprocessing, per (row i, query head h) -- the sink gradient of "GPT-OSS
 // Agentic RL training: a practical retrospective" (FlashAttention v3
@@ -10,9 +10,8 @@
 //   ds_h -= exp(s_h - L_i) D_i               (summed over all rows)
 // D and L go to the workspace for the main kernel.  The ds_h partial sums of
 // a wave are reduced with cross-lane shuffles, then added with one float
-// atomic per wave.  The same pass zeroes the fp32 accumulators of dQ (and,
-// from the first query head of each group, of dK and dV), so no separate
-// memset is needed.
+// atomic per wave.  The same pass zeroes the fp32 dK and dV accumulators
+// (from the first query head of each group), so no separate memset is needed.
 #include "common.h"
 
 namespace {
@@ -37,7 +36,6 @@ struct PreArgs {
   float* dsinks;
   float* d_ws;        // [Hq, rows] : D_i
   float* l_ws;        // [Hq, rows] : L_i (natural log)
-  float* dq_acc;      // [rows, Hq, D] fp32, zeroed here (may be null)
   float* dk_acc;      // [rows, Hkv, D] fp32, zeroed here (may be null)
   float* dv_acc;
   int seqlen, heads_q, heads_kv, group, rows_total;
@@ -74,11 +72,6 @@ __global__ __launch_bounds__(256) void sinkattn_bwd_pre(PreArgs a) {
       const T* pd = dout + off;
 #pragma unroll
       for (int e = 0; e < RS::kElems; ++e) dot += to_f32(po[e]) * to_f32(pd[e]);
-      if (a.dq_acc) {
-        float4* pz = (float4*)(a.dq_acc + off);
-#pragma unroll
-        for (int e = 0; e < RS::kElems / 4; ++e) pz[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
       if (zero_kv) {
         const size_t koff = (row * a.heads_kv + kvh) * D + sub * RS::kElems;
         float4* pk = (float4*)(a.dk_acc + koff);
@@ -112,8 +105,8 @@ __global__ void sinkattn_zero_f32(float* p, int n) {
   if (i < n) p[i] = 0.0f;
 }
 
-// fp32 accumulators -> output dtype, with the softmax scale folded into dQ
-// and dK here (the main kernel accumulates dS K and dS^T Q unscaled).
+// fp32 dK / dV accumulators -> output dtype, with the softmax scale folded
+// into dK here (the dK/dV kernel accumulates dS^T Q unscaled).
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, float4 v);
 template <>
@@ -126,15 +119,9 @@ __device__ __forceinline__ void store4<float>(float* dst, float4 v) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void sinkattn_convert(const float* dq_acc, const float* dk_acc,
-                                                        const float* dv_acc, T* dq, T* dk, T* dv,
-                                                        long long n_q4, long long n_kv4, float scale) {
+__global__ __launch_bounds__(256) void sinkattn_convert(const float* dk_acc, const float* dv_acc,
+                                                        T* dk, T* dv, long long n_kv4, float scale) {
   const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n_q4; i += stride) {
-    float4 x = ((const float4*)dq_acc)[i];
-    x.x *= scale; x.y *= scale; x.z *= scale; x.w *= scale;
-    store4<T>(dq + 4 * i, x);
-  }
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n_kv4; i += stride) {
     float4 x = ((const float4*)dk_acc)[i];
     x.x *= scale; x.y *= scale; x.z *= scale; x.w *= scale;
@@ -153,13 +140,13 @@ hipError_t launch_zero_f32(float* p, int n, hipStream_t stream) {
 
 hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const void* dout,
                           const float* lse, const float* sinks, const int* cu_seqlens,
-                          float* dsinks, float* d_ws, float* l_ws, float* dq_acc, float* dk_acc,
-                          float* dv_acc, int batch, int seqlen, int rows_total, int heads_q,
-                          int heads_kv, int lse_head_stride, hipStream_t stream) {
+                          float* dsinks, float* d_ws, float* l_ws, float* dk_acc, float* dv_acc,
+                          int batch, int seqlen, int rows_total, int heads_q, int heads_kv,
+                          int lse_head_stride, hipStream_t stream) {
   PreArgs a;
   a.o = o; a.dout = dout; a.lse = lse; a.sinks = sinks; a.cu_seqlens = cu_seqlens;
   a.dsinks = dsinks; a.d_ws = d_ws; a.l_ws = l_ws;
-  a.dq_acc = dq_acc; a.dk_acc = dk_acc; a.dv_acc = dv_acc;
+  a.dk_acc = dk_acc; a.dv_acc = dv_acc;
   a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
   a.group = heads_q / heads_kv; a.rows_total = rows_total;
   a.lse_head_stride = lse_head_stride;
@@ -178,21 +165,18 @@ hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const v
   return hipGetLastError();
 }
 
-hipError_t launch_convert(int dtype_is_f32, const float* dq_acc, const float* dk_acc,
-                          const float* dv_acc, void* dq, void* dk, void* dv, long long n_q,
-                          long long n_kv, float scale, hipStream_t stream) {
-  const long long n4 = (n_q / 4 > n_kv / 4) ? n_q / 4 : n_kv / 4;
+hipError_t launch_convert(int dtype_is_f32, const float* dk_acc, const float* dv_acc, void* dk,
+                          void* dv, long long n_kv, float scale, hipStream_t stream) {
+  const long long n4 = n_kv / 4;
   if (n4 == 0) return hipSuccess;
   long long blocks = (n4 + 255) / 256;
   if (blocks > 256 * 16) blocks = 256 * 16;
   if (dtype_is_f32) {
     hipLaunchKernelGGL(sinkattn_convert<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       dq_acc, dk_acc, dv_acc, (float*)dq, (float*)dk, (float*)dv, n_q / 4,
-                       n_kv / 4, scale);
+                       dk_acc, dv_acc, (float*)dk, (float*)dv, n4, scale);
   } else {
     hipLaunchKernelGGL(sinkattn_convert<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       dq_acc, dk_acc, dv_acc, (bf16*)dq, (bf16*)dk, (bf16*)dv, n_q / 4,
-                       n_kv / 4, scale);
+                       dk_acc, dv_acc, (bf16*)dk, (bf16*)dv, n4, scale);
   }
   return hipGetLastError();
 }

@@ -1,36 +1,33 @@
-// Backward of sink-aware masked attention, bf16, head dim 64, on gfx950 MFMA.
+// dK and dV of sink-aware masked attention, bf16, head dim 64, gfx950 MFMA.
 //
-// Given the saved content-only log-sum-exp l and the preprocessing pass's
-// D_i = rowsum(dO * O) and L_i = logaddexp(l_i, s_h) (sink-inclusive), the
-// gradients of attention with a zero-value sink key (arXiv 2608.10357,
-// section 5, "Zero-value sink equivalence"; per-head sink gradient as in
-// "GPT-OSS Agentic RL training: a practical retrospective", FlashAttention
-// v3 implementation section) are, for visible pairs only:
-//   P'_ij = exp(S_ij - L_i)            (S_ij = scale q_i . k_j)
-//   dV_j += P'_ij dO_i
-//   dS_ij = P'_ij (dO_i . v_j - D_i)
-//   dK_j += scale dS_ij q_i,  dQ_i += scale dS_ij k_j
-// The score matrix is recomputed tile by tile from Q, K and L; nothing of
-// size T x T is ever stored (the O(n^2) structure the same section warns of).
+// With the preprocessing pass's L_i = logaddexp(l_i, s_h) and
+// D_i = rowsum(dO * O), for the visible pairs of the mask
+// M[q,k] = 1[k<=q] AND 1[q-k<=w OR k<p] ("Efficient Reinforcement Learning
+// for Long-Horizon Tool-Use Agentic Tasks", summary page; the zero-value
+// sink of arXiv 2608.10357 section 5 only enters through L and D):
+//   P'_ij = exp(S_ij - L_i),  S_ij = scale q_i . k_j
+//   dV_j += sum_i P'_ij dO_i
+//   dK_j += scale sum_i P'_ij (dO_i . v_j - D_i) q_i
+// summed over the query heads of the kv head's GQA group.  No T x T buffer:
+// S and dP are recomputed tile by tile from Q, K, V, dO and L.
 //
-// Work decomposition: one workgroup = 4 waves = 128 keys of one kv head
-// (32 keys per wave, K and V fragments held in registers), looping over the
-// query heads it is given and, per head, over the 64-row query tiles that
-// can see its keys (from the mask: the rows of a prefix key run to the end
-// of the sequence, those of a window key to k + w).  Per query tile:
-//   1. S = Q K^T and dP = dO V^T on MFMA with one key per lane (C layout),
-//      so P' and dS come out in registers already shaped as the A operand
-//      of dV += P'^T dO and dK += dS^T Q; their B operands (dO, Q with the
-//      query index along k) are LDS transpose reads of the row-major tiles;
-//   2. dS is written to LDS as dS^T [key][query] (8-byte stores);
-//   3. dQ (64 x 64) = dS (64 x 128) K (128 x 64) is split over the 4 waves
-//      (one 32 x 32 block each, both operands by transpose reads) and added
-//      to the fp32 dQ accumulator with one float atomic per element, so the
-//      accumulator sees one add per 128 keys instead of per 32.
-// dK and dV (fp32, registers) are added to fp32 accumulators at the end; a
-// conversion pass applies the scale and writes bf16.  Query/dO tiles are
-// double-buffered through registers and LDS.  Rows past the end of a
-// sequence get L = +inf (so P' = 0) and are never written.
+// Work decomposition.  A workgroup (4 waves) owns 128 keys of one kv head,
+// 32 per wave, whose K and V fragments stay in registers.  The (query head,
+// 64-row query tile) pairs that can see those keys -- rows [k0, n) for a
+// prefix key, [k0, k1 + w] otherwise -- form a flat iteration list that is
+// cut into chunks of `chunk` iterations, one workgroup per chunk, so that
+// prefix keys (seen by every later row) and early causal keys do not leave
+// one workgroup running long after the rest.  A key block covered by one
+// chunk stores its fp32 result; a key block cut into several chunks adds
+// them with one float atomic per element, once per chunk.
+//
+// Per iteration, per wave, on MFMA 32x32x16 with one key per lane (C layout):
+//   S = Q K^T, dP = dO V^T   (A = Q, dO rows from LDS; B = K, V registers)
+//   P' and dS computed in registers are already the A operand (keys on m,
+//   queries on k) of dV += P'^T dO and dK += dS^T Q, whose B operands
+//   (queries on k) are transpose reads of the row-major dO and Q tiles.
+// Query tiles (Q, dO, L, D) are double-buffered: registers -> LDS.  Rows
+// past the end of a sequence get L = +inf, so P' = dS = 0 there.
 #include "common.h"
 #include "mask_tiles.h"
 
@@ -41,44 +38,116 @@ constexpr int WAVES = 4;
 constexpr int KW = 32;                 // keys per wave
 constexpr int BKW = WAVES * KW;        // 128 keys per workgroup
 constexpr int BQ = 64;                 // query rows per tile
-constexpr int LROW = D + 8;            // padded bf16 row of Q, dO, K tiles
-constexpr int SROW = BQ + 8;           // padded bf16 row of dS^T [key][query]
 
-struct BwdArgs {
+struct DkvArgs {
   const bf16* q;
   const bf16* k;
   const bf16* v;
   const bf16* dout;
-  const float* l_ws;      // [Hq, rows] L = logaddexp(l, s) (natural log)
-  const float* d_ws;      // [Hq, rows] D = rowsum(dO * O)
-  float* dq_acc;          // [rows, Hq, D]  sum dS K (unscaled)
+  const float* l_ws;      // [Hq, rows] L (natural log)
+  const float* d_ws;      // [Hq, rows] D
   float* dk_acc;          // [rows, Hkv, D] sum dS^T Q (unscaled)
   float* dv_acc;          // [rows, Hkv, D] sum P'^T dO
   const int* cu_seqlens;
   int seqlen, heads_q, heads_kv, group, window, prefix, rows_total;
-  int heads_per_wg;       // query heads handled by one workgroup (divides group)
-  int num_k_blocks;
-  float scale_log2;       // scale * log2(e)
+  int chunk;              // iterations per workgroup
+  int max_chunks;         // grid z = batch * max_chunks
+  float scale_log2;
 };
 
-struct __attribute__((aligned(16))) BwdSmem {
-  bf16 kt[BKW * LROW];          // K rows of this workgroup (for dQ)
-  bf16 qt[2][BQ * LROW];        // Q tile, double buffer
-  bf16 dot[2][BQ * LROW];       // dO tile, double buffer
-  bf16 dst[BKW * SROW];         // dS^T [key][query]
-  float l2[2][BQ];              // L * log2(e); +inf for rows past the end
-  float dd[2][BQ];              // D
+struct __attribute__((aligned(16))) DkvSmem {
+  bf16 qt[2][BQ * D];          // swizzled rows (tile_off)
+  bf16 dot[2][BQ * D];
+  float l2[2][BQ];
+  float dd[2][BQ];
 };
 
-__global__ __launch_bounds__(256, 2) void sinkattn_bwd_bf16_d64(BwdArgs a) {
-  __shared__ BwdSmem sm;
+// One 64-row query tile against this wave's 32 keys.  MASK: apply the element
+// predicate (partial tiles); full tiles run without any mask arithmetic.
+template <bool MASK>
+__device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const float* l2s,
+                                          const float* dds, const bf16x8 (&kf)[4],
+                                          const bf16x8 (&vf)[4], f32x16 (&dk)[2], f32x16 (&dv)[2],
+                                          int q0, int kw0, int window, int prefix,
+                                          float scale_log2, int lane) {
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int grp = lane >> 4;
+  const int li = lane & 15;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    // A operands (query rows, head dim along k) for S = Q K^T and dP = dO V^T
+    bf16x8 qa[4], da[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qa[s] = *(const bf16x8*)(qs + tile_off(qb * 32 + l32, 16 * s + 8 * g));
+      da[s] = *(const bf16x8*)(dos + tile_off(qb * 32 + l32, 16 * s + 8 * g));
+    }
+    f32x16 st = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      st = mfma32x32x16(qa[s], kf[s], st);
+      dp = mfma32x32x16(da[s], vf[s], dp);
+    }
+    // B operands of dV += P'^T dO and dK += dS^T Q (query index along k):
+    // transpose reads; issued before the softmax arithmetic
+    bf16x8 dob[2][2], qbt[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r0 = qb * 32 + 16 * hh + 4 * g + (li >> 2);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
+        dob[hh][db] = cat8(lds_read_tr4(dos + tile_off(r0, c0)), lds_read_tr4(dos + tile_off(r0 + 8, c0)));
+        qbt[hh][db] = cat8(lds_read_tr4(qs + tile_off(r0, c0)), lds_read_tr4(qs + tile_off(r0 + 8, c0)));
+      }
+    }
+    // P' = exp2(S*scale*log2e - L*log2e), dS = P' (dP - D); this lane's C rows
+    // are queries qb*32 + 8*(i/4) + 4g + i%4, its column is key kw0 + l32
+    float pp[16], dsv[16];
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int qr = qb * 32 + 8 * i4 + 4 * g;
+      const f32x4 l4 = *(const f32x4*)(l2s + qr);
+      const f32x4 d4 = *(const f32x4*)(dds + qr);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * i4 + e;
+        float p = fast_exp2(fmaf(st[i], scale_log2, -l4[e]));
+        if (MASK) {
+          const int q = q0 + qr + e, k = kw0 + l32;
+          const bool vis = (k <= q) & ((q - k <= window) | (k < prefix));
+          p = vis ? p : 0.0f;
+        }
+        pp[i] = p;
+        dsv[i] = p * (dp[i] - d4[e]);
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const bf16x8 pa = to_bf16x8(pp[8 * hh], pp[8 * hh + 1], pp[8 * hh + 2], pp[8 * hh + 3],
+                                  pp[8 * hh + 4], pp[8 * hh + 5], pp[8 * hh + 6], pp[8 * hh + 7]);
+      const bf16x8 sa = to_bf16x8(dsv[8 * hh], dsv[8 * hh + 1], dsv[8 * hh + 2], dsv[8 * hh + 3],
+                                  dsv[8 * hh + 4], dsv[8 * hh + 5], dsv[8 * hh + 6], dsv[8 * hh + 7]);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        dv[db] = mfma32x32x16(pa, dob[hh][db], dv[db]);
+        dk[db] = mfma32x32x16(sa, qbt[hh][db], dk[db]);
+      }
+    }
+  }
+}
 
-  const int nsplit = a.group / a.heads_per_wg;
-  const int kvh = blockIdx.x % a.heads_kv;
-  const int split = blockIdx.x / a.heads_kv;
+#ifndef SA_DKDV_OCC
+#define SA_DKDV_OCC 2   // waves per SIMD the register budget is set for
+#endif
+__global__ __launch_bounds__(256, SA_DKDV_OCC) void sinkattn_bwd_dkdv_bf16_d64(DkvArgs a) {
+  __shared__ DkvSmem sm;
+
+  const int kvh = blockIdx.x;
   const int kblk = blockIdx.y;
-  const int z = blockIdx.z;
-  (void)nsplit;
+  const int z = blockIdx.z / a.max_chunks;
+  const int chunk_id = blockIdx.z - z * a.max_chunks;
   const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
   const int k_start = kblk * BKW;
   if (k_start >= sv.len) return;
@@ -87,16 +156,18 @@ __global__ __launch_bounds__(256, 2) void sinkattn_bwd_bf16_d64(BwdArgs a) {
   if (!sa_query_range(k_start, k_last, sv.len, a.window, a.prefix, &q_lo, &q_hi)) return;
   const int qt_begin = q_lo / BQ;
   const int n_qt = q_hi / BQ - qt_begin + 1;
-  const int h_begin = kvh * a.group + split * a.heads_per_wg;
-  const int n_iter = n_qt * a.heads_per_wg;
+  const int n_iter_all = n_qt * a.group;
+  const int it_begin = chunk_id * a.chunk;
+  if (it_begin >= n_iter_all) return;
+  const int it_end = min(it_begin + a.chunk, n_iter_all);
+  const bool single = (it_begin == 0) && (it_end == n_iter_all);
+  const int h_begin = kvh * a.group;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  const int grp = lane >> 4;
-  const int li = lane & 15;
   const int kw0 = k_start + wave * KW;
   const bool wave_active = kw0 < sv.len;
 
@@ -105,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void sinkattn_bwd_bf16_d64(BwdArgs a) {
   const bf16* kbase = a.k + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
   const bf16* vbase = a.v + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
 
-  // K / V fragments as the B operand of S = Q K^T, dP = dO V^T:
+  // K / V fragments, B operand of S = Q K^T and dP = dO V^T:
   // lane = key kw0 + l32, head-dim chunk 16s + 8g .. +7.
   bf16x8 kf[4], vf[4];
   {
@@ -121,43 +192,22 @@ __global__ __launch_bounds__(256, 2) void sinkattn_bwd_bf16_d64(BwdArgs a) {
       }
     }
   }
-  // K rows of the whole workgroup into LDS (row-major) for the dQ stage.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int chunk = tid + 256 * i;          // 1024 chunks of 16 B
-    const int r = chunk >> 3;
-    const int c = (chunk & 7) * 8;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (k_start + r < sv.len) val = *(const uint4*)(kbase + (size_t)(k_start + r) * kv_row_stride + c);
-    *(uint4*)(sm.kt + r * LROW + c) = val;
-  }
 
-  // Q / dO / L / D tile loader (register prefetch, then LDS store).
-  const int ld_r = tid >> 3;                  // 0..31, and +32
-  const int ld_c = (tid & 7) * 8;
-  uint4 qreg[2], dreg[2];
+  // Q / dO tiles go straight from global memory into swizzled LDS tiles;
+  // L (in log2 units) and D go through one register per thread, with
+  // L = +inf for rows past the end of the sequence so P' = dS = 0 there.
   float lreg = 0.0f;
   auto tile_of = [&](int it, int* h, int* q0) {
     const int hi = it / n_qt;
     *h = h_begin + hi;
     *q0 = (qt_begin + (it - hi * n_qt)) * BQ;
   };
-  auto load_tile = [&](int it) {
+  auto load_tile = [&](int it, int buf) {
     int h, q0;
     tile_of(it, &h, &q0);
-    const bf16* qb = a.q + (size_t)sv.row_base * q_row_stride + (size_t)h * D;
-    const bf16* db = a.dout + (size_t)sv.row_base * q_row_stride + (size_t)h * D;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = q0 + ld_r + 32 * i;
-      if (r < sv.len) {
-        qreg[i] = *(const uint4*)(qb + (size_t)r * q_row_stride + ld_c);
-        dreg[i] = *(const uint4*)(db + (size_t)r * q_row_stride + ld_c);
-      } else {
-        qreg[i] = make_uint4(0, 0, 0, 0);
-        dreg[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
+    const size_t off = ((size_t)sv.row_base + q0) * q_row_stride + (size_t)h * D;
+    tile_load_lds<BQ, WAVES>(sm.qt[buf], a.q + off, q_row_stride, sv.len - q0, wave, lane);
+    tile_load_lds<BQ, WAVES>(sm.dot[buf], a.dout + off, q_row_stride, sv.len - q0, wave, lane);
     if (tid < 2 * BQ) {
       const int r = q0 + (tid & (BQ - 1));
       const size_t wi = (size_t)h * a.rows_total + sv.row_base + r;
@@ -165,12 +215,7 @@ __global__ __launch_bounds__(256, 2) void sinkattn_bwd_bf16_d64(BwdArgs a) {
       else lreg = (r < sv.len) ? a.d_ws[wi] : 0.0f;
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(uint4*)(sm.qt[buf] + (ld_r + 32 * i) * LROW + ld_c) = qreg[i];
-      *(uint4*)(sm.dot[buf] + (ld_r + 32 * i) * LROW + ld_c) = dreg[i];
-    }
+  auto store_stats = [&](int buf) {
     if (tid < BQ) sm.l2[buf][tid] = lreg;
     else if (tid < 2 * BQ) sm.dd[buf][tid - BQ] = lreg;
   };
@@ -178,104 +223,33 @@ __global__ __launch_bounds__(256, 2) void sinkattn_bwd_bf16_d64(BwdArgs a) {
   f32x16 dk_acc[2], dv_acc[2];
   dk_acc[0] = dk_acc[1] = dv_acc[0] = dv_acc[1] = f32x16{};
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(it_begin, 0);
+  store_stats(0);
+  wait_all_mem();
   __syncthreads();
 
-  for (int it = 0; it < n_iter; ++it) {
-    const int buf = it & 1;
+  for (int it = it_begin; it < it_end; ++it) {
+    const int buf = (it - it_begin) & 1;
     int h, q0;
     tile_of(it, &h, &q0);
-    if (it + 1 < n_iter) load_tile(it + 1);
+    (void)h;
+    if (it + 1 < it_end) load_tile(it + 1, buf ^ 1);
     const int q1 = min(q0 + BQ - 1, sv.len - 1);
     const int cls = wave_active ? sa_tile_class(q0, q1, kw0, kw0 + KW - 1, a.window, a.prefix)
                                 : SA_TILE_SKIP;
-    const bf16* qs = sm.qt[buf];
-    const bf16* ds_ = sm.dot[buf];
-    bf16* dsw = sm.dst + (wave * KW + l32) * SROW;   // this lane's dS^T row
-    if (cls != SA_TILE_SKIP) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 st = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 qa = *(const bf16x8*)(qs + (qb * 32 + l32) * LROW + 16 * s + 8 * g);
-          const bf16x8 da = *(const bf16x8*)(ds_ + (qb * 32 + l32) * LROW + 16 * s + 8 * g);
-          st = mfma32x32x16(qa, kf[s], st);
-          dp = mfma32x32x16(da, vf[s], dp);
-        }
-        // rows of this lane's C registers: queries qb*32 + 8*(i/4) + 4g + i%4
-        float pp[16], dsv[16];
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int qr = qb * 32 + 8 * i4 + 4 * g;
-          const f32x4 l4 = *(const f32x4*)(&sm.l2[buf][qr]);
-          const f32x4 d4 = *(const f32x4*)(&sm.dd[buf][qr]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            float p = fast_exp2(fmaf(st[i], a.scale_log2, -l4[e]));
-            if (cls == SA_TILE_PARTIAL && !sa_visible(q0 + qr + e, kw0 + l32, a.window, a.prefix)) p = 0.0f;
-            pp[i] = p;
-            dsv[i] = p * (dp[i] - d4[e]);
-          }
-        }
-        // dS^T to LDS: 4 contiguous queries per 8-byte store
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          *(bf16x4*)(dsw + qb * 32 + 8 * i4 + 4 * g) =
-              to_bf16x4(dsv[4 * i4], dsv[4 * i4 + 1], dsv[4 * i4 + 2], dsv[4 * i4 + 3]);
-        }
-        // dV += P'^T dO, dK += dS^T Q; k = 16 queries per step
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8 pa = to_bf16x8(pp[8 * hh], pp[8 * hh + 1], pp[8 * hh + 2], pp[8 * hh + 3],
-                                      pp[8 * hh + 4], pp[8 * hh + 5], pp[8 * hh + 6], pp[8 * hh + 7]);
-          const bf16x8 sa = to_bf16x8(dsv[8 * hh], dsv[8 * hh + 1], dsv[8 * hh + 2], dsv[8 * hh + 3],
-                                      dsv[8 * hh + 4], dsv[8 * hh + 5], dsv[8 * hh + 6], dsv[8 * hh + 7]);
-          const int r0 = qb * 32 + 16 * hh + 4 * g + (li >> 2);
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
-            const bf16x8 dob = cat8(lds_read_tr4(ds_ + r0 * LROW + c0), lds_read_tr4(ds_ + (r0 + 8) * LROW + c0));
-            const bf16x8 qbf = cat8(lds_read_tr4(qs + r0 * LROW + c0), lds_read_tr4(qs + (r0 + 8) * LROW + c0));
-            dv_acc[db] = mfma32x32x16(pa, dob, dv_acc[db]);
-            dk_acc[db] = mfma32x32x16(sa, qbf, dk_acc[db]);
-          }
-        }
-      }
-    } else {
-      // nothing visible for this wave: its dS^T rows are zero
-#pragma unroll
-      for (int c = 0; c < BQ; c += 4) *(bf16x4*)(dsw + c) = bf16x4{};
+    if (cls == SA_TILE_FULL) {
+      tile_step<false>(sm.qt[buf], sm.dot[buf], sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
+                       q0, kw0, a.window, a.prefix, a.scale_log2, lane);
+    } else if (cls == SA_TILE_PARTIAL) {
+      tile_step<true>(sm.qt[buf], sm.dot[buf], sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
+                      q0, kw0, a.window, a.prefix, a.scale_log2, lane);
     }
-    __syncthreads();
-    // ---- dQ block of this wave: rows qb = wave>>1, columns db = wave&1
-    const int wcls = sa_tile_class(q0, q1, k_start, k_last, a.window, a.prefix);
-    if (wcls != SA_TILE_SKIP) {
-      const int qb = wave >> 1, db = wave & 1;
-      f32x16 dq = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < BKW / 16; ++ks) {
-        const int r0 = ks * 16 + 8 * g + (li >> 2);
-        const int ca = qb * 32 + 16 * (grp & 1) + 4 * (li & 3);
-        const int cb = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
-        const bf16x8 sa = cat8(lds_read_tr4(sm.dst + r0 * SROW + ca), lds_read_tr4(sm.dst + (r0 + 4) * SROW + ca));
-        const bf16x8 kb = cat8(lds_read_tr4(sm.kt + r0 * LROW + cb), lds_read_tr4(sm.kt + (r0 + 4) * LROW + cb));
-        dq = mfma32x32x16(sa, kb, dq);
-      }
-      float* dqb = a.dq_acc + ((size_t)sv.row_base * a.heads_q + h) * D + db * 32 + l32;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qr = q0 + qb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (qr < sv.len) unsafeAtomicAdd(dqb + (size_t)qr * q_row_stride, dq[i]);
-      }
-    }
-    if (it + 1 < n_iter) store_tile(buf ^ 1);
+    if (it + 1 < it_end) store_stats(buf ^ 1);
+    wait_all_mem();
     __syncthreads();
   }
 
-  // ---- dK, dV: C rows are keys kw0 + 8*(i/4) + 4g + i%4, column d = db*32 + l32
+  // ---- C rows are keys kw0 + 8*(i/4) + 4g + i%4, column d = db*32 + l32
   if (wave_active) {
 #pragma unroll
     for (int db = 0; db < 2; ++db) {
@@ -285,8 +259,13 @@ __global__ __launch_bounds__(256, 2) void sinkattn_bwd_bf16_d64(BwdArgs a) {
       for (int i = 0; i < 16; ++i) {
         const int key = kw0 + 8 * (i >> 2) + 4 * g + (i & 3);
         if (key < sv.len) {
-          unsafeAtomicAdd(dkb + (size_t)key * kv_row_stride, dk_acc[db][i]);
-          unsafeAtomicAdd(dvb + (size_t)key * kv_row_stride, dv_acc[db][i]);
+          if (single) {
+            dkb[(size_t)key * kv_row_stride] = dk_acc[db][i];
+            dvb[(size_t)key * kv_row_stride] = dv_acc[db][i];
+          } else {
+            unsafeAtomicAdd(dkb + (size_t)key * kv_row_stride, dk_acc[db][i]);
+            unsafeAtomicAdd(dvb + (size_t)key * kv_row_stride, dv_acc[db][i]);
+          }
         }
       }
     }
@@ -295,23 +274,43 @@ __global__ __launch_bounds__(256, 2) void sinkattn_bwd_bf16_d64(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_bwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
-                               const float* l_ws, const float* d_ws, float* dq_acc, float* dk_acc,
-                               float* dv_acc, const int* cu_seqlens, int batch, int seqlen,
-                               int rows_total, int heads_q, int heads_kv, int window, int prefix,
-                               float scale, int heads_per_wg, hipStream_t stream) {
-  BwdArgs a;
+// Iterations per workgroup: aim for a few thousand workgroups over the whole
+// call so the longest one is short next to the total, but keep chunks long
+// enough that the per-chunk atomic flush of dK/dV stays small.
+int bwd_dkdv_chunk(int batch, int seqlen, int heads_kv, int group, int window, int prefix) {
+  long long total = 0;
+  const int nkb = (seqlen + BKW - 1) / BKW;
+  for (int kb = 0; kb < nkb; ++kb) {
+    int lo, hi;
+    const int k0 = kb * BKW;
+    if (sa_query_range(k0, sa_min(k0 + BKW - 1, seqlen - 1), seqlen, window, prefix, &lo, &hi))
+      total += (long long)(hi / BQ - lo / BQ + 1) * group;
+  }
+  total *= (long long)batch * heads_kv;
+  long long c = 32;
+  while (c < 256 && c * 2048 < total) c *= 2;
+  return (int)c;
+}
+
+hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
+                                    const bf16* dout, const float* l_ws, const float* d_ws,
+                                    float* dk_acc, float* dv_acc, const int* cu_seqlens,
+                                    int batch, int seqlen, int rows_total, int heads_q,
+                                    int heads_kv, int window, int prefix, float scale,
+                                    hipStream_t stream) {
+  DkvArgs a;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.l_ws = l_ws; a.d_ws = d_ws;
-  a.dq_acc = dq_acc; a.dk_acc = dk_acc; a.dv_acc = dv_acc; a.cu_seqlens = cu_seqlens;
+  a.dk_acc = dk_acc; a.dv_acc = dv_acc; a.cu_seqlens = cu_seqlens;
   a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
   a.group = heads_q / heads_kv; a.window = window; a.prefix = prefix;
   a.rows_total = rows_total;
-  a.heads_per_wg = heads_per_wg;
-  a.num_k_blocks = (seqlen + BKW - 1) / BKW;
   a.scale_log2 = scale * SA_LOG2E;
-  if (a.num_k_blocks == 0 || batch == 0) return hipSuccess;
-  const int nsplit = a.group / heads_per_wg;
-  dim3 grid(heads_kv * nsplit, a.num_k_blocks, batch);
-  hipLaunchKernelGGL(sinkattn_bwd_bf16_d64, grid, dim3(256), 0, stream, a);
+  const int nkb = (seqlen + BKW - 1) / BKW;
+  if (nkb == 0 || batch == 0) return hipSuccess;
+  a.chunk = bwd_dkdv_chunk(batch, seqlen, heads_kv, a.group, window, prefix);
+  const int max_iters = ((seqlen + BQ - 1) / BQ + 1) * a.group;
+  a.max_chunks = (max_iters + a.chunk - 1) / a.chunk;
+  dim3 grid(heads_kv, nkb, batch * a.max_chunks);
+  hipLaunchKernelGGL(sinkattn_bwd_dkdv_bf16_d64, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }

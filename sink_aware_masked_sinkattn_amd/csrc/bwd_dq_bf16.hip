@@ -1,0 +1,261 @@
+// dQ of sink-aware masked attention, bf16, head dim 64, gfx950 MFMA.
+//
+// For each query row i of head h, over the keys the mask leaves visible
+// (M[q,k] = 1[k<=q] AND 1[q-k<=w OR k<p]; "Efficient Reinforcement Learning
+// for Long-Horizon Tool-Use Agentic Tasks", summary page):
+//   P'_ij = exp(S_ij - L_i),  S_ij = scale q_i . k_j,  L_i = logaddexp(l_i, s_h)
+//   dS_ij = P'_ij (dO_i . v_j - D_i),    dQ_i = scale sum_j dS_ij k_j
+// (the zero-value sink key of arXiv 2608.10357 section 5 enters only through
+// L and D).  Query-stationary, like the forward: each workgroup owns 256
+// query rows of one head and walks the same key-tile list (prefix tiles +
+// window tiles), so dQ accumulates in registers and is written once, with
+// no atomics -- at the price of recomputing S and dP^T here (the dK/dV
+// kernel recomputes them too).
+//
+// Layout per wave (64 query rows = two 32-row MFMA blocks):
+//   S^T = K Q^T and dP^T = V dO^T with one query per lane (C layout); Q and
+//   dO fragments stay in registers as the B operand; K and V tiles come
+//   from LDS as the A operand.  L and D are then per-lane scalars.  The C
+//   layout of dS^T (lane = query, 16 keys in registers) is exactly the A
+//   operand of dQ = dS K; the B operand (keys along k) is a transpose read
+//   of the row-major K tile.
+#include "common.h"
+#include "mask_tiles.h"
+
+namespace {
+
+constexpr int D = 64;
+constexpr int QB = 2;
+constexpr int WAVES = 4;
+constexpr int BQ = WAVES * QB * 32;   // 256
+constexpr int BK = 64;
+constexpr int TILE_ELEMS = BK * D;     // swizzled rows (tile_off)
+constexpr int OROW = D + 8;            // padded row of the epilogue staging buffer
+// LDS: two K/V tile pairs during the key loop; afterwards the same memory
+// stages each wave's 64 output rows (padded) for row-contiguous stores.
+constexpr int STAGE_ELEMS = WAVES * QB * 32 * OROW;
+constexpr int SMEM_ELEMS = (4 * TILE_ELEMS > STAGE_ELEMS) ? 4 * TILE_ELEMS : STAGE_ELEMS;
+static_assert(SMEM_ELEMS >= 4 * TILE_ELEMS && SMEM_ELEMS >= STAGE_ELEMS, "LDS sizing");
+
+struct DqArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  const bf16* dout;
+  const float* l_ws;      // [Hq, rows] natural-log L
+  const float* d_ws;      // [Hq, rows] D
+  bf16* dq;
+  const int* cu_seqlens;
+  int seqlen, heads_q, heads_kv, group, window, prefix, rows_total, num_q_tiles;
+  float scale_log2;
+  float scale;
+};
+
+__device__ __forceinline__ int map_head(int x, int heads_q) {
+  if ((heads_q & 7) == 0) return (x & 7) * (heads_q >> 3) + (x >> 3);
+  return x;
+}
+
+// One 64-key tile against this wave's 64 query rows.  MASK: apply the element
+// predicate (partial tiles only).
+template <bool MASK>
+__device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const bf16x8 (&qf)[QB][4],
+                                          const bf16x8 (&df)[QB][4], const float (&l2)[QB],
+                                          const float (&dd)[QB], f32x16 (&acc)[QB][2], int qw0,
+                                          int k0, int window, int prefix, float scale_log2,
+                                          int lane) {
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int grp = lane >> 4;
+  const int li = lane & 15;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    // A operands of S^T = K Q^T and dP^T = V dO^T (keys on m, head dim on k)
+    bf16x8 kf[4], vf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kf[s] = *(const bf16x8*)(ks + tile_off(kb * 32 + l32, 16 * s + 8 * g));
+      vf[s] = *(const bf16x8*)(vs + tile_off(kb * 32 + l32, 16 * s + 8 * g));
+    }
+    // B operand of dQ += dS K (keys on k, head dim on n): transpose reads
+    bf16x8 kt[2][2];   // [hh][db]
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r0 = kb * 32 + 16 * hh + 4 * g + (li >> 2);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
+        kt[hh][db] = cat8(lds_read_tr4(ks + tile_off(r0, c0)), lds_read_tr4(ks + tile_off(r0 + 8, c0)));
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        st = mfma32x32x16(kf[s], qf[qb][s], st);
+        dpt = mfma32x32x16(vf[s], df[qb][s], dpt);
+      }
+      // dS^T: lane = query, rows = keys k0 + kb*32 + 8*(i/4) + 4g + i%4
+      const int q = qw0 + qb * 32 + l32;
+      float dsv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(fmaf(st[i], scale_log2, -l2[qb]));
+        if (MASK) {
+          const int k = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          const bool vis = (k <= q) & ((q - k <= window) | (k < prefix));
+          p = vis ? p : 0.0f;
+        }
+        dsv[i] = p * (dpt[i] - dd[qb]);
+      }
+      const bf16x8 d0 = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+      const bf16x8 d1 = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        acc[qb][db] = mfma32x32x16(d0, kt[0][db], acc[qb][db]);
+        acc[qb][db] = mfma32x32x16(d1, kt[1][db], acc[qb][db]);
+      }
+    }
+  }
+}
+
+#ifndef SA_DQ_OCC
+#define SA_DQ_OCC 2   // waves per SIMD the register budget is set for
+#endif
+__global__ __launch_bounds__(256, SA_DQ_OCC) void sinkattn_bwd_dq_bf16_d64(DqArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
+
+  const int h = map_head(blockIdx.x, a.heads_q);
+  const int z = blockIdx.y;
+  const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
+  const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
+  const int q_start = qt * BQ;
+  if (q_start >= sv.len) return;
+  const int q_last = min(q_start + BQ - 1, sv.len - 1);
+  const int kvh = h / a.group;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int grp = lane >> 4;
+  const int li = lane & 15;
+  const int qw0 = q_start + wave * (QB * 32);
+  const bool wave_active = qw0 < sv.len;
+  const int qw1 = min(qw0 + QB * 32 - 1, sv.len - 1);
+
+  const int q_row_stride = a.heads_q * D;
+  const int kv_row_stride = a.heads_kv * D;
+  const size_t qoff = (size_t)sv.row_base * q_row_stride + (size_t)h * D;
+  const bf16* kbase = a.k + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
+  const bf16* vbase = a.v + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
+
+  // Q, dO fragments (B operands), per-lane L (log2 domain) and D
+  bf16x8 qf[QB][4], df[QB][4];
+  float l2[QB], dd[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + qb * 32 + l32;
+    const bool ok = row < sv.len;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const size_t off = qoff + (size_t)row * q_row_stride + 16 * s + 8 * g;
+      qf[qb][s] = ok ? *(const bf16x8*)(a.q + off) : bf16x8{};
+      df[qb][s] = ok ? *(const bf16x8*)(a.dout + off) : bf16x8{};
+    }
+    const size_t wi = (size_t)h * a.rows_total + sv.row_base + row;
+    l2[qb] = ok ? a.l_ws[wi] * SA_LOG2E : INFINITY;
+    dd[qb] = ok ? a.d_ws[wi] : 0.0f;
+  }
+
+  int seg[4];
+  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BK, seg);
+  const int n0 = seg[1] - seg[0];
+  const int ntiles = n0 + (nseg > 1 ? seg[3] - seg[2] : 0);
+
+  // K / V tiles go straight from global memory into swizzled LDS tiles
+  auto load_tile = [&](int t, int buf) {
+    const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
+    const int r0 = kt * BK;
+    tile_load_lds<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
+                             kv_row_stride, sv.len - r0, wave, lane);
+    tile_load_lds<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
+                             kv_row_stride, sv.len - r0, wave, lane);
+  };
+
+  f32x16 acc[QB][2];   // dQ: C layout [m = query][n = d], lane = d
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) acc[qb][0] = acc[qb][1] = f32x16{};
+
+  load_tile(0, 0);
+  wait_all_mem();
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
+    const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
+    const int k0 = kt * BK;
+    const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
+                                : SA_TILE_SKIP;
+    const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
+    const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
+    if (cls == SA_TILE_FULL) {
+      tile_step<false>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+    } else if (cls == SA_TILE_PARTIAL) {
+      tile_step<true>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+    }
+    wait_all_mem();
+    __syncthreads();
+  }
+
+  // ---- dQ = scale * acc, C layout rows = queries qb*32 + 8*(i/4) + 4g + i%4,
+  // column d = db*32 + l32.  Stage through LDS for row-contiguous stores.
+  bf16* os = smem + wave * (QB * 32) * OROW;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = qb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        os[r * OROW + db * 32 + l32] = (bf16)(acc[qb][db][i] * a.scale);
+      }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  if (wave_active) {
+    bf16* obase = a.dq + qoff;
+#pragma unroll
+    for (int it = 0; it < (QB * 32 * D) / (64 * 8); ++it) {
+      const int chunk = it * 64 + lane;
+      const int r = chunk >> 3;
+      const int c = (chunk & 7) * 8;
+      const int qrow = qw0 + r;
+      if (qrow < sv.len) *(uint4*)(obase + (size_t)qrow * q_row_stride + c) = *(const uint4*)(os + r * OROW + c);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
+                                  const float* l_ws, const float* d_ws, bf16* dq,
+                                  const int* cu_seqlens, int batch, int seqlen, int rows_total,
+                                  int heads_q, int heads_kv, int window, int prefix, float scale,
+                                  hipStream_t stream) {
+  DqArgs a;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.l_ws = l_ws; a.d_ws = d_ws; a.dq = dq;
+  a.cu_seqlens = cu_seqlens;
+  a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
+  a.group = heads_q / heads_kv; a.window = window; a.prefix = prefix;
+  a.rows_total = rows_total;
+  a.num_q_tiles = (seqlen + BQ - 1) / BQ;
+  a.scale_log2 = scale * SA_LOG2E;
+  a.scale = scale;
+  if (a.num_q_tiles == 0 || batch == 0) return hipSuccess;
+  dim3 grid(heads_q, batch, a.num_q_tiles);
+  hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}

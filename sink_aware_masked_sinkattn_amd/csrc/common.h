@@ -96,3 +96,48 @@ __device__ __forceinline__ SeqView seq_view(const int* cu_seqlens, int z, int se
   }
   return s;
 }
+
+// ---------------------------------------------------------------------------
+// LDS tiles of R rows x 64 bf16 (128 B per row, no padding).  Each row's eight
+// 16-byte chunks are stored XOR-swizzled by the row index:
+//   physical chunk = chunk ^ (2*(r%4) + (r/4)%2) ^ (2*((r/8)%2))
+// which keeps both access patterns the kernels use free of bank conflicts
+// (checked against 32- and 64-bank models): 16-byte reads of one chunk by
+// 8 or 16 consecutive rows (MFMA operands with the head dim along k), and
+// ds_read_tr16_b64 reads of 4 consecutive rows x 32 bytes (operands with the
+// row index along k).
+__device__ __forceinline__ int tile_swz(int r) {
+  return (((r & 3) << 1) | ((r >> 2) & 1)) ^ ((r >> 2) & 2);
+}
+// element offset of (row r, column c); c's low 3 bits stay inside the chunk
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * 64 + ((((c >> 3) ^ tile_swz(r))) << 3) + (c & 7);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy a ROWS x 64 bf16 tile from global memory straight into a swizzled LDS
+// tile (global_load_lds_dwordx4: lane i's 16 bytes land at lds_ptr + 16*i, so
+// one instruction fills 8 rows; no VGPRs are used for the data).  Lane i of
+// an 8-row block fetches the global chunk that belongs at physical chunk i%8
+// of row i/8.  Rows at or past `nvalid` repeat row nvalid-1 (nvalid >= 1):
+// callers mask those rows out of every result.  Completion is tracked by
+// vmcnt: s_waitcnt vmcnt(0) before the barrier that publishes the tile.
+template <int ROWS, int WAVES>
+__device__ __forceinline__ void tile_load_lds(bf16* lds_tile, const bf16* gbase, size_t row_stride,
+                                              int nvalid, int wave, int lane) {
+  constexpr int PER_WAVE = ROWS / (8 * WAVES);
+  static_assert(PER_WAVE * 8 * WAVES == ROWS, "tile rows must split into 8-row blocks per wave");
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int blk = wave * PER_WAVE + j;
+    const int r = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ tile_swz(r);
+    const int rr = r < nvalid ? r : nvalid - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(gbase + (size_t)rr * row_stride + c * 8),
+                                     (lds_void*)(lds_tile + blk * 512), 16, 0, 0);
+  }
+}
+
+// wait for every outstanding memory operation of this wave (vmcnt, lgkmcnt = 0)
+__device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }

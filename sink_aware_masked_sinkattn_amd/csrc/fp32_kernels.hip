@@ -171,14 +171,19 @@ hipError_t f32_fwd_launch(const F32Args& a, int batch, hipStream_t st) {
 }
 
 template <int D>
-hipError_t f32_bwd_launch(const F32Args& a, int batch, hipStream_t st) {
-  dim3 gq((a.seqlen + 63) / 64, a.heads_q, batch);
-  hipLaunchKernelGGL(f32_dq<D>, gq, dim3(64), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dim3 gk((a.seqlen + 63) / 64, a.heads_kv, batch);
-  hipLaunchKernelGGL(f32_dkdv<D>, gk, dim3(64), 0, st, a);
-  return hipGetLastError();
+hipError_t f32_bwd_launch(const F32Args& a, int batch, bool do_dq, bool do_dkdv, hipStream_t st) {
+  if (do_dq) {
+    dim3 gq((a.seqlen + 63) / 64, a.heads_q, batch);
+    hipLaunchKernelGGL(f32_dq<D>, gq, dim3(64), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (do_dkdv) {
+    dim3 gk((a.seqlen + 63) / 64, a.heads_kv, batch);
+    hipLaunchKernelGGL(f32_dkdv<D>, gk, dim3(64), 0, st, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 F32Args make_args(const int* cu_seqlens, int seqlen, int total_tokens, int heads_q, int heads_kv,
@@ -211,12 +216,12 @@ hipError_t launch_bwd_f32(int head_dim, const float* q, const float* k, const fl
                           const float* dout, const float* l_ws, const float* d_ws, float* dq,
                           float* dk, float* dv, const int* cu_seqlens, int batch, int seqlen,
                           int total_tokens, int heads_q, int heads_kv, int window, int prefix,
-                          float scale, hipStream_t stream) {
+                          float scale, bool do_dq, bool do_dkdv, hipStream_t stream) {
   if (batch == 0 || seqlen == 0 || heads_q == 0) return hipSuccess;
   F32Args a = make_args(cu_seqlens, seqlen, total_tokens, heads_q, heads_kv, window, prefix, scale);
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.l_ws = l_ws; a.d_ws = d_ws;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  if (head_dim == 32) return f32_bwd_launch<32>(a, batch, stream);
-  if (head_dim == 64) return f32_bwd_launch<64>(a, batch, stream);
+  if (head_dim == 32) return f32_bwd_launch<32>(a, batch, do_dq, do_dkdv, stream);
+  if (head_dim == 64) return f32_bwd_launch<64>(a, batch, do_dq, do_dkdv, stream);
   return hipErrorInvalidValue;
 }

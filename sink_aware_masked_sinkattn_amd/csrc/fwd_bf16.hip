@@ -40,8 +40,17 @@ constexpr int QB = 2;                    // 32-row query blocks per wave
 constexpr int WAVES = 4;
 constexpr int BQ = WAVES * QB * 32;      // 256 query rows per workgroup
 constexpr int BK = 64;                   // key rows per LDS tile
-constexpr int LROW = D + 8;              // padded LDS row (bf16 elements, 144 B)
-constexpr int TILE_ELEMS = BK * LROW;
+constexpr int TILE_ELEMS = BK * D;       // swizzled rows (tile_off)
+constexpr int OROW = D + 8;              // padded row of the epilogue staging buffer
+// LDS: two K/V tile pairs during the key loop; afterwards the same memory
+// stages each wave's 64 output rows (padded) for row-contiguous stores.
+constexpr int STAGE_ELEMS = WAVES * QB * 32 * OROW;
+constexpr int SMEM_ELEMS = (4 * TILE_ELEMS > STAGE_ELEMS) ? 4 * TILE_ELEMS : STAGE_ELEMS;
+static_assert(SMEM_ELEMS >= 4 * TILE_ELEMS && SMEM_ELEMS >= STAGE_ELEMS, "LDS sizing");
+// Lazy rescaling: the running max used for the exponentials is only moved when
+// a row's true max exceeds it by more than this (log2 units), so probabilities
+// stay below 2^8 and most key tiles skip the accumulator rescale entirely.
+constexpr float RESCALE_THRESHOLD = 8.0f;
 
 struct FwdArgs {
   const bf16* q;
@@ -64,8 +73,103 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
   return x;
 }
 
-__global__ __launch_bounds__(256, 2) void sinkattn_fwd_bf16_d64(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[4 * TILE_ELEMS];  // K0 V0 K1 V1
+// One 64-key tile against this wave's 64 query rows (two 32-row blocks).
+// MASK: apply the element predicate (partial tiles only).
+template <bool MASK>
+__device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const bf16x8 (&qf)[QB][4],
+                                          f32x16 (&acc)[QB][2], float (&m_run)[QB],
+                                          float (&r_run)[QB], int qw0, int k0, int window,
+                                          int prefix, float scale_log2, int lane) {
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int grp = lane >> 4;
+  const int li = lane & 15;
+  // ---- S^T = K Q^T for both 32-key blocks and both query blocks: lane =
+  // query, 16 keys per block in registers.  Each K fragment (keys on m, head
+  // dim on k) is read from LDS right before the two MFMAs that use it.
+  f32x16 st[2][QB];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) st[kb][qb] = f32x16{};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bf16x8 kf = *(const bf16x8*)(ks + tile_off(kb * 32 + l32, 16 * s + 8 * g));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) st[kb][qb] = mfma32x32x16(kf, qf[qb][s], st[kb][qb]);
+    }
+  if (MASK) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int q = qw0 + qb * 32 + l32;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int k = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          const bool vis = (k <= q) & ((q - k <= window) | (k < prefix));
+          st[kb][qb][i] = vis ? st[kb][qb][i] : -INFINITY;
+        }
+    }
+  }
+  // ---- online softmax in the log2 domain, lazily rescaled
+  bf16x8 pf[2][QB][2];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float mx = st[0][qb][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb][qb][i]);
+    mx = halves_max(mx) * scale_log2;
+    if (__any(mx > m_run[qb] + RESCALE_THRESHOLD)) {
+      const float m_new = fmaxf(m_run[qb], mx);
+      const float corr = fast_exp2(m_run[qb] - m_new);
+      m_run[qb] = m_new;
+      r_run[qb] *= corr;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[qb][db][i] *= corr;
+    }
+    const float m_use = m_run[qb];
+    float rs = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = fast_exp2(fmaf(st[kb][qb][i], scale_log2, -m_use));
+        rs += p[i];
+      }
+      pf[kb][qb][0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+      pf[kb][qb][1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+    }
+    r_run[qb] += rs;
+  }
+  // ---- O^T += V^T P^T; V^T operands (head dim on m, keys on k) by transpose reads
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r0 = kb * 32 + 16 * hh + 4 * g + (li >> 2);
+        const bf16x8 vt = cat8(lds_read_tr4(vs + tile_off(r0, c0)), lds_read_tr4(vs + tile_off(r0 + 8, c0)));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(vt, pf[kb][qb][hh], acc[qb][db]);
+      }
+  }
+}
+
+#ifndef SA_FWD_OCC
+#define SA_FWD_OCC 2   // waves per SIMD the register budget is set for
+#endif
+__global__ __launch_bounds__(256, SA_FWD_OCC) void sinkattn_fwd_bf16_d64(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 smem[SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
 
   const int h = map_head(blockIdx.x, a.heads_q);
   const int z = blockIdx.y;
@@ -113,31 +217,14 @@ __global__ __launch_bounds__(256, 2) void sinkattn_fwd_bf16_d64(FwdArgs a) {
   const int ntiles = n0 + (nseg > 1 ? seg[3] - seg[2] : 0);
 
   // cooperative tile load: 512 chunks of 16 B per tensor, 2 per thread
-  const int ld_row0 = tid >> 3;          // 0..31 (and +32)
-  const int ld_col = (tid & 7) * 8;
-  uint4 kreg[2], vreg[2];
-  auto load_tile = [&](int t) {
+  // K / V tiles go straight from global memory into swizzled LDS tiles
+  auto load_tile = [&](int t, int buf) {
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = kt * BK + ld_row0 + 32 * i;
-      if (r < sv.len) {
-        kreg[i] = *(const uint4*)(kbase + (size_t)r * kv_row_stride + ld_col);
-        vreg[i] = *(const uint4*)(vbase + (size_t)r * kv_row_stride + ld_col);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
-    bf16* ks = smem + (2 * buf) * TILE_ELEMS;
-    bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *(uint4*)(ks + (ld_row0 + 32 * i) * LROW + ld_col) = kreg[i];
-      *(uint4*)(vs + (ld_row0 + 32 * i) * LROW + ld_col) = vreg[i];
-    }
+    const int r0 = kt * BK;
+    tile_load_lds<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
+                             kv_row_stride, sv.len - r0, wave, lane);
+    tile_load_lds<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
+                             kv_row_stride, sv.len - r0, wave, lane);
   };
 
   f32x16 acc[QB][2];
@@ -150,105 +237,31 @@ __global__ __launch_bounds__(256, 2) void sinkattn_fwd_bf16_d64(FwdArgs a) {
     r_run[qb] = 0.0f;
   }
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, 0);
+  wait_all_mem();
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+    if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
     const int k0 = kt * BK;
     const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
                                 : SA_TILE_SKIP;
-    if (cls != SA_TILE_SKIP) {
-      const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
-      const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
-      // ---- S^T = K Q^T: [kb][qb], lane = query, 16 keys in registers
-      f32x16 st[2][QB];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) st[kb][qb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = *(const bf16x8*)(ks + (kb * 32 + l32) * LROW + 16 * s + 8 * g);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) st[kb][qb] = mfma32x32x16(kf, qf[qb][s], st[kb][qb]);
-        }
-      }
-      if (cls == SA_TILE_PARTIAL) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int qrow = qw0 + qb * 32 + l32;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-              if (!sa_visible(qrow, key, a.window, a.prefix)) st[kb][qb][i] = -INFINITY;
-            }
-        }
-      }
-      // ---- online softmax (log2 domain), probabilities to bf16
-      bf16x8 pf[2][QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb][qb][i]);
-        mx = halves_max(mx);
-        const float m_new = fmaxf(m_run[qb], mx * a.scale_log2);
-        const float corr = fast_exp2(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        float rs = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          float p[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            p[i] = fast_exp2(fmaf(st[kb][qb][i], a.scale_log2, -m_new));
-            rs += p[i];
-          }
-          pf[kb][qb][0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-          pf[kb][qb][1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
-        }
-        r_run[qb] = r_run[qb] * corr + rs;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[qb][db][i] *= corr;
-      }
-      // ---- O^T += V^T P^T (A = V^T via LDS transpose reads)
-      const int grp = lane >> 4;           // 16-lane group 0..3
-      const int li = lane & 15;
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int r0 = kb * 32 + 16 * hh + 4 * g + (li >> 2);
-            const bf16x4 lo = lds_read_tr4(vs + r0 * LROW + c0);
-            const bf16x4 hi = lds_read_tr4(vs + (r0 + 8) * LROW + c0);
-            const bf16x8 vf = cat8(lo, hi);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(vf, pf[kb][qb][hh], acc[qb][db]);
-          }
-      }
+    const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
+    const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
+    if (cls == SA_TILE_FULL) {
+      tile_step<false>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+    } else if (cls == SA_TILE_PARTIAL) {
+      tile_step<true>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    wait_all_mem();
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / (r + exp(s - m)), l = ln(2) * (m + log2 r)
   // Stage each wave's 64 x 64 output through LDS for row-contiguous stores.
-  bf16* os = smem + wave * (QB * 32) * LROW;   // 64 rows x LROW per wave (fits in 4 tiles)
+  bf16* os = smem + wave * (QB * 32) * OROW;   // 64 rows x OROW per wave (fits in 4 tiles)
   const float sink_l2 = a.sinks[h] * SA_LOG2E;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -264,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void sinkattn_fwd_bf16_d64(FwdArgs a) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const int d = db * 32 + 8 * i4 + 4 * g;
-        *(bf16x4*)(os + (qb * 32 + l32) * LROW + d) =
+        *(bf16x4*)(os + (qb * 32 + l32) * OROW + d) =
             to_bf16x4(acc[qb][db][4 * i4] * inv, acc[qb][db][4 * i4 + 1] * inv,
                       acc[qb][db][4 * i4 + 2] * inv, acc[qb][db][4 * i4 + 3] * inv);
       }
@@ -280,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void sinkattn_fwd_bf16_d64(FwdArgs a) {
       const int c = (chunk & 7) * 8;
       const int qrow = qw0 + r;
       if (qrow < sv.len) {
-        *(uint4*)(obase + (size_t)qrow * q_row_stride + c) = *(const uint4*)(os + r * LROW + c);
+        *(uint4*)(obase + (size_t)qrow * q_row_stride + c) = *(const uint4*)(os + r * OROW + c);
       }
     }
   }

@@ -108,8 +108,8 @@ def test_workspace_checks():
     pb = _problem()
     need = _lib().sinkattn_bwd_workspace_size(ctypes.byref(pb))
     rows, hq, hkv, d = 256, 8, 2, 64
-    # D and L stats, fp32 dQ accumulator, fp32 dK and dV accumulators
-    assert need >= 4 * (2 * rows * hq + rows * hq * d + 2 * rows * hkv * d)
+    # D and L stats, fp32 dK and dV accumulators
+    assert need >= 4 * (2 * rows * hq + 2 * rows * hkv * d)
     assert _bwd(pb, ws=None) == 6
     assert _bwd(pb, ws_bytes=need - 1) == 6
     assert _bwd(pb, ws=A + 16, ws_bytes=need) == 5          # workspace must be 256-B aligned
@@ -118,7 +118,7 @@ def test_workspace_checks():
     assert need32 >= 4 * 2 * rows * hq
     pb_var = _problem(cu_seqlens=A, batch=3, total_tokens=1000, seqlen=600)
     need_var = _lib().sinkattn_bwd_workspace_size(ctypes.byref(pb_var))
-    assert need_var >= 4 * (2 * 1000 * hq + 1000 * hq * d + 2 * 1000 * hkv * d)
+    assert need_var >= 4 * (2 * 1000 * hq + 2 * 1000 * hkv * d)
     bad_var = _problem(cu_seqlens=A, batch=3, total_tokens=-1)
     assert _fwd(bad_var) == 2
 
@@ -128,3 +128,15 @@ def test_empty_forward_is_a_no_op():
     assert _fwd(_problem(batch=0)) == 0
     assert _fwd(_problem(seqlen=0)) == 0
     assert _fwd(_problem(batch=0), q=None, k=None, v=None, s=None, o=None, lse=None) == 0
+
+
+def test_bwd_phase_mask_validated():
+    pb = _problem()
+    lib = _lib()
+    args = (ctypes.byref(pb),) + (A,) * 11 + (A, 1 << 40, None)
+    assert lib.sinkattn_bwd_phases(0, *args) == 2
+    assert lib.sinkattn_bwd_phases(16, *args) == 2
+    assert lib.sinkattn_bwd_phases(1 | 32, *args) == 2
+    # a valid mask still runs the same host checks first (window < 0 here)
+    bad = _problem(window=-1)
+    assert lib.sinkattn_bwd_phases(15, ctypes.byref(bad), *args[1:]) == 3

@@ -214,3 +214,25 @@ def test_memory_grows_linearly():
     # doubling T must not more than double (plus slack) the extra memory
     assert peaks[4096] <= 2.1 * peaks[2048]
     assert peaks[8192] <= 2.1 * peaks[4096]
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("fp32", 32)])
+def test_bwd_phases_equal_single_call(dtype, d):
+    from sink_aware_masked_sinkattn_amd import (BWD_DKDV, BWD_DQ, BWD_FINISH, BWD_PREPARE,
+                                                sinkattn_bwd, sinkattn_bwd_phases, sinkattn_fwd)
+    inp = make_inputs(batch=1, seqlen=700, heads_q=8, heads_kv=2, head_dim=d, window=100,
+                      prefix=3, seed=31, std=0.5, dtype=dtype)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.do))
+    s = inp.sinks.to(dev)
+    o, lse = sinkattn_fwd(q, k, v, s, inp.window, inp.prefix, inp.scale)
+    ref = sinkattn_bwd(q, k, v, s, o, lse, do, inp.window, inp.prefix, inp.scale)
+    grads = tuple(torch.full_like(t, float("nan")) for t in ref)
+    ws = torch.full((1 << 26,), 255, dtype=torch.uint8, device=dev)
+    for ph in (BWD_PREPARE, BWD_DKDV, BWD_DQ, BWD_FINISH):
+        sinkattn_bwd_phases(ph, q, k, v, s, o, lse, do, inp.window, inp.prefix, inp.scale,
+                            workspace=ws, grads=grads)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, grads):
+        assert torch.isfinite(b).all()
+        torch.testing.assert_close(a.float(), b.float(), atol=1e-3, rtol=1e-3)
