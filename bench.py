@@ -35,6 +35,7 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 WINDOW_INF = 2**31 - 1
 CPU_SAMPLE_HEADS = 4
+COPY_PROBE_BYTES = 256 * 2**20
 
 KERNEL_SOURCES = {
     "sinkattn_fwd_bf16_d64": ["fwd_bf16.hip", "common.h", "mask_tiles.h"],
@@ -128,6 +129,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after timing, copy a 256 MiB buffer device-to-device 3 times: the "
+                         "reference for scaling hardware byte counters (FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -256,6 +260,15 @@ def main(argv=None):
                        "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                        "fwd_tflops": round(4 * d * p["pairs"] / (p["fwd_ms"] * 1e-3) / 1e12, 2),
                        "bwd_tflops": round(10 * d * p["pairs"] / (t_bwd * 1e-3) / 1e12, 2)}
+
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
