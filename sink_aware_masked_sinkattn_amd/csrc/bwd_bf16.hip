@@ -37,7 +37,11 @@ constexpr int D = 64;
 constexpr int WAVES = 4;
 constexpr int KW = 32;                 // keys per wave
 constexpr int BKW = WAVES * KW;        // 128 keys per workgroup
-constexpr int BQ = 64;                 // query rows per tile
+#ifndef SA_DKDV_BQ
+#define SA_DKDV_BQ 64
+#endif
+constexpr int BQ = SA_DKDV_BQ;         // query rows per tile (multiple of 32)
+constexpr int NQB = BQ / 32;           // 32-row MFMA blocks per tile
 
 struct DkvArgs {
   const bf16* q;
@@ -62,7 +66,7 @@ struct __attribute__((aligned(16))) DkvSmem {
   float dd[2][BQ];
 };
 
-// One 64-row query tile against this wave's 32 keys.  MASK: apply the element
+// One BQ-row query tile against this wave's 32 keys.  MASK: apply the element
 // predicate (partial tiles); full tiles run without any mask arithmetic.
 template <bool MASK>
 __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const float* l2s,
@@ -75,7 +79,7 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
   const int grp = lane >> 4;
   const int li = lane & 15;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQB; ++qb) {
     // A operands (query rows, head dim along k) for S = Q K^T and dP = dO V^T
     bf16x8 qa[4], da[4];
 #pragma unroll
@@ -141,7 +145,7 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
 #ifndef SA_DKDV_OCC
 #define SA_DKDV_OCC 2   // waves per SIMD the register budget is set for
 #endif
-__global__ __launch_bounds__(256, SA_DKDV_OCC) void sinkattn_bwd_dkdv_bf16_d64(DkvArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC, SA_DKDV_OCC))) void sinkattn_bwd_dkdv_bf16_d64(DkvArgs a) {
   __shared__ DkvSmem sm;
 
   const int kvh = blockIdx.x;
@@ -208,6 +212,7 @@ __global__ __launch_bounds__(256, SA_DKDV_OCC) void sinkattn_bwd_dkdv_bf16_d64(D
     const size_t off = ((size_t)sv.row_base + q0) * q_row_stride + (size_t)h * D;
     tile_load_lds<BQ, WAVES>(sm.qt[buf], a.q + off, q_row_stride, sv.len - q0, wave, lane);
     tile_load_lds<BQ, WAVES>(sm.dot[buf], a.dout + off, q_row_stride, sv.len - q0, wave, lane);
+    static_assert(2 * BQ <= 256, "L and D are staged by one thread per row");
     if (tid < 2 * BQ) {
       const int r = q0 + (tid & (BQ - 1));
       const size_t wi = (size_t)h * a.rows_total + sv.row_base + r;

@@ -25,11 +25,22 @@
 namespace {
 
 constexpr int D = 64;
-constexpr int QB = 2;
-constexpr int WAVES = 4;
+#ifndef SA_DQ_QB
+#define SA_DQ_QB 2
+#endif
+#ifndef SA_DQ_WAVES
+#define SA_DQ_WAVES 4
+#endif
+constexpr int QB = SA_DQ_QB;          // 32-row query blocks per wave
+constexpr int WAVES = SA_DQ_WAVES;    // waves per workgroup
 constexpr int BQ = WAVES * QB * 32;   // 256
 constexpr int BK = 64;
-constexpr int TILE_ELEMS = BK * D;     // swizzled rows (tile_off)
+#ifndef SA_DQ_KSUB
+#define SA_DQ_KSUB 1
+#endif
+constexpr int KSUB = SA_DQ_KSUB;           // 64-key compute steps per LDS key tile
+constexpr int BKL = BK * KSUB;          // key rows per LDS tile
+constexpr int TILE_ELEMS = BKL * D;     // swizzled rows (tile_off)
 constexpr int OROW = D + 8;            // padded row of the epilogue staging buffer
 // LDS: two K/V tile pairs during the key loop; afterwards the same memory
 // stages each wave's 64 output rows (padded) for row-contiguous stores.
@@ -123,7 +134,7 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
 #ifndef SA_DQ_OCC
 #define SA_DQ_OCC 2   // waves per SIMD the register budget is set for
 #endif
-__global__ __launch_bounds__(256, SA_DQ_OCC) void sinkattn_bwd_dq_bf16_d64(DqArgs a) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_DQ_OCC, SA_DQ_OCC))) void sinkattn_bwd_dq_bf16_d64(DqArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 smem[SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
 
   const int h = map_head(blockIdx.x, a.heads_q);
@@ -171,18 +182,18 @@ __global__ __launch_bounds__(256, SA_DQ_OCC) void sinkattn_bwd_dq_bf16_d64(DqArg
   }
 
   int seg[4];
-  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BK, seg);
+  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BKL, seg);
   const int n0 = seg[1] - seg[0];
   const int ntiles = n0 + (nseg > 1 ? seg[3] - seg[2] : 0);
 
   // K / V tiles go straight from global memory into swizzled LDS tiles
   auto load_tile = [&](int t, int buf) {
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
-    const int r0 = kt * BK;
-    tile_load_lds<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
-                             kv_row_stride, sv.len - r0, wave, lane);
-    tile_load_lds<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
-                             kv_row_stride, sv.len - r0, wave, lane);
+    const int r0 = kt * BKL;
+    tile_load_lds<BKL, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
+                              kv_row_stride, sv.len - r0, wave, lane);
+    tile_load_lds<BKL, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
+                              kv_row_stride, sv.len - r0, wave, lane);
   };
 
   f32x16 acc[QB][2];   // dQ: C layout [m = query][n = d], lane = d
@@ -197,15 +208,18 @@ __global__ __launch_bounds__(256, SA_DQ_OCC) void sinkattn_bwd_dq_bf16_d64(DqArg
     const int buf = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
-    const int k0 = kt * BK;
-    const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
-                                : SA_TILE_SKIP;
-    const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
-    const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
-    if (cls == SA_TILE_FULL) {
-      tile_step<false>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
-    } else if (cls == SA_TILE_PARTIAL) {
-      tile_step<true>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+#pragma unroll
+    for (int sub = 0; sub < KSUB; ++sub) {
+      const int k0 = kt * BKL + sub * BK;
+      const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
+                                  : SA_TILE_SKIP;
+      const bf16* ks = smem + (2 * buf) * TILE_ELEMS + sub * BK * D;
+      const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS + sub * BK * D;
+      if (cls == SA_TILE_FULL) {
+        tile_step<false>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      } else if (cls == SA_TILE_PARTIAL) {
+        tile_step<true>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      }
     }
     wait_all_mem();
     __syncthreads();
@@ -256,6 +270,6 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
   a.scale = scale;
   if (a.num_q_tiles == 0 || batch == 0) return hipSuccess;
   dim3 grid(heads_q, batch, a.num_q_tiles);
-  hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64, grid, dim3(WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }

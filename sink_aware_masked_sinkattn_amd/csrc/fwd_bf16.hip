@@ -15,9 +15,11 @@
 //   sigmoid(l - s) * Obar = acc / (r + exp(s - m)) when acc = sum exp(S - m) v,
 // the sink scaling costs one extra exponential per row in the epilogue.
 //
-// Work decomposition (one workgroup = 4 waves = 256 query rows of one head):
-//   * each wave owns 64 query rows (two 32-row MFMA blocks) whose Q fragments
-//     stay in registers for the whole kernel;
+// Work decomposition (one workgroup = WAVES waves x QB*32 query rows of one
+// head; by default 4 waves x 32 rows, 3 waves per SIMD):
+//   * each wave owns QB 32-row MFMA blocks of query rows whose Q fragments
+//     stay in registers for the whole kernel; each key tile's K and V^T
+//     operands are read from LDS once, up front, and shared by the blocks;
 //   * key tiles of 64 rows are listed per workgroup from the mask (prefix
 //     tiles + window tiles, each once), double-buffered in LDS: K row-major,
 //     V row-major and read transposed with ds_read_tr16_b64;
@@ -36,11 +38,22 @@
 namespace {
 
 constexpr int D = 64;
-constexpr int QB = 2;                    // 32-row query blocks per wave
-constexpr int WAVES = 4;
-constexpr int BQ = WAVES * QB * 32;      // 256 query rows per workgroup
+#ifndef SA_FWD_QB
+#define SA_FWD_QB 1
+#endif
+#ifndef SA_FWD_WAVES
+#define SA_FWD_WAVES 4
+#endif
+constexpr int QB = SA_FWD_QB;          // 32-row query blocks per wave
+constexpr int WAVES = SA_FWD_WAVES;    // waves per workgroup
+constexpr int BQ = WAVES * QB * 32;      // query rows per workgroup
 constexpr int BK = 64;                   // key rows per LDS tile
-constexpr int TILE_ELEMS = BK * D;       // swizzled rows (tile_off)
+#ifndef SA_FWD_KSUB
+#define SA_FWD_KSUB 1
+#endif
+constexpr int KSUB = SA_FWD_KSUB;           // 64-key compute steps per LDS key tile
+constexpr int BKL = BK * KSUB;          // key rows per LDS tile
+constexpr int TILE_ELEMS = BKL * D;       // swizzled rows (tile_off)
 constexpr int OROW = D + 8;              // padded row of the epilogue staging buffer
 // LDS: two K/V tile pairs during the key loop; afterwards the same memory
 // stages each wave's 64 output rows (padded) for row-contiguous stores.
@@ -73,7 +86,7 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
   return x;
 }
 
-// One 64-key tile against this wave's 64 query rows (two 32-row blocks).
+// One 64-key tile against this wave's QB blocks of 32 query rows.
 // MASK: apply the element predicate (partial tiles only).
 template <bool MASK>
 __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const bf16x8 (&qf)[QB][4],
@@ -84,9 +97,28 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
   const int g = lane >> 5;
   const int grp = lane >> 4;
   const int li = lane & 15;
-  // ---- S^T = K Q^T for both 32-key blocks and both query blocks: lane =
-  // query, 16 keys per block in registers.  Each K fragment (keys on m, head
-  // dim on k) is read from LDS right before the two MFMAs that use it.
+  // ---- operands of this tile, all issued up front so the LDS latency is
+  // paid once: K (keys on m, head dim on k) and V^T (head dim on m, keys on
+  // k, by transpose reads)
+  bf16x8 kf[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8*)(ks + tile_off(kb * 32 + l32, 16 * s + 8 * g));
+  bf16x8 vt[2][2][2];   // [db][kb][hh]
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r0 = kb * 32 + 16 * hh + 4 * g + (li >> 2);
+        vt[db][kb][hh] = cat8(lds_read_tr4(vs + tile_off(r0, c0)), lds_read_tr4(vs + tile_off(r0 + 8, c0)));
+      }
+  }
+  // ---- S^T = K Q^T for both 32-key blocks and all query blocks: lane =
+  // query, 16 keys per block in registers
   f32x16 st[2][QB];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -95,11 +127,9 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 kf = *(const bf16x8*)(ks + tile_off(kb * 32 + l32, 16 * s + 8 * g));
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) st[kb][qb] = mfma32x32x16(kf, qf[qb][s], st[kb][qb]);
-    }
+      for (int qb = 0; qb < QB; ++qb) st[kb][qb] = mfma32x32x16(kf[kb][s], qf[qb][s], st[kb][qb]);
   if (MASK) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -149,26 +179,21 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
     }
     r_run[qb] += rs;
   }
-  // ---- O^T += V^T P^T; V^T operands (head dim on m, keys on k) by transpose reads
+  // ---- O^T += V^T P^T
 #pragma unroll
-  for (int db = 0; db < 2; ++db) {
-    const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
+  for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r0 = kb * 32 + 16 * hh + 4 * g + (li >> 2);
-        const bf16x8 vt = cat8(lds_read_tr4(vs + tile_off(r0, c0)), lds_read_tr4(vs + tile_off(r0 + 8, c0)));
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(vt, pf[kb][qb][hh], acc[qb][db]);
-      }
-  }
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(vt[db][kb][hh], pf[kb][qb][hh], acc[qb][db]);
 }
 
 #ifndef SA_FWD_OCC
-#define SA_FWD_OCC 2   // waves per SIMD the register budget is set for
+#define SA_FWD_OCC 3   // waves per SIMD the register budget is set for
 #endif
-__global__ __launch_bounds__(256, SA_FWD_OCC) void sinkattn_fwd_bf16_d64(FwdArgs a) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC, SA_FWD_OCC))) void sinkattn_fwd_bf16_d64(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 smem[SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
 
   const int h = map_head(blockIdx.x, a.heads_q);
@@ -212,7 +237,7 @@ __global__ __launch_bounds__(256, SA_FWD_OCC) void sinkattn_fwd_bf16_d64(FwdArgs
   }
 
   int seg[4];
-  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BK, seg);
+  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BKL, seg);
   const int n0 = seg[1] - seg[0];
   const int ntiles = n0 + (nseg > 1 ? seg[3] - seg[2] : 0);
 
@@ -220,11 +245,11 @@ __global__ __launch_bounds__(256, SA_FWD_OCC) void sinkattn_fwd_bf16_d64(FwdArgs
   // K / V tiles go straight from global memory into swizzled LDS tiles
   auto load_tile = [&](int t, int buf) {
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
-    const int r0 = kt * BK;
-    tile_load_lds<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
-                             kv_row_stride, sv.len - r0, wave, lane);
-    tile_load_lds<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
-                             kv_row_stride, sv.len - r0, wave, lane);
+    const int r0 = kt * BKL;
+    tile_load_lds<BKL, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
+                              kv_row_stride, sv.len - r0, wave, lane);
+    tile_load_lds<BKL, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
+                              kv_row_stride, sv.len - r0, wave, lane);
   };
 
   f32x16 acc[QB][2];
@@ -245,15 +270,18 @@ __global__ __launch_bounds__(256, SA_FWD_OCC) void sinkattn_fwd_bf16_d64(FwdArgs
     const int buf = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
-    const int k0 = kt * BK;
-    const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
-                                : SA_TILE_SKIP;
-    const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
-    const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
-    if (cls == SA_TILE_FULL) {
-      tile_step<false>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
-    } else if (cls == SA_TILE_PARTIAL) {
-      tile_step<true>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+#pragma unroll
+    for (int sub = 0; sub < KSUB; ++sub) {
+      const int k0 = kt * BKL + sub * BK;
+      const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
+                                  : SA_TILE_SKIP;
+      const bf16* ks = smem + (2 * buf) * TILE_ELEMS + sub * BK * D;
+      const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS + sub * BK * D;
+      if (cls == SA_TILE_FULL) {
+        tile_step<false>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      } else if (cls == SA_TILE_PARTIAL) {
+        tile_step<true>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      }
     }
     wait_all_mem();
     __syncthreads();
@@ -287,7 +315,7 @@ __global__ __launch_bounds__(256, SA_FWD_OCC) void sinkattn_fwd_bf16_d64(FwdArgs
   if (wave_active) {
     bf16* obase = a.o + (size_t)sv.row_base * q_row_stride + (size_t)h * D;
 #pragma unroll
-    for (int it = 0; it < (QB * 32 * D) / (64 * 8); ++it) {   // 8 iterations of 64 lanes x 16 B
+    for (int it = 0; it < (QB * 32 * D) / (64 * 8); ++it) {   // 64 lanes x 16 B per iteration
       const int chunk = it * 64 + lane;
       const int r = chunk >> 3;
       const int c = (chunk & 7) * 8;
@@ -317,6 +345,6 @@ hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, cons
   a.scale_log2 = scale * SA_LOG2E;
   if (a.num_q_tiles == 0 || batch == 0 || heads_q == 0) return hipSuccess;
   dim3 grid(heads_q, batch, a.num_q_tiles);
-  hipLaunchKernelGGL(sinkattn_fwd_bf16_d64, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(sinkattn_fwd_bf16_d64, grid, dim3(WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }
