@@ -12,16 +12,19 @@
 // S and dP are recomputed tile by tile from Q, K, V, dO and L.
 //
 // Work decomposition.  A workgroup (4 waves) owns 128 keys of one kv head,
-// 32 per wave, whose K and V fragments stay in registers.  The (query head,
-// 64-row query tile) pairs that can see those keys -- rows [k0, n) for a
-// prefix key, [k0, k1 + w] otherwise -- form a flat iteration list that is
+// 32 per wave (by default; KB 32-key blocks per wave), whose K and V
+// fragments stay in registers; query tiles are BQ rows (128 by default).  The (query tile,
+// query head) pairs that can see those keys -- rows [k0, n) for a prefix
+// key, [k0, k1 + w] otherwise -- form a flat iteration list (tiles from the
+// last down, heads innermost) that is
 // cut into chunks of `chunk` iterations, one workgroup per chunk, so that
 // prefix keys (seen by every later row) and early causal keys do not leave
 // one workgroup running long after the rest.  A key block covered by one
 // chunk stores its fp32 result; a key block cut into several chunks adds
 // them with one float atomic per element, once per chunk.
 //
-// Per iteration, per wave, on MFMA 32x32x16 with one key per lane (C layout):
+// Per iteration, per wave and 32-row query block, on MFMA 32x32x16 with one
+// key per lane (C layout):
 //   S = Q K^T, dP = dO V^T   (A = Q, dO rows from LDS; B = K, V registers)
 //   P' and dS computed in registers are already the A operand (keys on m,
 //   queries on k) of dV += P'^T dO and dK += dS^T Q, whose B operands
@@ -35,10 +38,14 @@ namespace {
 
 constexpr int D = 64;
 constexpr int WAVES = 4;
-constexpr int KW = 32;                 // keys per wave
-constexpr int BKW = WAVES * KW;        // 128 keys per workgroup
+#ifndef SA_DKDV_KB
+#define SA_DKDV_KB 1
+#endif
+constexpr int KB = SA_DKDV_KB;         // 32-key MFMA blocks per wave
+constexpr int KW = 32 * KB;            // keys per wave
+constexpr int BKW = WAVES * KW;        // keys per workgroup
 #ifndef SA_DKDV_BQ
-#define SA_DKDV_BQ 64
+#define SA_DKDV_BQ 128
 #endif
 constexpr int BQ = SA_DKDV_BQ;         // query rows per tile (multiple of 32)
 constexpr int NQB = BQ / 32;           // 32-row MFMA blocks per tile
@@ -66,14 +73,16 @@ struct __attribute__((aligned(16))) DkvSmem {
   float dd[2][BQ];
 };
 
-// One BQ-row query tile against this wave's 32 keys.  MASK: apply the element
-// predicate (partial tiles); full tiles run without any mask arithmetic.
+// One BQ-row query tile against this wave's KW keys (KB blocks of 32).
+// MASK: apply the element predicate (partial tiles); full tiles run without
+// any mask arithmetic.  The query-side operands (Q, dO rows and their
+// transposes) are read once per 32-row block and shared by the key blocks.
 template <bool MASK>
 __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const float* l2s,
-                                          const float* dds, const bf16x8 (&kf)[4],
-                                          const bf16x8 (&vf)[4], f32x16 (&dk)[2], f32x16 (&dv)[2],
-                                          int q0, int kw0, int window, int prefix,
-                                          float scale_log2, int lane) {
+                                          const float* dds, const bf16x8 (&kf)[KB][4],
+                                          const bf16x8 (&vf)[KB][4], f32x16 (&dk)[KB][2],
+                                          f32x16 (&dv)[KB][2], int q0, int kw0, int window,
+                                          int prefix, float scale_log2, int lane) {
   const int l32 = lane & 31;
   const int g = lane >> 5;
   const int grp = lane >> 4;
@@ -87,11 +96,16 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
       qa[s] = *(const bf16x8*)(qs + tile_off(qb * 32 + l32, 16 * s + 8 * g));
       da[s] = *(const bf16x8*)(dos + tile_off(qb * 32 + l32, 16 * s + 8 * g));
     }
-    f32x16 st = f32x16{}, dp = f32x16{};
+    f32x16 st[KB], dp[KB];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      st = mfma32x32x16(qa[s], kf[s], st);
-      dp = mfma32x32x16(da[s], vf[s], dp);
+    for (int kb = 0; kb < KB; ++kb) {
+      st[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        st[kb] = mfma32x32x16(qa[s], kf[kb][s], st[kb]);
+        dp[kb] = mfma32x32x16(da[s], vf[kb][s], dp[kb]);
+      }
     }
     // B operands of dV += P'^T dO and dK += dS^T Q (query index along k):
     // transpose reads; issued before the softmax arithmetic
@@ -107,36 +121,39 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
       }
     }
     // P' = exp2(S*scale*log2e - L*log2e), dS = P' (dP - D); this lane's C rows
-    // are queries qb*32 + 8*(i/4) + 4g + i%4, its column is key kw0 + l32
-    float pp[16], dsv[16];
+    // are queries qb*32 + 8*(i/4) + 4g + i%4, its column is key kw0 + kb*32 + l32
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int qr = qb * 32 + 8 * i4 + 4 * g;
-      const f32x4 l4 = *(const f32x4*)(l2s + qr);
-      const f32x4 d4 = *(const f32x4*)(dds + qr);
+    for (int kb = 0; kb < KB; ++kb) {
+      float pp[16], dsv[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 4 * i4 + e;
-        float p = fast_exp2(fmaf(st[i], scale_log2, -l4[e]));
-        if (MASK) {
-          const int q = q0 + qr + e, k = kw0 + l32;
-          const bool vis = (k <= q) & ((q - k <= window) | (k < prefix));
-          p = vis ? p : 0.0f;
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int qr = qb * 32 + 8 * i4 + 4 * g;
+        const f32x4 l4 = *(const f32x4*)(l2s + qr);
+        const f32x4 d4 = *(const f32x4*)(dds + qr);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * i4 + e;
+          float p = fast_exp2(fmaf(st[kb][i], scale_log2, -l4[e]));
+          if (MASK) {
+            const int q = q0 + qr + e, k = kw0 + kb * 32 + l32;
+            const bool vis = (k <= q) & ((q - k <= window) | (k < prefix));
+            p = vis ? p : 0.0f;
+          }
+          pp[i] = p;
+          dsv[i] = p * (dp[kb][i] - d4[e]);
         }
-        pp[i] = p;
-        dsv[i] = p * (dp[i] - d4[e]);
       }
-    }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const bf16x8 pa = to_bf16x8(pp[8 * hh], pp[8 * hh + 1], pp[8 * hh + 2], pp[8 * hh + 3],
-                                  pp[8 * hh + 4], pp[8 * hh + 5], pp[8 * hh + 6], pp[8 * hh + 7]);
-      const bf16x8 sa = to_bf16x8(dsv[8 * hh], dsv[8 * hh + 1], dsv[8 * hh + 2], dsv[8 * hh + 3],
-                                  dsv[8 * hh + 4], dsv[8 * hh + 5], dsv[8 * hh + 6], dsv[8 * hh + 7]);
+      for (int hh = 0; hh < 2; ++hh) {
+        const bf16x8 pa = to_bf16x8(pp[8 * hh], pp[8 * hh + 1], pp[8 * hh + 2], pp[8 * hh + 3],
+                                    pp[8 * hh + 4], pp[8 * hh + 5], pp[8 * hh + 6], pp[8 * hh + 7]);
+        const bf16x8 sa = to_bf16x8(dsv[8 * hh], dsv[8 * hh + 1], dsv[8 * hh + 2], dsv[8 * hh + 3],
+                                    dsv[8 * hh + 4], dsv[8 * hh + 5], dsv[8 * hh + 6], dsv[8 * hh + 7]);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        dv[db] = mfma32x32x16(pa, dob[hh][db], dv[db]);
-        dk[db] = mfma32x32x16(sa, qbt[hh][db], dk[db]);
+        for (int db = 0; db < 2; ++db) {
+          dv[kb][db] = mfma32x32x16(pa, dob[hh][db], dv[kb][db]);
+          dk[kb][db] = mfma32x32x16(sa, qbt[hh][db], dk[kb][db]);
+        }
       }
     }
   }
@@ -181,18 +198,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC
   const bf16* vbase = a.v + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
 
   // K / V fragments, B operand of S = Q K^T and dP = dO V^T:
-  // lane = key kw0 + l32, head-dim chunk 16s + 8g .. +7.
-  bf16x8 kf[4], vf[4];
-  {
-    const int key = kw0 + l32;
+  // lane = key kw0 + kb*32 + l32, head-dim chunk 16s + 8g .. +7.
+  bf16x8 kf[KB][4], vf[KB][4];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int key = kw0 + kb * 32 + l32;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (key < sv.len) {
-        kf[s] = *(const bf16x8*)(kbase + (size_t)key * kv_row_stride + 16 * s + 8 * g);
-        vf[s] = *(const bf16x8*)(vbase + (size_t)key * kv_row_stride + 16 * s + 8 * g);
+        kf[kb][s] = *(const bf16x8*)(kbase + (size_t)key * kv_row_stride + 16 * s + 8 * g);
+        vf[kb][s] = *(const bf16x8*)(vbase + (size_t)key * kv_row_stride + 16 * s + 8 * g);
       } else {
-        kf[s] = bf16x8{};
-        vf[s] = bf16x8{};
+        kf[kb][s] = bf16x8{};
+        vf[kb][s] = bf16x8{};
       }
     }
   }
@@ -201,10 +219,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC
   // L (in log2 units) and D go through one register per thread, with
   // L = +inf for rows past the end of the sequence so P' = dS = 0 there.
   float lreg = 0.0f;
+  // Iteration order: query tiles from the last to the first, query heads
+  // innermost.  All key blocks of a causal layer share the same last tile, so
+  // workgroups running at the same time walk the same (tile, head) sequence
+  // in step and their Q/dO tiles stay in the XCD's L2.
+  const int qt_last = qt_begin + n_qt - 1;
   auto tile_of = [&](int it, int* h, int* q0) {
-    const int hi = it / n_qt;
-    *h = h_begin + hi;
-    *q0 = (qt_begin + (it - hi * n_qt)) * BQ;
+    const int ti = it / a.group;
+    *h = h_begin + (it - ti * a.group);
+    *q0 = (qt_last - ti) * BQ;
   };
   auto load_tile = [&](int it, int buf) {
     int h, q0;
@@ -225,8 +248,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC
     else if (tid < 2 * BQ) sm.dd[buf][tid - BQ] = lreg;
   };
 
-  f32x16 dk_acc[2], dv_acc[2];
-  dk_acc[0] = dk_acc[1] = dv_acc[0] = dv_acc[1] = f32x16{};
+  f32x16 dk_acc[KB][2], dv_acc[KB][2];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) dk_acc[kb][0] = dk_acc[kb][1] = dv_acc[kb][0] = dv_acc[kb][1] = f32x16{};
 
   load_tile(it_begin, 0);
   store_stats(0);
@@ -254,26 +278,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC
     __syncthreads();
   }
 
-  // ---- C rows are keys kw0 + 8*(i/4) + 4g + i%4, column d = db*32 + l32
+  // ---- C rows are keys kw0 + kb*32 + 8*(i/4) + 4g + i%4, column d = db*32 + l32
   if (wave_active) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db) {
-      float* dkb = a.dk_acc + ((size_t)sv.row_base * a.heads_kv + kvh) * D + db * 32 + l32;
-      float* dvb = a.dv_acc + ((size_t)sv.row_base * a.heads_kv + kvh) * D + db * 32 + l32;
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kw0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key < sv.len) {
-          if (single) {
-            dkb[(size_t)key * kv_row_stride] = dk_acc[db][i];
-            dvb[(size_t)key * kv_row_stride] = dv_acc[db][i];
-          } else {
-            unsafeAtomicAdd(dkb + (size_t)key * kv_row_stride, dk_acc[db][i]);
-            unsafeAtomicAdd(dvb + (size_t)key * kv_row_stride, dv_acc[db][i]);
+      for (int db = 0; db < 2; ++db) {
+        float* dkb = a.dk_acc + ((size_t)sv.row_base * a.heads_kv + kvh) * D + db * 32 + l32;
+        float* dvb = a.dv_acc + ((size_t)sv.row_base * a.heads_kv + kvh) * D + db * 32 + l32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kw0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key < sv.len) {
+            if (single) {
+              dkb[(size_t)key * kv_row_stride] = dk_acc[kb][db][i];
+              dvb[(size_t)key * kv_row_stride] = dv_acc[kb][db][i];
+            } else {
+              unsafeAtomicAdd(dkb + (size_t)key * kv_row_stride, dk_acc[kb][db][i]);
+              unsafeAtomicAdd(dvb + (size_t)key * kv_row_stride, dv_acc[kb][db][i]);
+            }
           }
         }
       }
-    }
   }
 }
 
