@@ -100,6 +100,72 @@ __global__ __launch_bounds__(256) void sinkattn_bwd_pre(PreArgs a) {
   if (lane == 0 && r_end > r_begin) unsafeAtomicAdd(a.dsinks + h, ds_part);
 }
 
+// Same pass, one thread per (row, head): thread t of a block handles query
+// head t % Hq of row (block row base) + t / Hq + k * (256 / Hq), k < passes.
+// Consecutive threads read consecutive heads of a row, i.e. one contiguous
+// Hq * D stretch of O and dO; every thread issues all 16-byte loads of its
+// row segment at once.  Used when 256 % Hq == 0.  ds_h partials are summed
+// per head in LDS, then added with one atomic per (block, head).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void sinkattn_bwd_pre_rows(PreArgs a, int passes) {
+  constexpr int kVec = 16 / (int)sizeof(T);          // elements per 16-byte load
+  constexpr int kLoads = D / kVec;
+  __shared__ float red[256];
+  const int t = threadIdx.x;
+  const int h = t % a.heads_q;
+  const int rows_per_pass = 256 / a.heads_q;
+  const int z = blockIdx.z;
+  const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
+  const int r_begin = blockIdx.x * rows_per_pass * passes + t / a.heads_q;
+  const float s = a.sinks[h];
+  const bool zero_kv = (a.dk_acc != nullptr) && (h % a.group == 0);
+  const int kvh = h / a.group;
+  float ds_part = 0.0f;
+  for (int k = 0; k < passes; ++k) {
+    const int r = r_begin + k * rows_per_pass;
+    if (r >= sv.len) break;
+    const size_t row = (size_t)sv.row_base + r;
+    const size_t off = (row * a.heads_q + h) * D;
+    uint4 ov[kLoads], dv[kLoads];
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      ov[j] = ((const uint4*)((const T*)a.o + off))[j];
+      dv[j] = ((const uint4*)((const T*)a.dout + off))[j];
+    }
+    float dot = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const T* po = (const T*)&ov[j];
+      const T* pd = (const T*)&dv[j];
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) dot = fmaf(to_f32(po[e]), to_f32(pd[e]), dot);
+    }
+    if (zero_kv) {
+      float4* pk = (float4*)(a.dk_acc + (row * a.heads_kv + kvh) * D);
+      float4* pv = (float4*)(a.dv_acc + (row * a.heads_kv + kvh) * D);
+#pragma unroll
+      for (int j = 0; j < D / 4; ++j) {
+        pk[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        pv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    const float l = a.lse[sv.lse_base + (size_t)h * a.lse_head_stride + r];
+    const float mx = fmaxf(l, s);
+    const float big_l = (s == -INFINITY) ? l : mx + log1pf(expf(-fabsf(l - s)));
+    const size_t wi = (size_t)h * a.rows_total + row;
+    a.d_ws[wi] = dot;
+    a.l_ws[wi] = big_l;
+    ds_part -= expf(s - big_l) * dot;
+  }
+  red[t] = ds_part;
+  __syncthreads();
+  if (t < a.heads_q) {
+    float sum = 0.0f;
+    for (int i = t; i < 256; i += a.heads_q) sum += red[i];
+    if (sum != 0.0f) unsafeAtomicAdd(a.dsinks + t, sum);
+  }
+}
+
 __global__ void sinkattn_zero_f32(float* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -150,9 +216,24 @@ hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const v
   a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
   a.group = heads_q / heads_kv; a.rows_total = rows_total;
   a.lse_head_stride = lse_head_stride;
+  if (seqlen == 0 || batch == 0) return hipSuccess;
+  if (256 % heads_q == 0) {
+    const int rows_per_pass = 256 / heads_q;
+    const int passes = 4;
+    dim3 grid((seqlen + rows_per_pass * passes - 1) / (rows_per_pass * passes), 1, batch);
+    if (!dtype_is_f32 && head_dim == 64) {
+      hipLaunchKernelGGL((sinkattn_bwd_pre_rows<bf16, 64>), grid, dim3(256), 0, stream, a, passes);
+    } else if (dtype_is_f32 && head_dim == 64) {
+      hipLaunchKernelGGL((sinkattn_bwd_pre_rows<float, 64>), grid, dim3(256), 0, stream, a, passes);
+    } else if (dtype_is_f32 && head_dim == 32) {
+      hipLaunchKernelGGL((sinkattn_bwd_pre_rows<float, 32>), grid, dim3(256), 0, stream, a, passes);
+    } else {
+      return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   a.rows_per_wave = 256;
   dim3 grid((seqlen + a.rows_per_wave - 1) / a.rows_per_wave, (heads_q + 3) / 4, batch);
-  if (grid.x == 0 || batch == 0) return hipSuccess;
   if (!dtype_is_f32 && head_dim == 64) {
     hipLaunchKernelGGL((sinkattn_bwd_pre<bf16, 64>), grid, dim3(256), 0, stream, a);
   } else if (dtype_is_f32 && head_dim == 64) {
