@@ -124,6 +124,9 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
     // are queries qb*32 + 8*(i/4) + 4g + i%4, its column is key kw0 + kb*32 + l32
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
+      const int k = kw0 + kb * 32 + l32;
+      const int lim = k < prefix ? SA_LIM_PREFIX : window;
+      const int base = sa_opaque(q0 + qb * 32 + 4 * g - k);   // q - k = base + 8*(i/4) + i%4
       float pp[16], dsv[16];
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
@@ -134,11 +137,7 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * i4 + e;
           float p = fast_exp2(fmaf(st[kb][i], scale_log2, -l4[e]));
-          if (MASK) {
-            const int q = q0 + qr + e, k = kw0 + kb * 32 + l32;
-            const bool vis = (k <= q) & ((q - k <= window) | (k < prefix));
-            p = vis ? p : 0.0f;
-          }
+          if (MASK) p = sa_vis(base + 8 * i4 + e, lim) ? p : 0.0f;
           pp[i] = p;
           dsv[i] = p * (dp[kb][i] - d4[e]);
         }

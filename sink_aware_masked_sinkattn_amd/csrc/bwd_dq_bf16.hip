@@ -33,7 +33,7 @@ constexpr int D = 64;
 #endif
 constexpr int QB = SA_DQ_QB;          // 32-row query blocks per wave
 constexpr int WAVES = SA_DQ_WAVES;    // waves per workgroup
-constexpr int BQ = WAVES * QB * 32;   // 256
+constexpr int BQ = WAVES * QB * 32;   // query rows per workgroup
 constexpr int BK = 64;
 #ifndef SA_DQ_KSUB
 #define SA_DQ_KSUB 1
@@ -67,8 +67,8 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
   return x;
 }
 
-// One 64-key tile against this wave's 64 query rows.  MASK: apply the element
-// predicate (partial tiles only).
+// One 64-key tile against this wave's QB blocks of 32 query rows.  MASK:
+// apply the element predicate (partial tiles only).
 template <bool MASK>
 __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const bf16x8 (&qf)[QB][4],
                                           const bf16x8 (&df)[QB][4], const float (&l2)[QB],
@@ -107,17 +107,17 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
         st = mfma32x32x16(kf[s], qf[qb][s], st);
         dpt = mfma32x32x16(vf[s], df[qb][s], dpt);
       }
-      // dS^T: lane = query, rows = keys k0 + kb*32 + 8*(i/4) + 4g + i%4
-      const int q = qw0 + qb * 32 + l32;
+      // dS^T: lane = query, rows = keys kr + 8*(i/4) + i%4, kr = k0 + kb*32 + 4g;
+      // hidden scores become -inf, so P' = 0 there (scale > 0)
+      if (MASK) {
+        const int kr = k0 + kb * 32 + 4 * g;
+        const int base = sa_opaque(qw0 + qb * 32 + l32 - kr);
+        mask_query_lane<true>(st, base, sa_opaque(prefix - kr), window);
+      }
       float dsv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(fmaf(st[i], scale_log2, -l2[qb]));
-        if (MASK) {
-          const int k = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          const bool vis = (k <= q) & ((q - k <= window) | (k < prefix));
-          p = vis ? p : 0.0f;
-        }
+        const float p = fast_exp2(fmaf(st[i], scale_log2, -l2[qb]));
         dsv[i] = p * (dpt[i] - dd[qb]);
       }
       const bf16x8 d0 = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);

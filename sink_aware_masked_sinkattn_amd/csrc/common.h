@@ -76,6 +76,33 @@ __device__ __forceinline__ bf16x4 to_bf16x4(float a0, float a1, float a2, float 
   return __builtin_shufflevector(b0, b1, 0, 1, 2, 3);
 }
 
+// The mask M[q,k] = 1[k<=q] AND 1[q-k<=w OR k<p] as one unsigned compare:
+// with d = q - k (no overflow for positions in [0, 2^31)), M holds iff
+// (unsigned)d <= lim where lim = INT32_MAX for a prefix key (k < p) and w
+// otherwise -- a negative d wraps above every lim since w <= INT32_MAX.
+__device__ __forceinline__ bool sa_vis(int d, int lim) { return (unsigned)d <= (unsigned)lim; }
+constexpr int SA_LIM_PREFIX = 0x7fffffff;
+// Keep v in a register as computed: stops the compiler from re-associating
+// base - c_i and hoisting one loop-invariant register per element.
+__device__ __forceinline__ int sa_opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Mask one lane's 16 C-layout elements of a 32-key block when the lane holds
+// one query and element i holds key kr + c_i, c_i = 8*(i/4) + i%4, so that
+// q - k = base - c_i.  Hidden elements become -inf.  GENERAL: the block may
+// hold prefix keys (those with c_i < pb = p - kr); otherwise lim = w for all.
+template <bool GENERAL>
+__device__ __forceinline__ void mask_query_lane(f32x16& st, int base, int pb, int window) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int c = 8 * (i >> 2) + (i & 3);
+    const int lim = (GENERAL && c < pb) ? SA_LIM_PREFIX : window;
+    st[i] = sa_vis(base - c, lim) ? st[i] : -INFINITY;
+  }
+}
+
 // Where a sequence lives in the packed/batched tensors.
 struct SeqView {
   int row_base;  // first token row of the sequence in [B*T] or [N]

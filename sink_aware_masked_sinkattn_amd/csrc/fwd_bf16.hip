@@ -131,18 +131,15 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) st[kb][qb] = mfma32x32x16(kf[kb][s], qf[qb][s], st[kb][qb]);
   if (MASK) {
+    // element i of key block kb holds key kr + 8*(i/4) + i%4, kr = k0 + kb*32 + 4g
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int q = qw0 + qb * 32 + l32;
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int k = k0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          const bool vis = (k <= q) & ((q - k <= window) | (k < prefix));
-          st[kb][qb][i] = vis ? st[kb][qb][i] : -INFINITY;
-        }
-    }
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kr = k0 + kb * 32 + 4 * g;
+        const int base = sa_opaque(qw0 + qb * 32 + l32 - kr);
+        mask_query_lane<true>(st[kb][qb], base, sa_opaque(prefix - kr), window);
+      }
   }
   // ---- online softmax in the log2 domain, lazily rescaled
   bf16x8 pf[2][QB][2];
