@@ -48,6 +48,24 @@ KERNEL_FLOP_PER_PAIR = {"sinkattn_fwd_bf16_d64": 4, "sinkattn_bwd_dkdv_bf16_d64"
                         "sinkattn_bwd_dq_bf16_d64": 2}
 
 
+def kernel_variants(key_tile: int, query_tile: int) -> dict:
+    """Names of the kernels one layer launches, per timed phase, for the tile
+    shapes the library reports (narrow tiles carry a suffix)."""
+    if query_tile != 128:
+        raise ValueError(f"no dK/dV kernel with {query_tile}-row query tiles")
+    k32 = "_k32" if key_tile == 32 else ""
+    return {"fwd_ms": "sinkattn_fwd_bf16_d64" + k32,
+            "bwd_dkdv_ms": "sinkattn_bwd_dkdv_bf16_d64",
+            "bwd_dq_ms": "sinkattn_bwd_dq_bf16_d64" + k32}
+
+
+def kernel_base(name: str) -> str:
+    for suffix in ("_k32",):
+        if name.endswith(suffix):
+            return name[:-len(suffix)]
+    return name
+
+
 def visible_pairs_per_head(n: int, window: int, prefix: int) -> int:
     """Number of (q, k) pairs the mask leaves visible in one sequence of n
     tokens: row i sees min(i + 1, w + p + 1) keys."""
@@ -68,7 +86,7 @@ def useful_pairs(inp) -> int:
 
 def kernel_source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
+    for f in KERNEL_SOURCES[kernel_base(kernel)]:
         with open(os.path.join(ROOT, "sink_aware_masked_sinkattn_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -145,7 +163,8 @@ def main(argv=None):
 
     from sink_aware_masked_sinkattn_amd import (BWD_DKDV, BWD_DQ, BWD_FINISH, BWD_PREPARE,
                                                 load_library, make_problem, sinkattn_bwd_phases,
-                                                sinkattn_bwd_workspace_size, sinkattn_fwd)
+                                                sinkattn_bwd_workspace_size, sinkattn_fwd,
+                                                sinkattn_tile_config)
     from workloads import WORKLOADS, workload_inputs
 
     if not torch.cuda.is_available():
@@ -179,6 +198,7 @@ def main(argv=None):
                       torch.empty_like(r["v"]), torch.empty_like(r["s"]))
         r["ws"] = torch.empty(sinkattn_bwd_workspace_size(pb), dtype=torch.uint8, device=dev)
         r["pairs"] = useful_pairs(inp)
+        r["kernels"] = kernel_variants(*sinkattn_tile_config(pb))
     torch.cuda.synchronize()
 
     def step(events=None):
@@ -231,14 +251,18 @@ def main(argv=None):
     total_flops = sum(14 * d * r["pairs"] for r in runs)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the one with the largest total time per step
-    phase_of = {"sinkattn_fwd_bf16_d64": "fwd_ms", "sinkattn_bwd_dkdv_bf16_d64": "bwd_dkdv_ms",
-                "sinkattn_bwd_dq_bf16_d64": "bwd_dq_ms"}
-    kern_time = {k: sum(p[ph] for p in per_layer) for k, ph in phase_of.items()}
-    kern_flops = {k: sum(KERNEL_FLOP_PER_PAIR[k] * d * p["pairs"] for p in per_layer)
-                  for k in phase_of}
+    # dominant kernel: the one with the largest total time per step; each
+    # layer launches the tile variant the library picks for its window
+    kern_time, kern_flops, kern_launches = {}, {}, {}
+    for p, r in zip(per_layer, runs):
+        p["kernels"] = r["kernels"]
+        for ph, name in r["kernels"].items():
+            base = kernel_base(name)
+            kern_time[name] = kern_time.get(name, 0.0) + p[ph]
+            kern_flops[name] = kern_flops.get(name, 0) + KERNEL_FLOP_PER_PAIR[base] * d * p["pairs"]
+            kern_launches[name] = kern_launches.get(name, 0) + 1
     dom = max(kern_time, key=kern_time.get)
-    launches = len(per_layer)
+    launches = kern_launches[dom]
     avg_ms = kern_time[dom] / launches
     achieved = kern_flops[dom] / launches / (avg_ms * 1e-3) / 1e12
     traffic = committed_traffic(dom, args.workload)

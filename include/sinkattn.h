@@ -174,6 +174,17 @@ int32_t sinkattn_tile_class(int32_t q0, int32_t q1, int32_t k0, int32_t k1,
 int32_t sinkattn_key_tile_segments(int32_t q0, int32_t q1, int32_t window,
                                    int32_t prefix, int32_t block_k, int32_t *out);
 
+/*
+ * Tile shapes the bf16 kernels use for a problem, chosen from its window
+ * (after clamping to seqlen): short windows (w < 1024) get 32-key tiles in
+ * the forward and dQ kernels, so that fewer masked pairs are computed at the
+ * band's edges, otherwise 64-key tiles; the dK/dV kernel uses 128-row query
+ * tiles throughout.  Writes out[0] = forward / dQ key-tile width, out[1] =
+ * dK/dV query-tile height.  Host only, no HIP calls.  Returns the problem's
+ * validation status (out is written only on SINKATTN_OK).
+ */
+sinkattn_status sinkattn_tile_config(const sinkattn_problem *problem, int32_t *out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,11 +6,11 @@ the C ABI of ``include/sinkattn.h``); this package only binds it.
 from .binding import (BWD_ALL, BWD_DKDV, BWD_DQ, BWD_FINISH, BWD_PREPARE, WINDOW_INF, Problem,
                       SinkAttnError, load_library, make_problem, sinkattn_bwd,
                       sinkattn_bwd_phases, sinkattn_bwd_workspace_size, sinkattn_fwd,
-                      sinkattn_key_tile_segments, sinkattn_tile_class)
+                      sinkattn_key_tile_segments, sinkattn_tile_class, sinkattn_tile_config)
 
 __all__ = [
     "WINDOW_INF", "Problem", "SinkAttnError", "load_library", "make_problem",
     "BWD_PREPARE", "BWD_DKDV", "BWD_DQ", "BWD_FINISH", "BWD_ALL",
     "sinkattn_fwd", "sinkattn_bwd", "sinkattn_bwd_phases", "sinkattn_bwd_workspace_size",
-    "sinkattn_tile_class", "sinkattn_key_tile_segments",
+    "sinkattn_tile_class", "sinkattn_key_tile_segments", "sinkattn_tile_config",
 ]

@@ -95,6 +95,8 @@ def load_library(path: str = LIB_PATH):
     lib.sinkattn_tile_class.restype = i32
     lib.sinkattn_key_tile_segments.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(i32)]
     lib.sinkattn_key_tile_segments.restype = i32
+    lib.sinkattn_tile_config.argtypes = [pp, ctypes.POINTER(i32)]
+    lib.sinkattn_tile_config.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -234,3 +236,14 @@ def sinkattn_key_tile_segments(q0: int, q1: int, window: int, prefix: int, block
     if n < 0:
         raise ValueError("invalid arguments")
     return [(out[2 * i], out[2 * i + 1]) for i in range(n)]
+
+
+def sinkattn_tile_config(pb: Problem):
+    """(forward / dQ key-tile width, dK/dV query-tile height) the bf16
+    kernels use for this problem; host only."""
+    lib = load_library()
+    out = (ctypes.c_int32 * 2)()
+    st = lib.sinkattn_tile_config(ctypes.byref(pb), out)
+    if st != 0:
+        raise SinkAttnError(st, "sinkattn_tile_config", lib)
+    return int(out[0]), int(out[1])

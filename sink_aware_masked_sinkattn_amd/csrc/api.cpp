@@ -43,6 +43,8 @@ hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const v
 hipError_t launch_convert(int dtype_is_f32, const float* dk_acc, const float* dv_acc, void* dk,
                           void* dv, long long n_kv, float scale, hipStream_t stream);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
+int fwd_key_tile(int window);
+int dkdv_query_tile(int window);
 
 namespace {
 
@@ -135,6 +137,17 @@ int32_t sinkattn_key_tile_segments(int32_t q0, int32_t q1, int32_t window, int32
   const int n = sa_key_tile_segments(q0, q1, window, prefix, block_k, tmp);
   for (int i = 0; i < 4; ++i) out[i] = tmp[i];
   return n;
+}
+
+sinkattn_status sinkattn_tile_config(const sinkattn_problem* pb, int32_t* out) {
+  Dims dims;
+  const sinkattn_status st = check_problem(pb, &dims);
+  if (st != SINKATTN_OK) return st;
+  if (!out) return SINKATTN_ERR_NULL_POINTER;
+  const int window = pb->window > pb->seqlen ? pb->seqlen : pb->window;
+  out[0] = fwd_key_tile(window);
+  out[1] = dkdv_query_tile(window);
+  return SINKATTN_OK;
 }
 
 size_t sinkattn_bwd_workspace_size(const sinkattn_problem* pb) {

@@ -13,15 +13,17 @@
 //
 // Work decomposition.  A workgroup (4 waves) owns 128 keys of one kv head,
 // 32 per wave (by default; KB 32-key blocks per wave), whose K and V
-// fragments stay in registers; query tiles are BQ rows (128 by default).  The (query tile,
-// query head) pairs that can see those keys -- rows [k0, n) for a prefix
-// key, [k0, k1 + w] otherwise -- form a flat iteration list (tiles from the
-// last down, heads innermost) that is
-// cut into chunks of `chunk` iterations, one workgroup per chunk, so that
-// prefix keys (seen by every later row) and early causal keys do not leave
-// one workgroup running long after the rest.  A key block covered by one
-// chunk stores its fp32 result; a key block cut into several chunks adds
-// them with one float atomic per element, once per chunk.
+// fragments stay in registers; query tiles are BQ rows (128).  The (query
+// tile, query head) pairs that can see those keys -- rows [k0, n) for a
+// prefix key, [k0, k1 + w] otherwise -- form the block's iteration list
+// (tiles from the last down, heads innermost), cut into work units of
+// 2^chunk_shift iterations.  The grid is the exact list of work units (one
+// workgroup each, the extra units of the longest key blocks first), so
+// prefix keys (seen by every later row) and early causal keys do not leave a
+// few workgroups running long after the rest, and no workgroup is launched
+// without work.  A key
+// block covered by one unit stores its fp32 result; a key block cut into
+// several units adds them with one float atomic per element, once per unit.
 //
 // Per iteration, per wave and 32-row query block, on MFMA 32x32x16 with one
 // key per lane (C layout):
@@ -44,11 +46,7 @@ constexpr int WAVES = 4;
 constexpr int KB = SA_DKDV_KB;         // 32-key MFMA blocks per wave
 constexpr int KW = 32 * KB;            // keys per wave
 constexpr int BKW = WAVES * KW;        // keys per workgroup
-#ifndef SA_DKDV_BQ
-#define SA_DKDV_BQ 128
-#endif
-constexpr int BQ = SA_DKDV_BQ;         // query rows per tile (multiple of 32)
-constexpr int NQB = BQ / 32;           // 32-row MFMA blocks per tile
+// Query tiles of BQ rows (a template parameter; 128 in the launched kernel).
 
 struct DkvArgs {
   const bf16* q;
@@ -61,11 +59,12 @@ struct DkvArgs {
   float* dv_acc;          // [rows, Hkv, D] sum P'^T dO
   const int* cu_seqlens;
   int seqlen, heads_q, heads_kv, group, window, prefix, rows_total;
-  int chunk;              // iterations per workgroup
-  int max_chunks;         // grid z = batch * max_chunks
+  int batch;
+  int chunk_shift;        // iterations per work unit: 2^chunk_shift
   float scale_log2;
 };
 
+template <int BQ>
 struct __attribute__((aligned(16))) DkvSmem {
   bf16 qt[2][BQ * D];          // swizzled rows (tile_off)
   bf16 dot[2][BQ * D];
@@ -77,7 +76,7 @@ struct __attribute__((aligned(16))) DkvSmem {
 // MASK: apply the element predicate (partial tiles); full tiles run without
 // any mask arithmetic.  The query-side operands (Q, dO rows and their
 // transposes) are read once per 32-row block and shared by the key blocks.
-template <bool MASK>
+template <int BQ, bool MASK>
 __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const float* l2s,
                                           const float* dds, const bf16x8 (&kf)[KB][4],
                                           const bf16x8 (&vf)[KB][4], f32x16 (&dk)[KB][2],
@@ -88,7 +87,7 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
   const int grp = lane >> 4;
   const int li = lane & 15;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
+  for (int qb = 0; qb < BQ / 32; ++qb) {
     // A operands (query rows, head dim along k) for S = Q K^T and dP = dO V^T
     bf16x8 qa[4], da[4];
 #pragma unroll
@@ -158,16 +157,70 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
   }
 }
 
+// The flat work list, sequence by sequence: chunk indices from the highest
+// down, and for each index the key blocks that have that many chunks, in key
+// order.  The extra chunks of the longest key blocks (prefix keys and early
+// causal keys see the most rows) so come first, and the workgroups in flight
+// together share a chunk index -- with the iteration order below, the same
+// few query tiles, which stay in L2.  Key block 0 always has the most chunks
+// (its query range starts lowest and ends highest).  Every wave of the
+// workgroup finds work unit `item` with the same lane-parallel count (64 key
+// blocks per step).  False if item is past the end (the grid of a packed
+// batch is sized for every sequence at the longest length).
+template <int BQ>
+__device__ __forceinline__ bool dkdv_find_unit(const DkvArgs& a, int item, int lane, int* z_out,
+                                               int* kb_out, int* chunk_out) {
+  for (int z = 0; z < a.batch; ++z) {
+    const int len = a.cu_seqlens ? a.cu_seqlens[z + 1] - a.cu_seqlens[z] : a.seqlen;
+    const int nkb = (len + BKW - 1) / BKW;
+    if (nkb == 0) continue;
+    const int cmax = sa_dkdv_block_chunks(0, len, a.window, a.prefix, a.group, BQ, BKW,
+                                          a.chunk_shift);
+    // chunk counts of this lane's key blocks are recomputed per level when
+    // the sequence has more than 64 blocks, kept in a register otherwise
+    const int own = lane < nkb ? sa_dkdv_block_chunks(lane, len, a.window, a.prefix, a.group, BQ,
+                                                      BKW, a.chunk_shift)
+                               : 0;
+    for (int c = cmax - 1; c >= 0; --c) {
+      for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
+        const int kb = kb0 + lane;
+        const int ch = kb0 == 0 ? own
+                                : (kb < nkb ? sa_dkdv_block_chunks(kb, len, a.window, a.prefix,
+                                                                   a.group, BQ, BKW, a.chunk_shift)
+                                            : 0);
+        const bool has = ch > c;
+        const unsigned long long m = __ballot(has);
+        const int n = __builtin_popcountll(m);
+        if (item < n) {
+          // lane holding the item-th set bit of m
+          const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+          const int L = __builtin_ctzll(__ballot(has && below == item));
+          *z_out = __builtin_amdgcn_readfirstlane(z);
+          *kb_out = __builtin_amdgcn_readfirstlane(kb0 + L);
+          *chunk_out = __builtin_amdgcn_readfirstlane(c);
+          return true;
+        }
+        item -= n;
+      }
+    }
+  }
+  return false;
+}
+
 #ifndef SA_DKDV_OCC
 #define SA_DKDV_OCC 2   // waves per SIMD the register budget is set for
 #endif
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC, SA_DKDV_OCC))) void sinkattn_bwd_dkdv_bf16_d64(DkvArgs a) {
-  __shared__ DkvSmem sm;
+template <int BQ>
+__device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
+  __shared__ DkvSmem<BQ> sm;
 
-  const int kvh = blockIdx.x;
-  const int kblk = blockIdx.y;
-  const int z = blockIdx.z / a.max_chunks;
-  const int chunk_id = blockIdx.z - z * a.max_chunks;
+  // grid x = heads_kv * work units, kv head fastest (consecutive workgroups
+  // go to consecutive XCDs, so each XCD keeps to its kv heads)
+  const int kvh = blockIdx.x % a.heads_kv;
+  int z, kblk, chunk_id;
+  if (!dkdv_find_unit<BQ>(a, blockIdx.x / a.heads_kv, threadIdx.x & 63, &z, &kblk, &chunk_id))
+    return;
   const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
   const int k_start = kblk * BKW;
   if (k_start >= sv.len) return;
@@ -177,9 +230,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC
   const int qt_begin = q_lo / BQ;
   const int n_qt = q_hi / BQ - qt_begin + 1;
   const int n_iter_all = n_qt * a.group;
-  const int it_begin = chunk_id * a.chunk;
+  const int it_begin = chunk_id << a.chunk_shift;
   if (it_begin >= n_iter_all) return;
-  const int it_end = min(it_begin + a.chunk, n_iter_all);
+  const int it_end = min(it_begin + (1 << a.chunk_shift), n_iter_all);
   const bool single = (it_begin == 0) && (it_end == n_iter_all);
   const int h_begin = kvh * a.group;
 
@@ -266,10 +319,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC
     const int cls = wave_active ? sa_tile_class(q0, q1, kw0, kw0 + KW - 1, a.window, a.prefix)
                                 : SA_TILE_SKIP;
     if (cls == SA_TILE_FULL) {
-      tile_step<false>(sm.qt[buf], sm.dot[buf], sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
+      tile_step<BQ, false>(sm.qt[buf], sm.dot[buf], sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
                        q0, kw0, a.window, a.prefix, a.scale_log2, lane);
     } else if (cls == SA_TILE_PARTIAL) {
-      tile_step<true>(sm.qt[buf], sm.dot[buf], sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
+      tile_step<BQ, true>(sm.qt[buf], sm.dot[buf], sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
                       q0, kw0, a.window, a.prefix, a.scale_log2, lane);
     }
     if (it + 1 < it_end) store_stats(buf ^ 1);
@@ -302,24 +355,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC
   }
 }
 
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC, SA_DKDV_OCC))) void sinkattn_bwd_dkdv_bf16_d64(DkvArgs a) {
+  dkdv_body<128>(a);
+}
 }  // namespace
 
-// Iterations per workgroup: aim for a few thousand workgroups over the whole
-// call so the longest one is short next to the total, but keep chunks long
-// enough that the per-chunk atomic flush of dK/dV stays small.
-int bwd_dkdv_chunk(int batch, int seqlen, int heads_kv, int group, int window, int prefix) {
-  long long total = 0;
-  const int nkb = (seqlen + BKW - 1) / BKW;
-  for (int kb = 0; kb < nkb; ++kb) {
-    int lo, hi;
-    const int k0 = kb * BKW;
-    if (sa_query_range(k0, sa_min(k0 + BKW - 1, seqlen - 1), seqlen, window, prefix, &lo, &hi))
-      total += (long long)(hi / BQ - lo / BQ + 1) * group;
-  }
-  total *= (long long)batch * heads_kv;
-  long long c = 32;
-  while (c < 256 && c * 2048 < total) c *= 2;
-  return (int)c;
+// Query-tile height of the dK/dV kernel for a window w (already clamped to
+// the sequence length).  128 rows for every window: shorter tiles were
+// measured slower even for w = 128 (more iterations per workgroup).
+int dkdv_query_tile(int window) { (void)window; return 128; }
+
+// Iterations per work unit: about SA_DKDV_TARGET_WGS units over the whole call
+// so the longest one is short next to the total (no long tail), but long
+// enough that the per-unit atomic flush of dK/dV stays small.  A power of two.
+#ifndef SA_DKDV_TARGET_WGS
+#define SA_DKDV_TARGET_WGS 8192
+#endif
+#ifndef SA_DKDV_MIN_CHUNK_SHIFT
+#define SA_DKDV_MIN_CHUNK_SHIFT 4
+#endif
+int bwd_dkdv_chunk_shift(long long total_iters) {
+  int sh = SA_DKDV_MIN_CHUNK_SHIFT;
+  while (sh < 8 && ((long long)1 << sh) * SA_DKDV_TARGET_WGS < total_iters) ++sh;
+  return sh;
 }
 
 hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
@@ -335,12 +393,23 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
   a.group = heads_q / heads_kv; a.window = window; a.prefix = prefix;
   a.rows_total = rows_total;
   a.scale_log2 = scale * SA_LOG2E;
+  a.batch = batch;
   const int nkb = (seqlen + BKW - 1) / BKW;
   if (nkb == 0 || batch == 0) return hipSuccess;
-  a.chunk = bwd_dkdv_chunk(batch, seqlen, heads_kv, a.group, window, prefix);
-  const int max_iters = ((seqlen + BQ - 1) / BQ + 1) * a.group;
-  a.max_chunks = (max_iters + a.chunk - 1) / a.chunk;
-  dim3 grid(heads_kv, nkb, batch * a.max_chunks);
+  const int BQ = dkdv_query_tile(window);
+  // iterations of one sequence of seqlen tokens (for a packed batch seqlen is
+  // the longest length, so this bounds every sequence)
+  long long iters = 0;
+  for (int kb = 0; kb < nkb; ++kb)
+    iters += (long long)sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW, 0);
+  a.chunk_shift = bwd_dkdv_chunk_shift(iters * batch * heads_kv);
+  long long units = 0;
+  for (int kb = 0; kb < nkb; ++kb)
+    units += sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW, a.chunk_shift);
+  units *= batch;
+  if (units * heads_kv > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (units == 0) return hipSuccess;
+  dim3 grid((unsigned)(units * heads_kv));
   hipLaunchKernelGGL(sinkattn_bwd_dkdv_bf16_d64, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }

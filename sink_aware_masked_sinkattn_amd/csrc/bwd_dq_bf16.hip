@@ -34,19 +34,18 @@ constexpr int D = 64;
 constexpr int QB = SA_DQ_QB;          // 32-row query blocks per wave
 constexpr int WAVES = SA_DQ_WAVES;    // waves per workgroup
 constexpr int BQ = WAVES * QB * 32;   // query rows per workgroup
-constexpr int BK = 64;
-#ifndef SA_DQ_KSUB
-#define SA_DQ_KSUB 1
-#endif
-constexpr int KSUB = SA_DQ_KSUB;           // 64-key compute steps per LDS key tile
-constexpr int BKL = BK * KSUB;          // key rows per LDS tile
-constexpr int TILE_ELEMS = BKL * D;     // swizzled rows (tile_off)
 constexpr int OROW = D + 8;            // padded row of the epilogue staging buffer
-// LDS: two K/V tile pairs during the key loop; afterwards the same memory
-// stages each wave's 64 output rows (padded) for row-contiguous stores.
 constexpr int STAGE_ELEMS = WAVES * QB * 32 * OROW;
-constexpr int SMEM_ELEMS = (4 * TILE_ELEMS > STAGE_ELEMS) ? 4 * TILE_ELEMS : STAGE_ELEMS;
-static_assert(SMEM_ELEMS >= 4 * TILE_ELEMS && SMEM_ELEMS >= STAGE_ELEMS, "LDS sizing");
+// Key tiles of NKB blocks of 32 keys (64 in general, 32 for short windows).
+// LDS: two K/V tile pairs during the key loop; afterwards the same memory
+// stages each wave's output rows (padded) for row-contiguous stores.
+template <int NKB>
+struct DqTiles {
+  static constexpr int BK = 32 * NKB;
+  static constexpr int TILE_ELEMS = BK * D;   // swizzled rows (tile_off)
+  static constexpr int SMEM_ELEMS = (4 * TILE_ELEMS > STAGE_ELEMS) ? 4 * TILE_ELEMS : STAGE_ELEMS;
+  static_assert(SMEM_ELEMS >= 4 * TILE_ELEMS && SMEM_ELEMS >= STAGE_ELEMS, "LDS sizing");
+};
 
 struct DqArgs {
   const bf16* q;
@@ -67,9 +66,9 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
   return x;
 }
 
-// One 64-key tile against this wave's QB blocks of 32 query rows.  MASK:
-// apply the element predicate (partial tiles only).
-template <bool MASK>
+// One key tile (NKB blocks of 32 keys) against this wave's QB blocks of 32
+// query rows.  MASK: apply the element predicate (partial tiles only).
+template <int NKB, bool MASK>
 __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const bf16x8 (&qf)[QB][4],
                                           const bf16x8 (&df)[QB][4], const float (&l2)[QB],
                                           const float (&dd)[QB], f32x16 (&acc)[QB][2], int qw0,
@@ -80,7 +79,7 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
   const int grp = lane >> 4;
   const int li = lane & 15;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < NKB; ++kb) {
     // A operands of S^T = K Q^T and dP^T = V dO^T (keys on m, head dim on k)
     bf16x8 kf[4], vf[4];
 #pragma unroll
@@ -134,8 +133,12 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
 #ifndef SA_DQ_OCC
 #define SA_DQ_OCC 2   // waves per SIMD the register budget is set for
 #endif
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_DQ_OCC, SA_DQ_OCC))) void sinkattn_bwd_dq_bf16_d64(DqArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
+template <int NKB>
+__device__ __forceinline__ void dq_body(const DqArgs& a) {
+  using T = DqTiles<NKB>;
+  constexpr int BK = T::BK;
+  constexpr int TILE_ELEMS = T::TILE_ELEMS;
+  __shared__ __attribute__((aligned(16))) bf16 smem[T::SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
 
   const int h = map_head(blockIdx.x, a.heads_q);
   const int z = blockIdx.y;
@@ -182,18 +185,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_D
   }
 
   int seg[4];
-  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BKL, seg);
+  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BK, seg);
   const int n0 = seg[1] - seg[0];
   const int ntiles = n0 + (nseg > 1 ? seg[3] - seg[2] : 0);
 
   // K / V tiles go straight from global memory into swizzled LDS tiles
   auto load_tile = [&](int t, int buf) {
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
-    const int r0 = kt * BKL;
-    tile_load_lds<BKL, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
-                              kv_row_stride, sv.len - r0, wave, lane);
-    tile_load_lds<BKL, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
-                              kv_row_stride, sv.len - r0, wave, lane);
+    const int r0 = kt * BK;
+    tile_load_lds<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
+                             kv_row_stride, sv.len - r0, wave, lane);
+    tile_load_lds<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
+                             kv_row_stride, sv.len - r0, wave, lane);
   };
 
   f32x16 acc[QB][2];   // dQ: C layout [m = query][n = d], lane = d
@@ -208,18 +211,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_D
     const int buf = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
-#pragma unroll
-    for (int sub = 0; sub < KSUB; ++sub) {
-      const int k0 = kt * BKL + sub * BK;
-      const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
-                                  : SA_TILE_SKIP;
-      const bf16* ks = smem + (2 * buf) * TILE_ELEMS + sub * BK * D;
-      const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS + sub * BK * D;
-      if (cls == SA_TILE_FULL) {
-        tile_step<false>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
-      } else if (cls == SA_TILE_PARTIAL) {
-        tile_step<true>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
-      }
+    const int k0 = kt * BK;
+    const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
+                                : SA_TILE_SKIP;
+    const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
+    const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
+    if (cls == SA_TILE_FULL) {
+      tile_step<NKB, false>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+    } else if (cls == SA_TILE_PARTIAL) {
+      tile_step<NKB, true>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     }
     wait_all_mem();
     __syncthreads();
@@ -252,7 +252,16 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_D
   }
 }
 
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_DQ_OCC, SA_DQ_OCC))) void sinkattn_bwd_dq_bf16_d64(DqArgs a) {
+  dq_body<2>(a);
+}
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_DQ_OCC, SA_DQ_OCC))) void sinkattn_bwd_dq_bf16_d64_k32(DqArgs a) {
+  dq_body<1>(a);
+}
+
 }  // namespace
+
+int fwd_key_tile(int window);
 
 hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
                                   const float* l_ws, const float* d_ws, bf16* dq,
@@ -270,6 +279,9 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
   a.scale = scale;
   if (a.num_q_tiles == 0 || batch == 0) return hipSuccess;
   dim3 grid(heads_q, batch, a.num_q_tiles);
-  hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64, grid, dim3(WAVES * 64), 0, stream, a);
+  if (fwd_key_tile(window) == 32)
+    hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64_k32, grid, dim3(WAVES * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64, grid, dim3(WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }

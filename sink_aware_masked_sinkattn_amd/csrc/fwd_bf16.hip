@@ -47,19 +47,20 @@ constexpr int D = 64;
 constexpr int QB = SA_FWD_QB;          // 32-row query blocks per wave
 constexpr int WAVES = SA_FWD_WAVES;    // waves per workgroup
 constexpr int BQ = WAVES * QB * 32;      // query rows per workgroup
-constexpr int BK = 64;                   // key rows per LDS tile
-#ifndef SA_FWD_KSUB
-#define SA_FWD_KSUB 1
-#endif
-constexpr int KSUB = SA_FWD_KSUB;           // 64-key compute steps per LDS key tile
-constexpr int BKL = BK * KSUB;          // key rows per LDS tile
-constexpr int TILE_ELEMS = BKL * D;       // swizzled rows (tile_off)
+// Key tiles hold NKB blocks of 32 keys: 64-key tiles in general, 32-key
+// tiles for short windows, where a 32-row query block needs only w + 32 keys
+// and wider tiles would mostly compute masked pairs.
 constexpr int OROW = D + 8;              // padded row of the epilogue staging buffer
-// LDS: two K/V tile pairs during the key loop; afterwards the same memory
-// stages each wave's 64 output rows (padded) for row-contiguous stores.
 constexpr int STAGE_ELEMS = WAVES * QB * 32 * OROW;
-constexpr int SMEM_ELEMS = (4 * TILE_ELEMS > STAGE_ELEMS) ? 4 * TILE_ELEMS : STAGE_ELEMS;
-static_assert(SMEM_ELEMS >= 4 * TILE_ELEMS && SMEM_ELEMS >= STAGE_ELEMS, "LDS sizing");
+// LDS: two K/V tile pairs during the key loop; afterwards the same memory
+// stages each wave's output rows (padded) for row-contiguous stores.
+template <int NKB>
+struct FwdTiles {
+  static constexpr int BK = 32 * NKB;                 // key rows per LDS tile
+  static constexpr int TILE_ELEMS = BK * D;           // swizzled rows (tile_off)
+  static constexpr int SMEM_ELEMS = (4 * TILE_ELEMS > STAGE_ELEMS) ? 4 * TILE_ELEMS : STAGE_ELEMS;
+  static_assert(SMEM_ELEMS >= 4 * TILE_ELEMS && SMEM_ELEMS >= STAGE_ELEMS, "LDS sizing");
+};
 // Lazy rescaling: the running max used for the exponentials is only moved when
 // a row's true max exceeds it by more than this (log2 units), so probabilities
 // stay below 2^8 and most key tiles skip the accumulator rescale entirely.
@@ -86,9 +87,9 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
   return x;
 }
 
-// One 64-key tile against this wave's QB blocks of 32 query rows.
-// MASK: apply the element predicate (partial tiles only).
-template <bool MASK>
+// One key tile (NKB blocks of 32 keys) against this wave's QB blocks of 32
+// query rows.  MASK: apply the element predicate (partial tiles only).
+template <int NKB, bool MASK>
 __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const bf16x8 (&qf)[QB][4],
                                           f32x16 (&acc)[QB][2], float (&m_run)[QB],
                                           float (&r_run)[QB], int qw0, int k0, int window,
@@ -100,17 +101,17 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
   // ---- operands of this tile, all issued up front so the LDS latency is
   // paid once: K (keys on m, head dim on k) and V^T (head dim on m, keys on
   // k, by transpose reads)
-  bf16x8 kf[2][4];
+  bf16x8 kf[NKB][4];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8*)(ks + tile_off(kb * 32 + l32, 16 * s + 8 * g));
-  bf16x8 vt[2][2][2];   // [db][kb][hh]
+  bf16x8 vt[2][NKB][2];   // [db][kb][hh]
 #pragma unroll
   for (int db = 0; db < 2; ++db) {
     const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int r0 = kb * 32 + 16 * hh + 4 * g + (li >> 2);
@@ -119,15 +120,15 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
   }
   // ---- S^T = K Q^T for both 32-key blocks and all query blocks: lane =
   // query, 16 keys per block in registers
-  f32x16 st[2][QB];
+  f32x16 st[NKB][QB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) st[kb][qb] = f32x16{};
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) st[kb][qb] = mfma32x32x16(kf[kb][s], qf[qb][s], st[kb][qb]);
   if (MASK) {
@@ -135,19 +136,19 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         const int kr = k0 + kb * 32 + 4 * g;
         const int base = sa_opaque(qw0 + qb * 32 + l32 - kr);
         mask_query_lane<true>(st[kb][qb], base, sa_opaque(prefix - kr), window);
       }
   }
   // ---- online softmax in the log2 domain, lazily rescaled
-  bf16x8 pf[2][QB][2];
+  bf16x8 pf[NKB][QB][2];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     float mx = st[0][qb][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kb][qb][i]);
     mx = halves_max(mx) * scale_log2;
@@ -164,7 +165,7 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
     const float m_use = m_run[qb];
     float rs = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       float p[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -180,7 +181,7 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
 #pragma unroll
   for (int db = 0; db < 2; ++db)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -190,8 +191,12 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
 #ifndef SA_FWD_OCC
 #define SA_FWD_OCC 3   // waves per SIMD the register budget is set for
 #endif
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC, SA_FWD_OCC))) void sinkattn_fwd_bf16_d64(FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 smem[SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
+template <int NKB>
+__device__ __forceinline__ void fwd_body(const FwdArgs& a) {
+  using T = FwdTiles<NKB>;
+  constexpr int BK = T::BK;
+  constexpr int TILE_ELEMS = T::TILE_ELEMS;
+  __shared__ __attribute__((aligned(16))) bf16 smem[T::SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
 
   const int h = map_head(blockIdx.x, a.heads_q);
   const int z = blockIdx.y;
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_F
   }
 
   int seg[4];
-  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BKL, seg);
+  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BK, seg);
   const int n0 = seg[1] - seg[0];
   const int ntiles = n0 + (nseg > 1 ? seg[3] - seg[2] : 0);
 
@@ -242,11 +247,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_F
   // K / V tiles go straight from global memory into swizzled LDS tiles
   auto load_tile = [&](int t, int buf) {
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
-    const int r0 = kt * BKL;
-    tile_load_lds<BKL, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
-                              kv_row_stride, sv.len - r0, wave, lane);
-    tile_load_lds<BKL, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
-                              kv_row_stride, sv.len - r0, wave, lane);
+    const int r0 = kt * BK;
+    tile_load_lds<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
+                             kv_row_stride, sv.len - r0, wave, lane);
+    tile_load_lds<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
+                             kv_row_stride, sv.len - r0, wave, lane);
   };
 
   f32x16 acc[QB][2];
@@ -267,18 +272,15 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_F
     const int buf = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1, buf ^ 1);
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
-#pragma unroll
-    for (int sub = 0; sub < KSUB; ++sub) {
-      const int k0 = kt * BKL + sub * BK;
-      const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
-                                  : SA_TILE_SKIP;
-      const bf16* ks = smem + (2 * buf) * TILE_ELEMS + sub * BK * D;
-      const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS + sub * BK * D;
-      if (cls == SA_TILE_FULL) {
-        tile_step<false>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
-      } else if (cls == SA_TILE_PARTIAL) {
-        tile_step<true>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
-      }
+    const int k0 = kt * BK;
+    const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
+                                : SA_TILE_SKIP;
+    const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
+    const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
+    if (cls == SA_TILE_FULL) {
+      tile_step<NKB, false>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+    } else if (cls == SA_TILE_PARTIAL) {
+      tile_step<NKB, true>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     }
     wait_all_mem();
     __syncthreads();
@@ -324,7 +326,21 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_F
   }
 }
 
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC, SA_FWD_OCC))) void sinkattn_fwd_bf16_d64(FwdArgs a) {
+  fwd_body<2>(a);
+}
+#ifndef SA_FWD_OCC_K32
+#define SA_FWD_OCC_K32 4
+#endif
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC_K32, SA_FWD_OCC_K32))) void sinkattn_fwd_bf16_d64_k32(FwdArgs a) {
+  fwd_body<1>(a);
+}
+
 }  // namespace
+
+// Key-tile width of the forward and dQ kernels for a window w (already
+// clamped to the sequence length): 32 keys when w < 1024, else 64.
+int fwd_key_tile(int window) { return window < 1024 ? 32 : 64; }
 
 // Host-side launcher (called from the C ABI after validation).
 hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const float* sinks,
@@ -342,6 +358,9 @@ hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, cons
   a.scale_log2 = scale * SA_LOG2E;
   if (a.num_q_tiles == 0 || batch == 0 || heads_q == 0) return hipSuccess;
   dim3 grid(heads_q, batch, a.num_q_tiles);
-  hipLaunchKernelGGL(sinkattn_fwd_bf16_d64, grid, dim3(WAVES * 64), 0, stream, a);
+  if (fwd_key_tile(window) == 32)
+    hipLaunchKernelGGL(sinkattn_fwd_bf16_d64_k32, grid, dim3(WAVES * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(sinkattn_fwd_bf16_d64, grid, dim3(WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }

@@ -75,3 +75,18 @@ SA_HD bool sa_query_range(int k0, int k1, int n, int w, int p, int* qlo, int* qh
   *qhi = (int)hi;
   return *qlo <= *qhi;
 }
+
+// Work units of the dK/dV backward: key block kb (keys [kb*bkw, kb*bkw+bkw))
+// of a sequence of n tokens is paired with every (query tile of bq rows,
+// query head of the group) that can see it; those iterations are cut into
+// chunks of 2^chunk_shift.  Returns the number of chunks (0 if no row sees
+// the block).  Host and kernel use this same count to size and walk the flat
+// work list.
+SA_HD int sa_dkdv_block_chunks(int kb, int n, int w, int p, int group, int bq, int bkw,
+                               int chunk_shift) {
+  const int k0 = kb * bkw;
+  int lo, hi;
+  if (!sa_query_range(k0, sa_min(k0 + bkw - 1, n - 1), n, w, p, &lo, &hi)) return 0;
+  const int n_iter = (hi / bq - lo / bq + 1) * group;
+  return (n_iter + (1 << chunk_shift) - 1) >> chunk_shift;
+}

@@ -140,3 +140,16 @@ def test_bwd_phase_mask_validated():
     # a valid mask still runs the same host checks first (window < 0 here)
     bad = _problem(window=-1)
     assert lib.sinkattn_bwd_phases(15, ctypes.byref(bad), *args[1:]) == 3
+
+
+def test_tile_config():
+    # short windows: 32-key forward / dQ tiles; dK/dV always 128-row tiles; the
+    # window is clamped to the sequence length first (w >= T is plain causal)
+    assert binding.sinkattn_tile_config(_problem(window=128, seqlen=8192)) == (32, 128)
+    assert binding.sinkattn_tile_config(_problem(window=1023, seqlen=8192)) == (32, 128)
+    assert binding.sinkattn_tile_config(_problem(window=1024, seqlen=8192)) == (64, 128)
+    assert binding.sinkattn_tile_config(_problem(window=2**31 - 1, seqlen=8192)) == (64, 128)
+    assert binding.sinkattn_tile_config(_problem(window=2**31 - 1, seqlen=300)) == (32, 128)
+    with pytest.raises(binding.SinkAttnError):
+        binding.sinkattn_tile_config(_problem(window=-1))
+    assert _lib().sinkattn_tile_config(ctypes.byref(_problem()), None) == 1

@@ -34,3 +34,14 @@ def test_target_workload_flop_count():
 
 def test_multi_gpu_request_refused():
     assert bench.main(["--gpus", "2"]) == 2
+
+
+def test_kernel_variant_names():
+    import bench
+    wide = bench.kernel_variants(64, 128)
+    narrow = bench.kernel_variants(32, 128)
+    assert wide == {"fwd_ms": "sinkattn_fwd_bf16_d64", "bwd_dkdv_ms": "sinkattn_bwd_dkdv_bf16_d64",
+                    "bwd_dq_ms": "sinkattn_bwd_dq_bf16_d64"}
+    for ph, name in narrow.items():
+        assert bench.kernel_base(name) == wide[ph]
+        assert bench.kernel_source_sha(name) == bench.kernel_source_sha(wide[ph])

@@ -1,8 +1,8 @@
 """GPU parity: the HIP library (through its C ABI) against the fp64 oracle on
 the same seeded inputs.  Tolerances are in tests/parity_util.py.
 
-Small cases span several query tiles (256 rows forward, 64 backward) and key
-tiles (64 forward, 128 backward) with ragged tails, every mask regime
+Small cases span several query and key tiles of both tile configurations
+(narrow tiles for windows under 1024, wide ones otherwise) with ragged tails, every mask regime
 (plain causal, window, prefix, window+prefix, w=0, prefix past the end), GQA
 and varlen packing with empty, single-token and tile-edge lengths.  The
 named workloads run at their full sizes, compared on whole GQA groups.
@@ -31,6 +31,11 @@ SMALL = [
     (1, 64, 2, 1, 16, 4, 1.0),
     (3, 129, 16, 2, 31, 2, 0.5),
     (1, 1, 2, 1, 0, 0, 1.0),
+    # windows >= 1024 after clamping run the wide-tile kernels (64-key forward /
+    # dQ tiles, 128-row dK/dV tiles); shorter ones the narrow-tile kernels
+    (1, 1100, 4, 2, WINDOW_INF, 0, 0.5),
+    (1, 1090, 4, 1, 1030, 70, 0.5),
+    (2, 1200, 4, 2, 2000, 3, 0.5),
 ]
 
 
@@ -48,6 +53,7 @@ def test_bf16_small(case):
     ((0, 5, 0, 130), 4, 2),
     ((512, 1, 77), WINDOW_INF, 0),
     ((200, 300), 128, 16),
+    ((1100, 37, 0, 1030), WINDOW_INF, 5),
 ])
 def test_bf16_varlen_small(lengths, w, p):
     inp = make_inputs(batch=0, seqlen=0, heads_q=8, heads_kv=2, head_dim=64, window=w, prefix=p,
