@@ -4,7 +4,7 @@
 One step = one full pass of the hot path over the long-context workload
 (B=1, Hq=64, Hkv=8, d=64, T=8192, two attention layers: a 128-token
 sliding window with 4 prefix keys, and full causal): per layer the forward
-kernel, then the backward's prepare / main / finish phases.  Inputs are
+kernel, then the backward phases (prepare, dQ, dK/dV, finish).  Inputs are
 seeded synthetic bf16 tensors already resident in device memory; outputs
 and workspace are preallocated.
 
@@ -214,7 +214,7 @@ def main(argv=None):
                 ev[1].record()
             bargs = (*a, r["o"], r["lse"], r["do"], inp.window, inp.prefix, inp.scale, r["cu"],
                      r["ms"])
-            for j, ph in enumerate((BWD_PREPARE, BWD_DKDV, BWD_DQ, BWD_FINISH)):
+            for j, ph in enumerate((BWD_PREPARE, BWD_DQ, BWD_DKDV, BWD_FINISH)):
                 sinkattn_bwd_phases(ph, *bargs, workspace=r["ws"], grads=r["grads"])
                 if ev:
                     ev[2 + j].record()
@@ -247,7 +247,7 @@ def main(argv=None):
               for j in range(5)]
         per_layer.append({"window": r["inp"].window, "prefix": r["inp"].prefix,
                           "pairs": r["pairs"], "fwd_ms": ph[0], "bwd_prepare_ms": ph[1],
-                          "bwd_dkdv_ms": ph[2], "bwd_dq_ms": ph[3], "bwd_finish_ms": ph[4]})
+                          "bwd_dq_ms": ph[2], "bwd_dkdv_ms": ph[3], "bwd_finish_ms": ph[4]})
     total_flops = sum(14 * d * r["pairs"] for r in runs)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 

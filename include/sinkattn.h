@@ -126,23 +126,25 @@ sinkattn_status sinkattn_bwd(const sinkattn_problem *problem, const void *q,
  * work (or timing events) between them.  `phases` is a non-empty OR of the
  * flags below (other bits: SINKATTN_ERR_BAD_SHAPE); the other arguments are
  * exactly those of sinkattn_bwd and are validated the same way.  Phases must
- * run in flag order across calls on one stream, with the same arguments and
- * workspace; DKDV and DQ depend only on PREPARE, FINISH on DKDV.
- *   PREPARE: clears dsinks, then the row pass D = rowsum(dout * o),
- *            L = logaddexp(lse, s_h) and dsinks (the sink gradient of
- *            "GPT-OSS Agentic RL training: a practical retrospective",
- *            FlashAttention v3 implementation section); clears accumulators;
+ * run in flag order (PREPARE, DQ, DKDV, FINISH) across calls on one stream,
+ * with the same arguments and workspace; each depends on the one before.
+ * The row statistics D = rowsum(dout * o), L = logaddexp(lse, s_h) and the
+ * sink gradient dsinks (of "GPT-OSS Agentic RL training: a practical
+ * retrospective", FlashAttention v3 implementation section) are computed in
+ * PREPARE for fp32 and inside DQ for bf16.
+ *   PREPARE: clears dsinks (fp32: and runs the row pass);
+ *   DQ:      dQ, written to dq (bf16: also the row statistics, dsinks, and
+ *            clearing the fp32 dK/dV workspace accumulators);
  *   DKDV:    dK, dV from the recomputed probabilities exp(S - L) (bf16: into
- *            fp32 workspace accumulators; fp32: into dk, dv);
- *   DQ:      dQ, written to dq;
+ *            the fp32 workspace accumulators; fp32: into dk, dv);
  *   FINISH:  scales and converts the dK/dV accumulators into dk, dv (bf16;
  *            nothing to do for fp32).
  * sinkattn_bwd(...) == sinkattn_bwd_phases(SINKATTN_BWD_ALL, ...).
  */
 enum {
   SINKATTN_BWD_PREPARE = 1,
-  SINKATTN_BWD_DKDV = 2,
-  SINKATTN_BWD_DQ = 4,
+  SINKATTN_BWD_DQ = 2,
+  SINKATTN_BWD_DKDV = 4,
   SINKATTN_BWD_FINISH = 8,
   SINKATTN_BWD_ALL = 15
 };

@@ -24,8 +24,8 @@ SINKATTN_FP32 = 1
 
 # backward phase flags (sinkattn_bwd_phases)
 BWD_PREPARE = 1
-BWD_DKDV = 2
-BWD_DQ = 4
+BWD_DQ = 2
+BWD_DKDV = 4
 BWD_FINISH = 8
 BWD_ALL = 15
 
@@ -218,8 +218,8 @@ def sinkattn_bwd(q, k, v, sinks, o, lse, dout, window: int, prefix: int, softmax
 def sinkattn_bwd_phases(phases: int, q, k, v, sinks, o, lse, dout, window, prefix,
                         softmax_scale=None, cu_seqlens=None, max_seqlen=None, *, workspace,
                         grads):
-    """Run some phases of the backward (OR of BWD_PREPARE, BWD_DKDV, BWD_DQ,
-    BWD_FINISH); the workspace and grads must be the same across the calls
+    """Run some phases of the backward (OR of BWD_PREPARE, BWD_DQ, BWD_DKDV,
+    BWD_FINISH, run in that order); the workspace and grads must be the same across the calls
     that make up one backward."""
     return _bwd_call(int(phases), q, k, v, sinks, o, lse, dout, window, prefix, softmax_scale,
                      cu_seqlens, max_seqlen, workspace, grads)

@@ -22,10 +22,11 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                     int heads_kv, int window, int prefix, float scale,
                                     hipStream_t stream);
 hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
-                                  const float* l_ws, const float* d_ws, bf16* dq,
-                                  const int* cu_seqlens, int batch, int seqlen, int rows_total,
-                                  int heads_q, int heads_kv, int window, int prefix, float scale,
-                                  hipStream_t stream);
+                                  const bf16* o, const float* lse, const float* sinks,
+                                  float* dsinks, float* l_ws, float* d_ws, float* dk_acc,
+                                  float* dv_acc, bf16* dq, const int* cu_seqlens, int batch,
+                                  int seqlen, int rows_total, int heads_q, int heads_kv, int window,
+                                  int prefix, float scale, hipStream_t stream);
 hipError_t launch_fwd_f32(int head_dim, const float* q, const float* k, const float* v,
                           const float* sinks, float* o, float* lse, const int* cu_seqlens,
                           int batch, int seqlen, int total_tokens, int heads_q, int heads_kv,
@@ -45,6 +46,8 @@ hipError_t launch_convert(int dtype_is_f32, const float* dk_acc, const float* dv
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
 int fwd_key_tile(int window);
 int dkdv_query_tile(int window);
+bool dq_clears_dkdv_accumulators();
+hipError_t launch_zero_f32_vec(float* p, long long n, hipStream_t stream);
 
 namespace {
 
@@ -223,10 +226,25 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
   const int prefix = pb->prefix > pb->seqlen ? pb->seqlen : pb->prefix;
   const int rows = (int)dims.rows;
   const int lse_stride = dims.varlen ? rows : pb->seqlen;
-  if (phases & SINKATTN_BWD_PREPARE) {
-    e = launch_bwd_pre(is_f32, pb->head_dim, o, dout, lse, sinks, pb->cu_seqlens, dsinks, d_ws,
-                       l_ws, dk_acc, dv_acc, pb->batch, pb->seqlen, rows, pb->heads_q,
-                       pb->heads_kv, lse_stride, s);
+  // fp32: the row pass (D, L, dsinks) is its own kernel; bf16: the dQ kernel
+  // computes the row statistics of its rows, writes them for the dK/dV
+  // kernel and zeroes the dK/dV accumulators, so it runs first
+  if (is_f32 && (phases & SINKATTN_BWD_PREPARE)) {
+    e = launch_bwd_pre(1, pb->head_dim, o, dout, lse, sinks, pb->cu_seqlens, dsinks, d_ws, l_ws,
+                       nullptr, nullptr, pb->batch, pb->seqlen, rows, pb->heads_q, pb->heads_kv,
+                       lse_stride, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (!is_f32 && (phases & SINKATTN_BWD_PREPARE) && !dq_clears_dkdv_accumulators()) {
+    // the dK and dV accumulators fill the workspace from dk_off to its end
+    e = launch_zero_f32_vec(dk_acc, (long long)((wl.total - wl.dk_off) / sizeof(float)), s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (!is_f32 && (phases & SINKATTN_BWD_DQ)) {
+    e = launch_bwd_dq_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
+                               (const bf16*)o, lse, sinks, dsinks, l_ws, d_ws, dk_acc, dv_acc,
+                               (bf16*)dq, pb->cu_seqlens, pb->batch, pb->seqlen, rows,
+                               pb->heads_q, pb->heads_kv, window, prefix, pb->softmax_scale, s);
     if (e != hipSuccess) return hip_status(e);
   }
   if (is_f32 && (phases & (SINKATTN_BWD_DKDV | SINKATTN_BWD_DQ))) {
@@ -243,12 +261,6 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
                                  (const bf16*)dout, l_ws, d_ws, dk_acc, dv_acc, pb->cu_seqlens,
                                  pb->batch, pb->seqlen, rows, pb->heads_q, pb->heads_kv, window,
                                  prefix, pb->softmax_scale, s);
-    if (e != hipSuccess) return hip_status(e);
-  }
-  if (!is_f32 && (phases & SINKATTN_BWD_DQ)) {
-    e = launch_bwd_dq_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
-                               l_ws, d_ws, (bf16*)dq, pb->cu_seqlens, pb->batch, pb->seqlen, rows,
-                               pb->heads_q, pb->heads_kv, window, prefix, pb->softmax_scale, s);
     if (e != hipSuccess) return hip_status(e);
   }
   if ((phases & SINKATTN_BWD_FINISH) && !is_f32) {

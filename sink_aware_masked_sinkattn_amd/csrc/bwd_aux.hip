@@ -1,5 +1,7 @@
 // Backward helpers around the dK/dV and dQ kernels: the row preprocessing
-// pass and the dK/dV conversion pass.  Both are HBM-bound streaming kernels.
+// pass of the fp32 path (the bf16 dQ kernel computes the same statistics for
+// its own rows) and the dK/dV conversion pass.  Both are HBM-bound streaming
+// kernels.
 //
 // Preprocessing, per (row i, query head h) -- the sink gradient of "GPT-OSS
 // Agentic RL training: a practical retrospective" (FlashAttention v3
@@ -171,6 +173,13 @@ __global__ void sinkattn_zero_f32(float* p, int n) {
   if (i < n) p[i] = 0.0f;
 }
 
+// p[0, 4*n4) = 0, 16 bytes per store, grid-stride
+__global__ __launch_bounds__(256) void sinkattn_zero_f32x4(float4* p, long long n4) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 // fp32 dK / dV accumulators -> output dtype, with the softmax scale folded
 // into dK here (the dK/dV kernel accumulates dS^T Q unscaled).
 template <typename T>
@@ -204,6 +213,17 @@ hipError_t launch_zero_f32(float* p, int n, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Clears n floats at p (p 16-byte aligned, n a multiple of 4).
+hipError_t launch_zero_f32_vec(float* p, long long n, hipStream_t stream) {
+  const long long n4 = n / 4;
+  if (n4 <= 0) return hipSuccess;
+  long long blocks = (n4 + 255) / 256;
+  if (blocks > 256 * 8) blocks = 256 * 8;
+  hipLaunchKernelGGL(sinkattn_zero_f32x4, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (float4*)p, n4);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const void* dout,
                           const float* lse, const float* sinks, const int* cu_seqlens,
                           float* dsinks, float* d_ws, float* l_ws, float* dk_acc, float* dv_acc,
@@ -221,9 +241,7 @@ hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const v
     const int rows_per_pass = 256 / heads_q;
     const int passes = 4;
     dim3 grid((seqlen + rows_per_pass * passes - 1) / (rows_per_pass * passes), 1, batch);
-    if (!dtype_is_f32 && head_dim == 64) {
-      hipLaunchKernelGGL((sinkattn_bwd_pre_rows<bf16, 64>), grid, dim3(256), 0, stream, a, passes);
-    } else if (dtype_is_f32 && head_dim == 64) {
+    if (dtype_is_f32 && head_dim == 64) {
       hipLaunchKernelGGL((sinkattn_bwd_pre_rows<float, 64>), grid, dim3(256), 0, stream, a, passes);
     } else if (dtype_is_f32 && head_dim == 32) {
       hipLaunchKernelGGL((sinkattn_bwd_pre_rows<float, 32>), grid, dim3(256), 0, stream, a, passes);
@@ -234,9 +252,7 @@ hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const v
   }
   a.rows_per_wave = 256;
   dim3 grid((seqlen + a.rows_per_wave - 1) / a.rows_per_wave, (heads_q + 3) / 4, batch);
-  if (!dtype_is_f32 && head_dim == 64) {
-    hipLaunchKernelGGL((sinkattn_bwd_pre<bf16, 64>), grid, dim3(256), 0, stream, a);
-  } else if (dtype_is_f32 && head_dim == 64) {
+  if (dtype_is_f32 && head_dim == 64) {
     hipLaunchKernelGGL((sinkattn_bwd_pre<float, 64>), grid, dim3(256), 0, stream, a);
   } else if (dtype_is_f32 && head_dim == 32) {
     hipLaunchKernelGGL((sinkattn_bwd_pre<float, 32>), grid, dim3(256), 0, stream, a);

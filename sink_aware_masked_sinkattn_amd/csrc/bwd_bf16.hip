@@ -1,7 +1,7 @@
 // dK and dV of sink-aware masked attention, bf16, head dim 64, gfx950 MFMA.
 //
-// With the preprocessing pass's L_i = logaddexp(l_i, s_h) and
-// D_i = rowsum(dO * O), for the visible pairs of the mask
+// With L_i = logaddexp(l_i, s_h) and D_i = rowsum(dO * O) from the dQ
+// kernel (which runs first), for the visible pairs of the mask
 // M[q,k] = 1[k<=q] AND 1[q-k<=w OR k<p] ("Efficient Reinforcement Learning
 // for Long-Horizon Tool-Use Agentic Tasks", summary page; the zero-value
 // sink of arXiv 2608.10357 section 5 only enters through L and D):
@@ -53,7 +53,7 @@ struct DkvArgs {
   const bf16* k;
   const bf16* v;
   const bf16* dout;
-  const float* l_ws;      // [Hq, rows] L (natural log)
+  const float* l2_ws;     // [Hq, rows] L in log2 units (written by the dQ kernel)
   const float* d_ws;      // [Hq, rows] D
   float* dk_acc;          // [rows, Hkv, D] sum dS^T Q (unscaled)
   float* dv_acc;          // [rows, Hkv, D] sum P'^T dO
@@ -291,7 +291,7 @@ __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
     if (tid < 2 * BQ) {
       const int r = q0 + (tid & (BQ - 1));
       const size_t wi = (size_t)h * a.rows_total + sv.row_base + r;
-      if (tid < BQ) lreg = (r < sv.len) ? a.l_ws[wi] * SA_LOG2E : INFINITY;
+      if (tid < BQ) lreg = (r < sv.len) ? a.l2_ws[wi] : INFINITY;
       else lreg = (r < sv.len) ? a.d_ws[wi] : 0.0f;
     }
   };
@@ -387,7 +387,7 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                     int heads_kv, int window, int prefix, float scale,
                                     hipStream_t stream) {
   DkvArgs a;
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.l_ws = l_ws; a.d_ws = d_ws;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.l2_ws = l_ws; a.d_ws = d_ws;
   a.dk_acc = dk_acc; a.dv_acc = dv_acc; a.cu_seqlens = cu_seqlens;
   a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
   a.group = heads_q / heads_kv; a.window = window; a.prefix = prefix;

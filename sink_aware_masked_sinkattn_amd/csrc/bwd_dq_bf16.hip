@@ -47,16 +47,27 @@ struct DqTiles {
   static_assert(SMEM_ELEMS >= 4 * TILE_ELEMS && SMEM_ELEMS >= STAGE_ELEMS, "LDS sizing");
 };
 
+#ifndef SA_DQ_ZERO_ACC
+#define SA_DQ_ZERO_ACC 1   // the dQ kernel clears the dK/dV accumulators
+#endif
+
 struct DqArgs {
   const bf16* q;
   const bf16* k;
   const bf16* v;
   const bf16* dout;
-  const float* l_ws;      // [Hq, rows] natural-log L
-  const float* d_ws;      // [Hq, rows] D
+  const bf16* o;
+  const float* lse;       // forward log-sum-exp (natural log, content keys only)
+  const float* sinks;
+  float* dsinks;          // accumulated into (cleared beforehand)
+  float* l2_ws;           // [Hq, rows] L in log2 units (L * log2 e), written here
+  float* d_ws;            // [Hq, rows] D, written here
+  float* dk_acc;          // [rows, Hkv, D] fp32 dK / dV accumulators, zeroed here
+  float* dv_acc;
   bf16* dq;
   const int* cu_seqlens;
   int seqlen, heads_q, heads_kv, group, window, prefix, rows_total, num_q_tiles;
+  int lse_head_stride;    // T (fixed length) or N (packed)
   float scale_log2;
   float scale;
 };
@@ -166,24 +177,6 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   const bf16* kbase = a.k + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
   const bf16* vbase = a.v + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
 
-  // Q, dO fragments (B operands), per-lane L (log2 domain) and D
-  bf16x8 qf[QB][4], df[QB][4];
-  float l2[QB], dd[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + qb * 32 + l32;
-    const bool ok = row < sv.len;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const size_t off = qoff + (size_t)row * q_row_stride + 16 * s + 8 * g;
-      qf[qb][s] = ok ? *(const bf16x8*)(a.q + off) : bf16x8{};
-      df[qb][s] = ok ? *(const bf16x8*)(a.dout + off) : bf16x8{};
-    }
-    const size_t wi = (size_t)h * a.rows_total + sv.row_base + row;
-    l2[qb] = ok ? a.l_ws[wi] * SA_LOG2E : INFINITY;
-    dd[qb] = ok ? a.d_ws[wi] : 0.0f;
-  }
-
   int seg[4];
   const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, BK, seg);
   const int n0 = seg[1] - seg[0];
@@ -199,11 +192,49 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
                              kv_row_stride, sv.len - r0, wave, lane);
   };
 
+  // the first K/V tile load goes out before the row loads below
+  load_tile(0, 0);
+
+  // Q, dO fragments (B operands) and the row statistics of the backward for
+  // this wave's rows -- the sink gradient of "GPT-OSS Agentic RL training: a
+  // practical retrospective" (FlashAttention v3 implementation section),
+  // with the sink as a zero-value key (arXiv 2608.10357, section 5):
+  //   D = rowsum(dO * O),  L = logaddexp(l, s_h),  ds_h -= exp(s_h - L) D.
+  // O is read in the layout of the dO fragment (this lane: half of the row's
+  // head dim), so D is a register dot product plus one half-wave swap.  D and
+  // L (log2 units) go to the workspace for the dK/dV kernel, which runs after
+  // this one; those stores wait for the epilogue, so that the loads here
+  // overlap with the first K/V tile load.
+  bf16x8 qf[QB][4], df[QB][4];
+  float l2[QB], dd[QB];
+  const float sink = a.sinks[h];
+  float ds_part = 0.0f;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + qb * 32 + l32;
+    const bool ok = row < sv.len;
+    float dot = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const size_t off = qoff + (size_t)row * q_row_stride + 16 * s + 8 * g;
+      qf[qb][s] = ok ? *(const bf16x8*)(a.q + off) : bf16x8{};
+      df[qb][s] = ok ? *(const bf16x8*)(a.dout + off) : bf16x8{};
+      const bf16x8 of = ok ? *(const bf16x8*)(a.o + off) : bf16x8{};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dot += (float)of[j] * (float)df[qb][s][j];
+    }
+    dot = halves_sum(dot);
+    const float l = ok ? a.lse[sv.lse_base + (size_t)h * a.lse_head_stride + row] : 0.0f;
+    const float big_l = (sink == -INFINITY) ? l : fmaxf(l, sink) + log1pf(expf(-fabsf(l - sink)));
+    l2[qb] = ok ? big_l * SA_LOG2E : INFINITY;
+    dd[qb] = ok ? dot : 0.0f;
+    if (ok && g == 0) ds_part -= expf(sink - big_l) * dot;
+  }
+
   f32x16 acc[QB][2];   // dQ: C layout [m = query][n = d], lane = d
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) acc[qb][0] = acc[qb][1] = f32x16{};
 
-  load_tile(0, 0);
   wait_all_mem();
   __syncthreads();
 
@@ -250,6 +281,32 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
       if (qrow < sv.len) *(uint4*)(obase + (size_t)qrow * q_row_stride + c) = *(const uint4*)(os + r * OROW + c);
     }
   }
+  // row statistics for the dK/dV kernel, and this wave's share of ds_h
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + qb * 32 + l32;
+    if (row < sv.len && g == 0) {
+      const size_t wi = (size_t)h * a.rows_total + sv.row_base + row;
+      a.d_ws[wi] = dd[qb];
+      a.l2_ws[wi] = l2[qb];
+    }
+  }
+#pragma unroll
+  for (int w = 1; w < 64; w <<= 1) ds_part += __shfl_xor(ds_part, w);
+  if (lane == 0 && wave_active) unsafeAtomicAdd(a.dsinks + h, ds_part);
+  // Zero this workgroup's share of the fp32 dK / dV accumulators (the dK/dV
+  // kernel adds into them): rows of the tile congruent to h mod group, so the
+  // group's query heads split the kv head's rows between them.
+  if (SA_DQ_ZERO_ACC) {
+    const int part = h - kvh * a.group;
+    const int n_mine = (q_last - q_start + a.group - part) / a.group;   // rows part, part+group, ...
+    for (int i = tid; i < n_mine * (D / 4); i += WAVES * 64) {
+      const int r = q_start + part + a.group * (i / (D / 4));
+      const size_t e = ((size_t)(sv.row_base + r) * a.heads_kv + kvh) * D + 4 * (i % (D / 4));
+      *(float4*)(a.dk_acc + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+      *(float4*)(a.dv_acc + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
 }
 
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_DQ_OCC, SA_DQ_OCC))) void sinkattn_bwd_dq_bf16_d64(DqArgs a) {
@@ -263,13 +320,21 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_D
 
 int fwd_key_tile(int window);
 
+// Whether the dQ kernel clears the fp32 dK/dV accumulators (else the caller
+// must before the dK/dV kernel runs).
+bool dq_clears_dkdv_accumulators() { return SA_DQ_ZERO_ACC != 0; }
+
 hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
-                                  const float* l_ws, const float* d_ws, bf16* dq,
-                                  const int* cu_seqlens, int batch, int seqlen, int rows_total,
-                                  int heads_q, int heads_kv, int window, int prefix, float scale,
-                                  hipStream_t stream) {
+                                  const bf16* o, const float* lse, const float* sinks,
+                                  float* dsinks, float* l_ws, float* d_ws, float* dk_acc,
+                                  float* dv_acc, bf16* dq, const int* cu_seqlens, int batch,
+                                  int seqlen, int rows_total, int heads_q, int heads_kv, int window,
+                                  int prefix, float scale, hipStream_t stream) {
   DqArgs a;
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.l_ws = l_ws; a.d_ws = d_ws; a.dq = dq;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.o = o; a.lse = lse; a.sinks = sinks;
+  a.dsinks = dsinks; a.l2_ws = l_ws; a.d_ws = d_ws; a.dk_acc = dk_acc; a.dv_acc = dv_acc;
+  a.dq = dq;
+  a.lse_head_stride = cu_seqlens ? rows_total : seqlen;
   a.cu_seqlens = cu_seqlens;
   a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
   a.group = heads_q / heads_kv; a.window = window; a.prefix = prefix;

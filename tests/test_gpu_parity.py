@@ -235,7 +235,7 @@ def test_bwd_phases_equal_single_call(dtype, d):
     ref = sinkattn_bwd(q, k, v, s, o, lse, do, inp.window, inp.prefix, inp.scale)
     grads = tuple(torch.full_like(t, float("nan")) for t in ref)
     ws = torch.full((1 << 26,), 255, dtype=torch.uint8, device=dev)
-    for ph in (BWD_PREPARE, BWD_DKDV, BWD_DQ, BWD_FINISH):
+    for ph in (BWD_PREPARE, BWD_DQ, BWD_DKDV, BWD_FINISH):
         sinkattn_bwd_phases(ph, q, k, v, s, o, lse, do, inp.window, inp.prefix, inp.scale,
                             workspace=ws, grads=grads)
     torch.cuda.synchronize()
