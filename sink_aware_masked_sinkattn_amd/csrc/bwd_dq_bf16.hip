@@ -6,13 +6,14 @@
 //   P'_ij = exp(S_ij - L_i),  S_ij = scale q_i . k_j,  L_i = logaddexp(l_i, s_h)
 //   dS_ij = P'_ij (dO_i . v_j - D_i),    dQ_i = scale sum_j dS_ij k_j
 // (the zero-value sink key of arXiv 2608.10357 section 5 enters only through
-// L and D).  Query-stationary, like the forward: each workgroup owns 256
-// query rows of one head and walks the same key-tile list (prefix tiles +
-// window tiles), so dQ accumulates in registers and is written once, with
-// no atomics -- at the price of recomputing S and dP^T here (the dK/dV
-// kernel recomputes them too).
+// L and D).  Query-stationary, like the forward: each workgroup owns the
+// query rows of its waves (4 waves x QB blocks of 32 rows: 64 rows per wave
+// with 64-key tiles, 32 rows with the 32-key tiles of short windows) of one
+// head and walks the same key-tile list (prefix tiles + window tiles), so dQ
+// accumulates in registers and is written once, with no atomics -- at the
+// price of recomputing S and dP^T here (the dK/dV kernel recomputes them too).
 //
-// Layout per wave (64 query rows = two 32-row MFMA blocks):
+// Layout per wave (QB 32-row MFMA blocks):
 //   S^T = K Q^T and dP^T = V dO^T with one query per lane (C layout); Q and
 //   dO fragments stay in registers as the B operand; K and V tiles come
 //   from LDS as the A operand.  L and D are then per-lane scalars.  The C
@@ -26,21 +27,23 @@ namespace {
 
 constexpr int D = 64;
 #ifndef SA_DQ_QB
-#define SA_DQ_QB 2
+#define SA_DQ_QB 2      // 32-row query blocks per wave, 64-key-tile instance
+#endif
+#ifndef SA_DQ_QB_K32
+#define SA_DQ_QB_K32 1  // the same for the 32-key-tile (short window) instance
 #endif
 #ifndef SA_DQ_WAVES
 #define SA_DQ_WAVES 4
 #endif
-constexpr int QB = SA_DQ_QB;          // 32-row query blocks per wave
 constexpr int WAVES = SA_DQ_WAVES;    // waves per workgroup
-constexpr int BQ = WAVES * QB * 32;   // query rows per workgroup
 constexpr int OROW = D + 8;            // padded row of the epilogue staging buffer
-constexpr int STAGE_ELEMS = WAVES * QB * 32 * OROW;
 // Key tiles of NKB blocks of 32 keys (64 in general, 32 for short windows).
 // LDS: two K/V tile pairs during the key loop; afterwards the same memory
 // stages each wave's output rows (padded) for row-contiguous stores.
-template <int NKB>
+template <int NKB, int QB>
 struct DqTiles {
+  static constexpr int BQ = WAVES * QB * 32;   // query rows per workgroup
+  static constexpr int STAGE_ELEMS = WAVES * QB * 32 * OROW;
   static constexpr int BK = 32 * NKB;
   static constexpr int TILE_ELEMS = BK * D;   // swizzled rows (tile_off)
   static constexpr int SMEM_ELEMS = (4 * TILE_ELEMS > STAGE_ELEMS) ? 4 * TILE_ELEMS : STAGE_ELEMS;
@@ -79,7 +82,7 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
 
 // One key tile (NKB blocks of 32 keys) against this wave's QB blocks of 32
 // query rows.  MASK: apply the element predicate (partial tiles only).
-template <int NKB, bool MASK>
+template <int NKB, int QB, bool MASK>
 __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const bf16x8 (&qf)[QB][4],
                                           const bf16x8 (&df)[QB][4], const float (&l2)[QB],
                                           const float (&dd)[QB], f32x16 (&acc)[QB][2], int qw0,
@@ -144,9 +147,10 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
 #ifndef SA_DQ_OCC
 #define SA_DQ_OCC 2   // waves per SIMD the register budget is set for
 #endif
-template <int NKB>
+template <int NKB, int QB>
 __device__ __forceinline__ void dq_body(const DqArgs& a) {
-  using T = DqTiles<NKB>;
+  using T = DqTiles<NKB, QB>;
+  constexpr int BQ = T::BQ;
   constexpr int BK = T::BK;
   constexpr int TILE_ELEMS = T::TILE_ELEMS;
   __shared__ __attribute__((aligned(16))) bf16 smem[T::SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
@@ -248,9 +252,9 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
     const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
     const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
     if (cls == SA_TILE_FULL) {
-      tile_step<NKB, false>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, QB, false>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     } else if (cls == SA_TILE_PARTIAL) {
-      tile_step<NKB, true>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, QB, true>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     }
     wait_all_mem();
     __syncthreads();
@@ -310,10 +314,15 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
 }
 
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_DQ_OCC, SA_DQ_OCC))) void sinkattn_bwd_dq_bf16_d64(DqArgs a) {
-  dq_body<2>(a);
+  dq_body<2, SA_DQ_QB>(a);
 }
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_DQ_OCC, SA_DQ_OCC))) void sinkattn_bwd_dq_bf16_d64_k32(DqArgs a) {
-  dq_body<1>(a);
+// short windows: 32-key tiles and (by default) 32 rows per wave at 3 waves
+// per SIMD -- a 64-row wave would span w + 64 keys of which fewer are visible
+#ifndef SA_DQ_OCC_K32
+#define SA_DQ_OCC_K32 3
+#endif
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_DQ_OCC_K32, SA_DQ_OCC_K32))) void sinkattn_bwd_dq_bf16_d64_k32(DqArgs a) {
+  dq_body<1, SA_DQ_QB_K32>(a);
 }
 
 }  // namespace
@@ -339,12 +348,14 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
   a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
   a.group = heads_q / heads_kv; a.window = window; a.prefix = prefix;
   a.rows_total = rows_total;
+  const bool k32 = fwd_key_tile(window) == 32;
+  const int BQ = k32 ? DqTiles<1, SA_DQ_QB_K32>::BQ : DqTiles<2, SA_DQ_QB>::BQ;
   a.num_q_tiles = (seqlen + BQ - 1) / BQ;
   a.scale_log2 = scale * SA_LOG2E;
   a.scale = scale;
   if (a.num_q_tiles == 0 || batch == 0) return hipSuccess;
   dim3 grid(heads_q, batch, a.num_q_tiles);
-  if (fwd_key_tile(window) == 32)
+  if (k32)
     hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64_k32, grid, dim3(WAVES * 64), 0, stream, a);
   else
     hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64, grid, dim3(WAVES * 64), 0, stream, a);
