@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
 and the CPU-baseline leg of ``bench.py``; never by the library.
 """
-from .sinkattn_ref import (attend_head, attend_head_grad, backward, forward,
+from .sinkattn_ref import (attend_head, attend_head_grad, backward, decode, forward,
                            visible_mask)
 
-__all__ = ["visible_mask", "attend_head", "attend_head_grad", "forward", "backward"]
+__all__ = ["visible_mask", "attend_head", "attend_head_grad", "forward", "backward", "decode"]

@@ -30,6 +30,15 @@ fine here).  Readings where the pages leave a step open:
     packed sequence; the q-head h reads kv-head h // group;
   * one fp32 sink logit per query head, shared by all rows and sequences.
 
+Decode (the rollout side of the same attention; arXiv 2608.10357 section 4
+"Rollout workers": sampling from the current policy; [RETRO], section on the
+training-inference mismatch through attention sinks: the rollout engine must
+give the trainer's token probabilities, sink included): one new query token
+per sequence against its key/value cache of n tokens, the new token's own
+key and value already at position n - 1.  The plain reading is that the
+query sits at position n - 1 under the same mask, so the result is row
+n - 1 of the forward on the whole sequence.
+
 Backward (not printed on the pages; it is the chain rule through [S5]'s
 softmax with one extra zero-valued column of logit s):
   L_i   = logaddexp(l_i, s)           (log of the sink-inclusive normaliser)
@@ -198,3 +207,45 @@ def backward(q, k, v, sinks, do, window: int, prefix: int, scale: float,
                 dv[rows, kv, :] += g_v
             dsinks[h] += g_s
     return dq, dk, dv, dsinks
+
+
+def decode(q, k_cache, v_cache, cache_seqlens, sinks, window: int, prefix: int,
+           scale: float):
+    """Decode: one query token per sequence against its key/value cache.
+
+    q [B, Hq, d]; k_cache, v_cache [B, Tmax, Hkv, d]; cache_seqlens ints [B]
+    (n_b cached tokens, the new token's key and value at position n_b - 1).
+    The query at position n_b - 1 sees key j iff j <= n_b - 1 and
+    (n_b - 1 - j <= w or j < p) ([SUM] mask) and gets
+    o = sigmoid(l - s_h) * softmax(S) v with l the content-only log-sum-exp
+    ([SUM]).  Returns (o [B, Hq, d], lse [B, Hq]), fp64.  A sequence with
+    n_b = 0 has no keys: o = 0, lse = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_cache = np.asarray(k_cache, dtype=np.float64)
+    v_cache = np.asarray(v_cache, dtype=np.float64)
+    sinks = np.asarray(sinks, dtype=np.float64)
+    bsz, hq, d = q.shape
+    group = hq // k_cache.shape[2]
+    o = np.zeros((bsz, hq, d), np.float64)
+    lse = np.full((bsz, hq), -np.inf, np.float64)
+    for b in range(bsz):
+        n = int(cache_seqlens[b])
+        if n == 0:
+            continue
+        pos = n - 1
+        j = np.arange(n)
+        vis = (j <= pos) & ((pos - j <= window) | (j < prefix))
+        for h in range(hq):
+            kh = k_cache[b, :n, h // group, :]
+            vh = v_cache[b, :n, h // group, :]
+            sc = np.where(vis, scale * (kh @ q[b, h]), -np.inf)
+            mx = sc.max()
+            e = np.exp(sc - mx)
+            z = e.sum()
+            l = mx + np.log(z)
+            alpha = 1.0 / (1.0 + np.exp(sinks[h] - l))      # sigmoid(l - s)
+            o[b, h] = alpha * (e @ vh) / z
+            lse[b, h] = l
+    return o, lse
+

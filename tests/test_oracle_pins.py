@@ -330,3 +330,93 @@ def test_infinite_negative_sink_gives_zero_sink_gradient():
     dq, dk, dv, ds = oracle.backward(q, k, v, s, do, 2, 1, inp.scale)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(dq)) and np.all(np.isfinite(dk))
     assert ds[0] == 0.0 and ds[1] != 0.0
+
+
+# ------------------------------------------------------------------- decode
+
+def _decode_case(seed, lens, tmax, hq, hkv, d):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(len(lens), hq, d, generator=g, dtype=torch.float64)
+    k = torch.randn(len(lens), tmax, hkv, d, generator=g, dtype=torch.float64)
+    v = torch.randn(len(lens), tmax, hkv, d, generator=g, dtype=torch.float64)
+    s = torch.randn(hq, generator=g, dtype=torch.float64)
+    return q.numpy(), k.numpy(), v.numpy(), s.numpy()
+
+
+@pytest.mark.parametrize("w,p", [(WINDOW_INF, 0), (5, 0), (3, 2), (0, 0), (0, 4), (100, 100)])
+def test_decode_equals_explicit_sink_row(w, p):
+    # independent explicit-sink softmax over the visible keys of the last
+    # position, built from index ranges (not the predicate)
+    lens, tmax, hq, hkv, d = [1, 2, 9, 17], 20, 4, 2, 8
+    q, k, v, s = _decode_case(11, lens, tmax, hq, hkv, d)
+    scale = 0.3
+    o, l = oracle.decode(q, k, v, lens, s, w, p, scale)
+    for b, n in enumerate(lens):
+        pos = n - 1
+        keys = sorted(set(range(max(0, pos - min(w, n)), pos + 1)) | set(range(min(p, n))))
+        for h in range(hq):
+            kv = h // (hq // hkv)
+            logits = np.array([scale * q[b, h] @ k[b, j, kv] for j in keys] + [s[h]])
+            wts = np.exp(logits - logits.max())
+            wts /= wts.sum()
+            vals = np.vstack([v[b, keys, kv], np.zeros((1, d))])
+            assert np.allclose(o[b, h], wts @ vals, atol=1e-12)
+            content = logits[:-1]
+            assert abs(l[b, h] - (content.max() + np.log(np.exp(content - content.max()).sum()))) < 1e-12
+
+
+def test_decode_is_last_row_of_forward():
+    # the rollout engine must reproduce the trainer's probabilities: decode on
+    # a cache of n tokens equals row n - 1 of the forward on those n tokens
+    for w, p in [(WINDOW_INF, 0), (6, 3), (2, 0)]:
+        lens, hq, hkv, d = [1, 5, 12], 8, 2, 8
+        q, k, v, s = _decode_case(12, lens, 12, hq, hkv, d)
+        # training-side queries: the decode query is the last row, the others random
+        qt = np.random.default_rng(3).standard_normal((len(lens), 12, hq, d))
+        for b, n in enumerate(lens):
+            qt[b, n - 1] = q[b]
+        od, ld = oracle.decode(q, k, v, lens, s, w, p, 0.25)
+        for b, n in enumerate(lens):
+            of, lf = oracle.forward(qt[b:b + 1, :n], k[b:b + 1, :n], v[b:b + 1, :n], s, w, p, 0.25)
+            assert np.allclose(od[b], of[0, n - 1], atol=1e-12)
+            assert np.allclose(ld[b], lf[0, :, n - 1], atol=1e-12)
+
+
+@pytest.mark.parametrize("w,p", [(WINDOW_INF, 0), (4, 2)])
+def test_decode_infinite_negative_sink_reduces_to_sdpa(w, p):
+    lens, tmax, hq, hkv, d = [3, 10, 16], 16, 4, 4, 8
+    q, k, v, s = _decode_case(13, lens, tmax, hq, hkv, d)
+    s[:] = -np.inf
+    o, _ = oracle.decode(q, k, v, lens, s, w, p, 1.0 / math.sqrt(d))
+    for b, n in enumerate(lens):
+        mask = torch.zeros(1, n, dtype=torch.bool)
+        mask[0, max(0, n - 1 - min(w, n)):n] = True
+        mask[0, :min(p, n)] = True
+        for h in range(hq):
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q[b, h][None, None]), torch.from_numpy(k[b, :n, h][None].copy()),
+                torch.from_numpy(v[b, :n, h][None].copy()), attn_mask=mask[None])
+            assert np.allclose(o[b, h], ref[0, 0].numpy(), atol=1e-12)
+
+
+def test_decode_closed_forms():
+    lens, tmax, hq, hkv, d = [1, 7, 0], 8, 2, 1, 4
+    q, k, v, s = _decode_case(14, lens, tmax, hq, hkv, d)
+    # w = 0, p = 0: only the new token's own key is visible
+    o, l = oracle.decode(q, k, v, lens, s, 0, 0, 0.5)
+    for b, n in enumerate(lens[:2]):
+        for h in range(hq):
+            lh = 0.5 * q[b, h] @ k[b, n - 1, 0]
+            assert abs(l[b, h] - lh) < 1e-12
+            assert np.allclose(o[b, h], v[b, n - 1, 0] / (1.0 + np.exp(s[h] - lh)), atol=1e-12)
+    # an empty cache: no keys, o = 0 and lse = -inf
+    assert np.all(o[2] == 0) and np.all(np.isneginf(l[2]))
+    # uniform keys: l = scale q.k + ln(count), o = alpha * mean of the visible values
+    k[:] = k[:, :1]
+    o, l = oracle.decode(q, k, v, lens, s, 2, 1, 0.5)
+    n = 7
+    keys = [0, 4, 5, 6]
+    for h in range(hq):
+        lh = 0.5 * q[1, h] @ k[1, 0, 0] + math.log(len(keys))
+        assert abs(l[1, h] - lh) < 1e-12
+        assert np.allclose(o[1, h], v[1, keys, 0].mean(axis=0) / (1.0 + np.exp(s[h] - lh)), atol=1e-12)
