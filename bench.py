@@ -15,6 +15,8 @@ with HIP events on the library's stream), peak device memory, and the fp64
 oracle timed on a bounded sample on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --workload decode_grpo_32   (rollout decode: its own JSON line,
+                                                     effective HBM GB/s)
 """
 from __future__ import annotations
 
@@ -140,6 +142,150 @@ def cpu_baseline(layers, head_dim: int):
             "seconds": round(dt, 3)}
 
 
+DECODE_METRIC = "sink-attn decode: effective HBM GB/s of the visible K/V cache rows"
+
+
+def decode_visible(n: int, window: int, prefix: int) -> int:
+    """Keys the query at position n - 1 sees in a cache of n tokens."""
+    if n <= 0:
+        return 0
+    return min(n, min(window, n - 1) + 1 + min(prefix, max(0, n - 1 - min(window, n - 1))))
+
+
+def decode_cpu_baseline(layers, min_seconds: float = 10.0):
+    """The fp64 oracle's decode over the whole workload (every sequence, both
+    layers; inputs converted to fp64 beforehand), repeated until about
+    `min_seconds` of CPU time."""
+    import torch
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    prepared, step_bytes = [], 0
+    for inp in layers:
+        lens = inp.cache_seqlens.tolist()
+        cap = max(lens)
+        prepared.append((inp.q.to(torch.float64).numpy(),
+                         inp.k_cache[:, :cap].to(torch.float64).numpy(),
+                         inp.v_cache[:, :cap].to(torch.float64).numpy(), lens,
+                         inp.sinks.to(torch.float64).numpy(), inp))
+        hkv, d = inp.k_cache.shape[2], inp.k_cache.shape[3]
+        step_bytes += sum(decode_visible(n, inp.window, inp.prefix) for n in lens) * hkv * d * 4
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        for q, k, v, lens, s, inp in prepared:
+            oracle.decode(q, k, v, lens, s, inp.window, inp.prefix, inp.scale)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": step_bytes * reps / dt / 1e9, "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"the whole workload (all sequences, both layers), fp64 decode, "
+                      f"{reps} repetitions in {dt:.1f} s; GB/s of visible K/V rows",
+            "seconds": round(dt, 3)}
+
+
+def run_decode(args) -> int:
+    """One step = one decode call per layer of a decode workload (one new token
+    for every sequence of the batch); inputs resident, outputs and workspace
+    preallocated.  value = compulsory bytes (visible K/V rows, q, o, lse) of
+    the step / step time."""
+    import torch
+
+    from sink_aware_masked_sinkattn_amd import (load_library, make_decode_problem,
+                                                sinkattn_decode,
+                                                sinkattn_decode_workspace_size)
+    from workloads import DECODE_WORKLOADS, decode_workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    load_library()
+    wl = DECODE_WORKLOADS[args.workload]
+    layers = decode_workload_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    runs = []
+    for inp in layers:
+        r = {"inp": inp, "q": inp.q.to(dev), "k": inp.k_cache.to(dev), "v": inp.v_cache.to(dev),
+             "lens": inp.cache_seqlens.to(dev), "s": inp.sinks.to(dev)}
+        r["o"] = torch.empty_like(r["q"])
+        r["lse"] = torch.empty(r["q"].shape[:2], dtype=torch.float32, device=dev)
+        pb = make_decode_problem(r["q"], r["k"], inp.window, inp.prefix, inp.scale)
+        r["ws"] = torch.empty(max(1, sinkattn_decode_workspace_size(pb)), dtype=torch.uint8,
+                              device=dev)
+        vis = sum(decode_visible(n, inp.window, inp.prefix) for n in inp.cache_seqlens.tolist())
+        hq, d = inp.q.shape[1], inp.q.shape[2]
+        hkv = inp.k_cache.shape[2]
+        r["bytes"] = vis * hkv * d * 2 * 2 + 2 * inp.q.numel() * 2 + inp.q.shape[0] * hq * 4
+        r["flops"] = 4 * d * hq * vis
+        runs.append(r)
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        for li, r in enumerate(runs):
+            inp = r["inp"]
+            if events:
+                events[li][0].record()
+            sinkattn_decode(r["q"], r["k"], r["v"], r["lens"], r["s"], inp.window, inp.prefix,
+                            inp.scale, out=r["o"], lse=r["lse"], workspace=r["ws"])
+            if events:
+                events[li][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in runs]
+              for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+    per_layer = []
+    for li, r in enumerate(runs):
+        ms = sum(events[i][li][0].elapsed_time(events[i][li][1]) for i in range(K)) / K
+        per_layer.append({"window": r["inp"].window if r["inp"].window < WINDOW_INF else "inf",
+                          "prefix": r["inp"].prefix, "ms": round(ms, 5),
+                          "bytes": r["bytes"], "gbs": round(r["bytes"] / (ms * 1e-3) / 1e9, 1),
+                          "tflops": round(r["flops"] / (ms * 1e-3) / 1e12, 3)})
+    total_bytes = sum(r["bytes"] for r in runs)
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    dom = max(range(len(runs)), key=lambda i: per_layer[i]["ms"])
+    achieved = runs[dom]["bytes"] / (per_layer[dom]["ms"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "sinkattn_decode_split_bf16_d64 + sinkattn_decode_combine_bf16_d64 "
+                          f"(one sinkattn_decode call, layer {dom})",
+                "avg_launch_ms": per_layer[dom]["ms"],
+                "algorithmic_bytes_per_launch": runs[dom]["bytes"]}
+    cpu = None if args.no_cpu_baseline else decode_cpu_baseline(layers)
+    out = {
+        "metric": DECODE_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": wl.batch, "cache_capacity": wl.capacity,
+                   "cache_lengths": list(wl.lengths), "heads_q": wl.heads_q,
+                   "heads_kv": wl.heads_kv, "head_dim": wl.head_dim,
+                   "layers": [{"window": w if w < WINDOW_INF else "inf", "prefix": p}
+                              for (w, p) in wl.layers],
+                   "parallelism": "single GPU"},
+        "per_layer": per_layer,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +304,10 @@ def main(argv=None):
               "the sink-attention path here is a single-GPU kernel library; multi-GPU sharding "
               "is described in the design notes but not built.", file=sys.stderr)
         return 2
+
+    from workloads import DECODE_WORKLOADS
+    if args.workload in DECODE_WORKLOADS:
+        return run_decode(args)
 
     import torch
 

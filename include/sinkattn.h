@@ -187,6 +187,49 @@ int32_t sinkattn_key_tile_segments(int32_t q0, int32_t q1, int32_t window,
  */
 sinkattn_status sinkattn_tile_config(const sinkattn_problem *problem, int32_t *out);
 
+/*
+ * Decode: one new query token per sequence against its key/value cache -- the
+ * rollout side of the same attention.  The rollout workers sample from the
+ * current policy (arXiv 2608.10357, section 4 "Rollout workers"), and the
+ * rollout engine must give the trainer's token probabilities, sink included
+ * ("GPT-OSS Agentic RL training: a practical retrospective", section on the
+ * training-inference mismatch through attention sinks).  For sequence b with
+ * n = cache_seqlens[b] cached tokens (the new token's key and value already
+ * written at position n - 1) the query sits at position n - 1 under the same
+ * mask M[q,k] = 1[k<=q] AND 1[q-k<=w OR k<p] and sink scaling as sinkattn_fwd:
+ * the result equals row n - 1 of sinkattn_fwd on those n tokens (up to bf16
+ * rounding of the output).  n = 0 gives o = 0 and lse = -inf; n is clamped to
+ * [0, cache_capacity].
+ *
+ * Layouts (bf16, head_dim 64, contiguous): q and o [batch, heads_q, 64];
+ * k_cache and v_cache [batch, cache_capacity, heads_kv, 64];
+ * cache_seqlens int32 [batch] (device); sinks fp32 [heads_q];
+ * lse fp32 [batch, heads_q] (content-only log-sum-exp, natural log; may be
+ * NULL).  heads_q / heads_kv must be at most 16.  The workspace (caller-owned
+ * device memory of sinkattn_decode_workspace_size bytes, 256-byte aligned)
+ * holds the per-split partial results; its contents on entry do not matter.
+ * Validation happens on the host before any HIP call, as for sinkattn_fwd.
+ */
+typedef struct {
+  int32_t batch;            /* sequences, one new query token each */
+  int32_t cache_capacity;   /* rows per sequence in k_cache / v_cache */
+  int32_t heads_q;
+  int32_t heads_kv;         /* heads_q / heads_kv <= 16 */
+  int32_t head_dim;         /* 64 */
+  int32_t window;           /* w >= 0; SINKATTN_WINDOW_INF for plain causal */
+  int32_t prefix;           /* p >= 0 */
+  float softmax_scale;
+} sinkattn_decode_problem;
+
+/* Bytes of device workspace sinkattn_decode needs (0 if the problem is invalid). */
+size_t sinkattn_decode_workspace_size(const sinkattn_decode_problem *problem);
+
+sinkattn_status sinkattn_decode(const sinkattn_decode_problem *problem, const void *q,
+                                const void *k_cache, const void *v_cache,
+                                const int32_t *cache_seqlens, const float *sinks, void *o,
+                                float *lse, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

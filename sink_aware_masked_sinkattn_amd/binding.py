@@ -66,6 +66,19 @@ class Problem(ctypes.Structure):
     ]
 
 
+class DecodeProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("cache_capacity", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("prefix", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
 _LIB = None
 
 
@@ -97,6 +110,11 @@ def load_library(path: str = LIB_PATH):
     lib.sinkattn_key_tile_segments.restype = i32
     lib.sinkattn_tile_config.argtypes = [pp, ctypes.POINTER(i32)]
     lib.sinkattn_tile_config.restype = ctypes.c_int
+    dp = ctypes.POINTER(DecodeProblem)
+    lib.sinkattn_decode_workspace_size.argtypes = [dp]
+    lib.sinkattn_decode_workspace_size.restype = sz
+    lib.sinkattn_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sinkattn_decode.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -247,3 +265,53 @@ def sinkattn_tile_config(pb: Problem):
     if st != 0:
         raise SinkAttnError(st, "sinkattn_tile_config", lib)
     return int(out[0]), int(out[1])
+
+
+def make_decode_problem(q: torch.Tensor, k_cache: torch.Tensor, window: int, prefix: int,
+                        softmax_scale: Optional[float] = None) -> DecodeProblem:
+    """Decode problem from q [B, Hq, d] and k_cache [B, Tmax, Hkv, d]."""
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16:
+        raise ValueError("decode takes bf16 q and caches")
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and the caches [B, Tmax, Hkv, d]")
+    pb = DecodeProblem()
+    pb.batch, pb.heads_q, pb.head_dim = q.shape
+    pb.cache_capacity = k_cache.shape[1]
+    pb.heads_kv = k_cache.shape[2]
+    pb.window = int(min(window, WINDOW_INF))
+    pb.prefix = int(prefix)
+    pb.softmax_scale = float(softmax_scale if softmax_scale is not None
+                             else 1.0 / math.sqrt(q.shape[-1]))
+    return pb
+
+
+def sinkattn_decode_workspace_size(pb: DecodeProblem) -> int:
+    return int(load_library().sinkattn_decode_workspace_size(ctypes.byref(pb)))
+
+
+def sinkattn_decode(q, k_cache, v_cache, cache_seqlens, sinks, window: int, prefix: int,
+                    softmax_scale=None, out=None, lse=None, want_lse: bool = True,
+                    workspace=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Decode one query token per sequence against its cache: returns (o, lse),
+    o [B, Hq, d] bf16, lse [B, Hq] fp32 (content-only log-sum-exp)."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (cache_seqlens, "cache_seqlens"), (sinks, "sinks")):
+        _dev(t, n)
+    if cache_seqlens.dtype != torch.int32:
+        raise ValueError("cache_seqlens must be int32")
+    pb = make_decode_problem(q, k_cache, window, prefix, softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((pb.batch, pb.heads_q), dtype=torch.float32, device=q.device)
+    need = sinkattn_decode_workspace_size(pb)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.sinkattn_decode(ctypes.byref(pb), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                             _ptr(cache_seqlens), _ptr(sinks), _ptr(out), _ptr(lse),
+                             _ptr(workspace), workspace.numel(), _stream())
+    if st != 0:
+        raise SinkAttnError(st, "sinkattn_decode", lib)
+    return out, lse
+

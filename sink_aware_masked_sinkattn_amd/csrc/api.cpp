@@ -44,6 +44,12 @@ hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const v
 hipError_t launch_convert(int dtype_is_f32, const float* dk_acc, const float* dv_acc, void* dk,
                           void* dv, long long n_kv, float scale, hipStream_t stream);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
+hipError_t launch_decode_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
+                                  const int* cache_seqlens, const float* sinks, bf16* o,
+                                  float* lse, float* workspace, int batch, int t_max, int heads_q,
+                                  int heads_kv, int window, int prefix, float scale,
+                                  hipStream_t stream);
+size_t decode_workspace_bytes(int batch, int t_max, int heads_kv, int window, int prefix);
 int fwd_key_tile(int window);
 int dkdv_query_tile(int window);
 bool dq_clears_dkdv_accumulators();
@@ -109,6 +115,23 @@ Workspace workspace_layout(const sinkattn_problem* pb, const Dims& dims) {
 }
 
 sinkattn_status hip_status(hipError_t e) { return e == hipSuccess ? SINKATTN_OK : SINKATTN_ERR_HIP; }
+
+// Decode problem checks.  No HIP calls.
+sinkattn_status check_decode(const sinkattn_decode_problem* pb) {
+  if (!pb) return SINKATTN_ERR_NULL_POINTER;
+  if (pb->batch < 0 || pb->cache_capacity < 0 || pb->heads_q <= 0 || pb->heads_kv <= 0 ||
+      pb->head_dim <= 0)
+    return SINKATTN_ERR_BAD_SHAPE;
+  if (pb->heads_q % pb->heads_kv != 0) return SINKATTN_ERR_BAD_SHAPE;
+  if (pb->window < 0 || pb->prefix < 0) return SINKATTN_ERR_BAD_MASK;
+  if (pb->head_dim != 64 || pb->heads_q / pb->heads_kv > 16) return SINKATTN_ERR_UNSUPPORTED;
+  if (!(pb->softmax_scale > 0.0f) || pb->softmax_scale > 1.0e30f) return SINKATTN_ERR_BAD_SHAPE;
+  if ((long long)pb->batch * pb->cache_capacity > (1LL << 31) - 1) return SINKATTN_ERR_BAD_SHAPE;
+  if ((long long)pb->heads_q * pb->head_dim > (1LL << 30)) return SINKATTN_ERR_BAD_SHAPE;
+  return SINKATTN_OK;
+}
+
+int clamp_window(int window, int capacity) { return window > capacity ? capacity : window; }
 
 }  // namespace
 
@@ -284,6 +307,43 @@ sinkattn_status sinkattn_bwd(SINKATTN_BWD_ARGS) {
 sinkattn_status sinkattn_bwd_phases(uint32_t phases, SINKATTN_BWD_ARGS) {
   if (phases == 0 || (phases & ~(uint32_t)SINKATTN_BWD_ALL) != 0) return SINKATTN_ERR_BAD_SHAPE;
   return bwd_phases(phases, pb, SINKATTN_BWD_PASS);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t sinkattn_decode_workspace_size(const sinkattn_decode_problem* pb) {
+  if (check_decode(pb) != SINKATTN_OK) return 0;
+  return round_up(decode_workspace_bytes(pb->batch, pb->cache_capacity, pb->heads_kv,
+                                         clamp_window(pb->window, pb->cache_capacity),
+                                         clamp_window(pb->prefix, pb->cache_capacity)));
+}
+
+sinkattn_status sinkattn_decode(const sinkattn_decode_problem* pb, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* cache_seqlens, const float* sinks, void* o,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  const sinkattn_status st = check_decode(pb);
+  if (st != SINKATTN_OK) return st;
+  if (pb->batch == 0) return SINKATTN_OK;
+  if (!q || !k_cache || !v_cache || !cache_seqlens || !sinks || !o)
+    return SINKATTN_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(sinks) || (lse && !aligned16(lse)) ||
+      (reinterpret_cast<uintptr_t>(cache_seqlens) & 3u) != 0)
+    return SINKATTN_ERR_MISALIGNED;
+  const int window = clamp_window(pb->window, pb->cache_capacity);
+  const int prefix = clamp_window(pb->prefix, pb->cache_capacity);
+  const size_t need = decode_workspace_bytes(pb->batch, pb->cache_capacity, pb->heads_kv, window,
+                                             prefix);
+  if (!workspace || workspace_bytes < need) return SINKATTN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SINKATTN_ERR_MISALIGNED;
+  return hip_status(launch_decode_bf16_d64(
+      (const bf16*)q, (const bf16*)k_cache, (const bf16*)v_cache, cache_seqlens, sinks, (bf16*)o,
+      lse, (float*)workspace, pb->batch, pb->cache_capacity, pb->heads_q, pb->heads_kv, window,
+      prefix, pb->softmax_scale, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

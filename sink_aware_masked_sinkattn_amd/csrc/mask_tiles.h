@@ -90,3 +90,45 @@ SA_HD int sa_dkdv_block_chunks(int kb, int n, int w, int p, int group, int bq, i
   const int n_iter = (hi / bq - lo / bq + 1) * group;
   return (n_iter + (1 << chunk_shift) - 1) >> chunk_shift;
 }
+
+// Decode: the keys the query at position n - 1 of a sequence of n tokens sees
+// are the prefix [0, min(p, n)) and the window [max(0, n - 1 - w), n), merged
+// when they touch.  Writes the two ranges to out[0..3] (begin0, end0, begin1,
+// end1; the first is empty when there is no prefix, the second when merged)
+// and returns the number of chunks of kw keys, each range cut from its start.
+SA_HD int sa_decode_ranges(int n, int w, int p, int kw, int* out) {
+  if (n <= 0) {
+    out[0] = out[1] = out[2] = out[3] = 0;
+    return 0;
+  }
+  const int pe = sa_min(p, n);
+  const long long wbl = (long long)(n - 1) - (long long)w;
+  const int wb = wbl > 0 ? (int)wbl : 0;
+  if (pe >= wb) {
+    out[0] = 0; out[1] = n; out[2] = n; out[3] = n;
+    return (n + kw - 1) / kw;
+  }
+  out[0] = 0; out[1] = pe; out[2] = wb; out[3] = n;
+  return (pe + kw - 1) / kw + (n - wb + kw - 1) / kw;
+}
+
+// Keys [k0, k1) of chunk c (0 <= c < the count above) of the ranges r.
+SA_HD void sa_decode_chunk(const int* r, int kw, int c, int* k0, int* k1) {
+  const int ca = (r[1] - r[0] + kw - 1) / kw;
+  if (c < ca) {
+    *k0 = r[0] + c * kw;
+    *k1 = sa_min(*k0 + kw, r[1]);
+  } else {
+    *k0 = r[2] + (c - ca) * kw;
+    *k1 = sa_min(*k0 + kw, r[3]);
+  }
+}
+
+// Upper bound of the chunk count over every n <= t_max: the prefix range
+// holds at most min(p, t_max) keys and the window range min(w + 1, t_max);
+// when the two merge, ceil((a + b) / kw) <= ceil(a / kw) + ceil(b / kw).
+SA_HD int sa_decode_max_chunks(int t_max, int w, int p, int kw) {
+  const int pw = sa_min(p, t_max);
+  const long long win = (long long)w + 1 < (long long)t_max ? (long long)w + 1 : t_max;
+  return (pw + kw - 1) / kw + (int)((win + kw - 1) / kw);
+}

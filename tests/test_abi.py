@@ -153,3 +153,60 @@ def test_tile_config():
     with pytest.raises(binding.SinkAttnError):
         binding.sinkattn_tile_config(_problem(window=-1))
     assert _lib().sinkattn_tile_config(ctypes.byref(_problem()), None) == 1
+
+
+def _dproblem(**kw):
+    pb = binding.DecodeProblem()
+    pb.batch = kw.get("batch", 4)
+    pb.cache_capacity = kw.get("cache_capacity", 1024)
+    pb.heads_q = kw.get("heads_q", 8)
+    pb.heads_kv = kw.get("heads_kv", 1)
+    pb.head_dim = kw.get("head_dim", 64)
+    pb.window = kw.get("window", 128)
+    pb.prefix = kw.get("prefix", 4)
+    pb.softmax_scale = kw.get("softmax_scale", 0.125)
+    return pb
+
+
+def _decode(pb, ws=A, ws_bytes=1 << 40, **ptrs):
+    p = {n: ptrs.get(n, A) for n in ("q", "k", "v", "lens", "s", "o", "lse")}
+    return _lib().sinkattn_decode(ctypes.byref(pb), p["q"], p["k"], p["v"], p["lens"], p["s"],
+                                  p["o"], p["lse"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(heads_q=6, heads_kv=4), 2),
+    (dict(batch=-1), 2),
+    (dict(cache_capacity=-1), 2),
+    (dict(softmax_scale=0.0), 2),
+    (dict(window=-1), 3),
+    (dict(prefix=-1), 3),
+    (dict(head_dim=128), 4),
+    (dict(heads_q=32, heads_kv=1), 4),     # more than 16 query heads per kv head
+])
+def test_decode_invalid_problem_rejected(kw, code):
+    pb = _dproblem(**kw)
+    assert _decode(pb) == code
+    assert _lib().sinkattn_decode_workspace_size(ctypes.byref(pb)) == 0
+
+
+def test_decode_pointer_and_workspace_checks():
+    pb = _dproblem()
+    need = _lib().sinkattn_decode_workspace_size(ctypes.byref(pb))
+    assert need > 0 and need % 256 == 0
+    assert _lib().sinkattn_decode(None, A, A, A, A, A, A, A, A, need, None) == 1
+    for name in ("q", "k", "v", "lens", "s", "o"):
+        assert _decode(pb, **{name: None}) == 1, name
+    for name in ("q", "k", "v", "s", "o", "lse"):
+        assert _decode(pb, **{name: A + 8}) == 5, name
+    assert _decode(pb, lens=A + 2) == 5
+    assert _decode(pb, ws=None) == 6
+    assert _decode(pb, ws_bytes=1) == 6
+    assert _decode(pb, ws=A + 64, ws_bytes=need) == 5
+    # no sequences: nothing to do, no pointer is touched
+    assert _decode(_dproblem(batch=0), q=None, k=None, v=None, lens=None, s=None, o=None,
+                   lse=None, ws=None, ws_bytes=0) == 0
+    # the workspace grows with the batch and the cache length
+    big = _lib().sinkattn_decode_workspace_size(ctypes.byref(_dproblem(batch=8, cache_capacity=8192,
+                                                                      window=2**31 - 1, prefix=0)))
+    assert big >= need

@@ -45,3 +45,14 @@ def test_kernel_variant_names():
     for ph, name in narrow.items():
         assert bench.kernel_base(name) == wide[ph]
         assert bench.kernel_source_sha(name) == bench.kernel_source_sha(wide[ph])
+
+
+def test_decode_visible_count():
+    import bench
+
+    def brute(n, w, p):
+        return sum(1 for k in range(n) if k <= n - 1 and (n - 1 - k <= w or k < p))
+    for n in range(0, 70):
+        for w in (0, 1, 5, 63, 2**31 - 1):
+            for p in (0, 1, 4, 64, 100):
+                assert bench.decode_visible(n, w, p) == brute(n, w, p)

@@ -170,3 +170,86 @@ def workload_inputs(name: str) -> list:
                                lengths=lengths, gen=gen))
         out[-1].meta["workload"] = name
     return out
+
+
+# ------------------------------------------------------------------ decode
+#
+# Rollout decode: one new query token per sequence against a key/value cache
+# of up to ``capacity`` rows.  Recipe: one generator seeded ``2000 + index``;
+# the cache lengths first (uniform on [lo, hi]), then per layer q [B, Hq, d],
+# the K and V caches [B, capacity, Hkv, d] (``std * N(0, 1)``, rounded once
+# to bf16; rows past a sequence's length are drawn too and must not matter),
+# then the sinks ``N(0, 1)`` (fp32).
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    index: int                      # seed = 2000 + index
+    batch: int                      # sequences (rollouts) decoded together
+    capacity: int                   # cache rows per sequence
+    lengths: Tuple[int, int]        # cached tokens per sequence ~ U[lo, hi]
+    heads_q: int
+    heads_kv: int
+    head_dim: int
+    std: float
+    layers: Tuple[Tuple[int, int], ...]   # (window, prefix) per layer
+
+    @property
+    def seed(self) -> int:
+        return 2000 + self.index
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        # four GRPO groups of 8 rollouts, 1k-8k tokens each, the layer pair of
+        # the long-context training workload
+        DecodeWorkload("decode_grpo_32", 0, 32, 8192, (1024, 8192), 64, 8, 64, 0.5,
+                       ((128, 4), (WINDOW_INF, 0))),
+    ]
+}
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor                 # [B, Hq, d]
+    k_cache: torch.Tensor           # [B, capacity, Hkv, d]
+    v_cache: torch.Tensor
+    cache_seqlens: torch.Tensor     # int32 [B]
+    sinks: torch.Tensor             # [Hq] fp32
+    window: int
+    prefix: int
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+
+def make_decode_inputs(*, lengths: Tuple[int, ...], capacity: int, heads_q: int, heads_kv: int,
+                       head_dim: int, window: int, prefix: int, seed: int, std: float = 1.0,
+                       gen: Optional[torch.Generator] = None) -> DecodeInputs:
+    """Draw one decode call's inputs (bf16 q and caches, fp32 sinks)."""
+    if gen is None:
+        gen = torch.Generator().manual_seed(seed)
+    b = len(lengths)
+    q = draw(gen, (b, heads_q, head_dim), std, "bf16")
+    k = draw(gen, (b, capacity, heads_kv, head_dim), std, "bf16")
+    v = draw(gen, (b, capacity, heads_kv, head_dim), std, "bf16")
+    sinks = torch.randn(heads_q, generator=gen, dtype=torch.float32)
+    return DecodeInputs(q=q, k_cache=k, v_cache=v,
+                        cache_seqlens=torch.tensor(lengths, dtype=torch.int32), sinks=sinks,
+                        window=int(window), prefix=int(prefix),
+                        scale=1.0 / math.sqrt(head_dim),
+                        meta={"seed": seed, "std": std})
+
+
+def decode_workload_inputs(name: str) -> list:
+    """All layers' inputs of a named decode workload, from its own generator."""
+    wl = DECODE_WORKLOADS[name]
+    gen = torch.Generator().manual_seed(wl.seed)
+    lengths = draw_lengths(gen, wl.batch, *wl.lengths)
+    out = []
+    for (w, p) in wl.layers:
+        out.append(make_decode_inputs(lengths=lengths, capacity=wl.capacity, heads_q=wl.heads_q,
+                                      heads_kv=wl.heads_kv, head_dim=wl.head_dim, window=w,
+                                      prefix=p, seed=wl.seed, std=wl.std, gen=gen))
+        out[-1].meta["workload"] = name
+    return out
