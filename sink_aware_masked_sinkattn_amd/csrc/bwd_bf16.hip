@@ -86,16 +86,15 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
   const int g = lane >> 5;
   const int grp = lane >> 4;
   const int li = lane & 15;
-#pragma unroll
-  for (int qb = 0; qb < BQ / 32; ++qb) {
-    // A operands (query rows, head dim along k) for S = Q K^T and dP = dO V^T
+  // S = Q K^T and dP = dO V^T of 32-row query block qb (A operands: query
+  // rows, head dim along k, from LDS)
+  auto sdp = [&](int qb, f32x16 (&st)[KB], f32x16 (&dp)[KB]) {
     bf16x8 qa[4], da[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       qa[s] = *(const bf16x8*)(qs + tile_off(qb * 32 + l32, 16 * s + 8 * g));
       da[s] = *(const bf16x8*)(dos + tile_off(qb * 32 + l32, 16 * s + 8 * g));
     }
-    f32x16 st[KB], dp[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       st[kb] = f32x16{};
@@ -106,8 +105,11 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
         dp[kb] = mfma32x32x16(da[s], vf[kb][s], dp[kb]);
       }
     }
+  };
+  // P', dS of block qb from its S and dP, then dV += P'^T dO, dK += dS^T Q
+  auto rest = [&](int qb, const f32x16 (&st)[KB], const f32x16 (&dp)[KB]) {
     // B operands of dV += P'^T dO and dK += dS^T Q (query index along k):
-    // transpose reads; issued before the softmax arithmetic
+    // transpose reads
     bf16x8 dob[2][2], qbt[2][2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -154,6 +156,12 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
         }
       }
     }
+  };
+#pragma unroll
+  for (int qb = 0; qb < BQ / 32; ++qb) {
+    f32x16 st[KB], dp[KB];
+    sdp(qb, st, dp);
+    rest(qb, st, dp);
   }
 }
 
