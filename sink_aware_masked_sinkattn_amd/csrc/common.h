@@ -34,8 +34,14 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Transposed 4 x 16-bit read from LDS (see header comment).
-__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+// Transposed 4 x 16-bit read from LDS (see header comment).  The builtin's
+// memory operand carries no alias information of its own, and without any the
+// compiler makes each such read wait (s_waitcnt vmcnt(0)) for every LDS load
+// DMA in flight -- including the prefetch of the next tile into the other
+// buffer, which then overlaps nothing.  A restrict parameter gives the inlined
+// read an alias scope, so only the kernels' own explicit waits remain (every
+// tile is waited for and published with a barrier before it is read).
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* __restrict__ p) {
   s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(bf16x4, r);
 }
