@@ -72,97 +72,117 @@ struct __attribute__((aligned(16))) DkvSmem {
   float dd[2][BQ];
 };
 
-// One BQ-row query tile against this wave's KW keys (KB blocks of 32).
-// MASK: apply the element predicate (partial tiles); full tiles run without
-// any mask arithmetic.  The query-side operands (Q, dO rows and their
-// transposes) are read once per 32-row block and shared by the key blocks.
+// One BQ-row query tile against this wave's 32 keys.  MASK: apply the
+// element predicate (partial tiles); full tiles run without any mask
+// arithmetic.
+//
+// Issue order.  Per 32-row query block the work is four MFMA chains of four
+// (S, dP, dV, dK) and two stretches of VALU work that depend on them in turn
+// (P' from S; dS from P' and dP).  Left to itself the compiler issues the
+// MFMAs in bunches and the VALU work between them, so a wave keeps only one
+// of the two units busy at a time.  Here the block is issued as
+//   S chain, with L and the dV operands (transpose reads) in its shadow;
+//   dP chain, each MFMA followed by a quarter of the P' work;
+//   dV chain, each MFMA followed by a quarter of the dS work;
+//   dK chain, with the next block's Q and dO rows read in its shadow;
+// so each wave overlaps its own VALU work with MFMAs.  sched_barrier fences
+// hold every part in place (the compiler may still order inside a part).
+// Live registers stay those of the plain order.
 template <int BQ, bool MASK>
 __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const float* l2s,
                                           const float* dds, const bf16x8 (&kf)[KB][4],
                                           const bf16x8 (&vf)[KB][4], f32x16 (&dk)[KB][2],
                                           f32x16 (&dv)[KB][2], int q0, int kw0, int window,
                                           int prefix, float scale_log2, int lane) {
+  static_assert(KB == 1, "the issue order is written for one 32-key block per wave");
   const int l32 = lane & 31;
   const int g = lane >> 5;
   const int grp = lane >> 4;
   const int li = lane & 15;
-  // S = Q K^T and dP = dO V^T of 32-row query block qb (A operands: query
-  // rows, head dim along k, from LDS)
-  auto sdp = [&](int qb, f32x16 (&st)[KB], f32x16 (&dp)[KB]) {
-    bf16x8 qa[4], da[4];
+  const int k = kw0 + l32;
+  const int lim = k < prefix ? SA_LIM_PREFIX : window;
+  // A operands of S = Q K^T and dP = dO V^T (query rows, head dim along k)
+  bf16x8 qa[4], da[4];
+  auto read_rows = [&](int qb) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       qa[s] = *(const bf16x8*)(qs + tile_off(qb * 32 + l32, 16 * s + 8 * g));
       da[s] = *(const bf16x8*)(dos + tile_off(qb * 32 + l32, 16 * s + 8 * g));
     }
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      st[kb] = f32x16{};
-      dp[kb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        st[kb] = mfma32x32x16(qa[s], kf[kb][s], st[kb]);
-        dp[kb] = mfma32x32x16(da[s], vf[kb][s], dp[kb]);
-      }
-    }
   };
-  // P', dS of block qb from its S and dP, then dV += P'^T dO, dK += dS^T Q
-  auto rest = [&](int qb, const f32x16 (&st)[KB], const f32x16 (&dp)[KB]) {
-    // B operands of dV += P'^T dO and dK += dS^T Q (query index along k):
-    // transpose reads
-    bf16x8 dob[2][2], qbt[2][2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int r0 = qb * 32 + 16 * hh + 4 * g + (li >> 2);
-#pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
-        dob[hh][db] = cat8(lds_read_tr4(dos + tile_off(r0, c0)), lds_read_tr4(dos + tile_off(r0 + 8, c0)));
-        qbt[hh][db] = cat8(lds_read_tr4(qs + tile_off(r0, c0)), lds_read_tr4(qs + tile_off(r0 + 8, c0)));
-      }
-    }
-    // P' = exp2(S*scale*log2e - L*log2e), dS = P' (dP - D); this lane's C rows
-    // are queries qb*32 + 8*(i/4) + 4g + i%4, its column is key kw0 + kb*32 + l32
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int k = kw0 + kb * 32 + l32;
-      const int lim = k < prefix ? SA_LIM_PREFIX : window;
-      const int base = sa_opaque(q0 + qb * 32 + 4 * g - k);   // q - k = base + 8*(i/4) + i%4
-      float pp[16], dsv[16];
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int qr = qb * 32 + 8 * i4 + 4 * g;
-        const f32x4 l4 = *(const f32x4*)(l2s + qr);
-        const f32x4 d4 = *(const f32x4*)(dds + qr);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * i4 + e;
-          float p = fast_exp2(fmaf(st[kb][i], scale_log2, -l4[e]));
-          if (MASK) p = sa_vis(base + 8 * i4 + e, lim) ? p : 0.0f;
-          pp[i] = p;
-          dsv[i] = p * (dp[kb][i] - d4[e]);
-        }
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const bf16x8 pa = to_bf16x8(pp[8 * hh], pp[8 * hh + 1], pp[8 * hh + 2], pp[8 * hh + 3],
-                                    pp[8 * hh + 4], pp[8 * hh + 5], pp[8 * hh + 6], pp[8 * hh + 7]);
-        const bf16x8 sa = to_bf16x8(dsv[8 * hh], dsv[8 * hh + 1], dsv[8 * hh + 2], dsv[8 * hh + 3],
-                                    dsv[8 * hh + 4], dsv[8 * hh + 5], dsv[8 * hh + 6], dsv[8 * hh + 7]);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          dv[kb][db] = mfma32x32x16(pa, dob[hh][db], dv[kb][db]);
-          dk[kb][db] = mfma32x32x16(sa, qbt[hh][db], dk[kb][db]);
-        }
-      }
-    }
+  // B operand (query index along k) of a dV or dK MFMA: rows qb*32 + 16*hh +
+  // 8*(i/4) + 4g + i%4 ... of the row-major tile, columns db*32 + l32
+  auto read_tr = [&](const bf16* t, int qb, int hh, int db) {
+    const int r0 = qb * 32 + 16 * hh + 4 * g + (li >> 2);
+    const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
+    return cat8(lds_read_tr4(t + tile_off(r0, c0)), lds_read_tr4(t + tile_off(r0 + 8, c0)));
   };
+  read_rows(0);
+
 #pragma unroll
   for (int qb = 0; qb < BQ / 32; ++qb) {
-    f32x16 st[KB], dp[KB];
-    sdp(qb, st, dp);
-    rest(qb, st, dp);
+    // this lane's C rows are queries qb*32 + 8*(i/4) + 4g + i%4, its column
+    // is key k: q - k = base + 8*(i/4) + i%4
+    const int base = sa_opaque(q0 + qb * 32 + 4 * g - k);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 st = {};
+    f32x4 l4[4];
+    bf16x8 dob[2][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      st = mfma32x32x16(qa[j], kf[0][j], st);
+      l4[j] = *(const f32x4*)(l2s + qb * 32 + 8 * j + 4 * g);
+      dob[j >> 1][j & 1] = read_tr(dos, qb, j >> 1, j & 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // P' = exp2(S*scale*log2e - L*log2e), a quarter after each dP MFMA
+    f32x16 dp = {};
+    float pp[16];
+    bf16x8 pa[2], qbt[2][2];
+    f32x4 d4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dp = mfma32x32x16(da[j], vf[0][j], dp);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * j + e;
+        float p = fast_exp2(fmaf(st[i], scale_log2, -l4[j][e]));
+        if (MASK) p = sa_vis(base + 8 * j + e, lim) ? p : 0.0f;
+        pp[i] = p;
+      }
+      if (j & 1) {
+        const int o = 8 * (j >> 1);
+        pa[j >> 1] = to_bf16x8(pp[o], pp[o + 1], pp[o + 2], pp[o + 3], pp[o + 4], pp[o + 5],
+                               pp[o + 6], pp[o + 7]);
+      }
+      d4[j] = *(const f32x4*)(dds + qb * 32 + 8 * j + 4 * g);
+      qbt[j >> 1][j & 1] = read_tr(qs, qb, j >> 1, j & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dV += P'^T dO; dS = P' (dP - D), a quarter after each dV MFMA
+    float dsv[16];
+    bf16x8 sa[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      dv[0][j & 1] = mfma32x32x16(pa[j >> 1], dob[j >> 1][j & 1], dv[0][j & 1]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * j + e;
+        dsv[i] = pp[i] * (dp[i] - d4[j][e]);
+      }
+      if (j & 1) {
+        const int o = 8 * (j >> 1);
+        sa[j >> 1] = to_bf16x8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5],
+                               dsv[o + 6], dsv[o + 7]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // dK += dS^T Q, and the next block's rows
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dk[0][j & 1] = mfma32x32x16(sa[j >> 1], qbt[j >> 1][j & 1], dk[0][j & 1]);
+    if (qb + 1 < BQ / 32) read_rows(qb + 1);
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // The flat work list, sequence by sequence: chunk indices from the highest
