@@ -82,8 +82,16 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
 
 // One key tile (NKB blocks of 32 keys) against this wave's QB blocks of 32
 // query rows.  MASK: apply the element predicate (partial tiles only).
+//
+// Issue order, per (key block, query block): S^T chain; dP^T chain with a
+// quarter of the P' work after each MFMA; the first half of dS, then its two
+// dQ MFMAs with the second half of dS behind them, then the last two.  A wave
+// so overlaps most of its own VALU work with its MFMAs instead of leaving
+// that to the other waves of its SIMD.  The next key block's operands are
+// read behind the last query block's MFMAs.  sched_barrier fences hold each
+// part in place.
 template <int NKB, int QB, bool MASK>
-__device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const bf16x8 (&qf)[QB][4],
+__device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB][4],
                                           const bf16x8 (&df)[QB][4], const float (&l2)[QB],
                                           const float (&dd)[QB], f32x16 (&acc)[QB][2], int qw0,
                                           int k0, int window, int prefix, float scale_log2,
@@ -92,56 +100,86 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
   const int g = lane >> 5;
   const int grp = lane >> 4;
   const int li = lane & 15;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    // A operands of S^T = K Q^T and dP^T = V dO^T (keys on m, head dim on k)
-    bf16x8 kf[4], vf[4];
+  // LDS: the K tile at byte address ktile, the V tile right after it.  One
+  // base register per read pattern (row reads, transpose reads), recomputed
+  // per tile rather than kept live across the loop.
+  constexpr int VOFF = NKB * 32 * 128;
+  const uint32_t ra = (uint32_t)sa_opaque((int)ktile + tile_row_base(l32, g));
+  const uint32_t ta =
+      (uint32_t)sa_opaque((int)ktile + tile_tr_base(4 * g + (li >> 2), 16 * (grp & 1) + 4 * (li & 3)));
+  // A operands of S^T = K Q^T and dP^T = V dO^T (keys on m, head dim on k)
+  bf16x8 kf[4], vf[4];
+  auto read_kv = [&](int kb) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      kf[s] = *(const bf16x8*)(ks + tile_off(kb * 32 + l32, 16 * s + 8 * g));
-      vf[s] = *(const bf16x8*)(vs + tile_off(kb * 32 + l32, 16 * s + 8 * g));
+      kf[s] = lds_read8((ra ^ (32 * s)) + kb * 4096);
+      vf[s] = lds_read8((ra ^ (32 * s)) + kb * 4096 + VOFF);
     }
-    // B operand of dQ += dS K (keys on k, head dim on n): transpose reads
-    bf16x8 kt[2][2];   // [hh][db]
+  };
+  // B operand of dQ += dS K (keys on k, head dim on n): transpose reads of
+  // rows kb*32 + 16*hh + 4g + li/4 (+8), columns db*32 + 16*(grp&1) + 4*(li&3)
+  bf16x8 kt[2][2];   // [hh][db]
+  auto read_kt = [&](int kb) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int r0 = kb * 32 + 16 * hh + 4 * g + (li >> 2);
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
-        kt[hh][db] = cat8(lds_read_tr4(ks + tile_off(r0, c0)), lds_read_tr4(ks + tile_off(r0 + 8, c0)));
+        const uint32_t t = (ta ^ (64 * db)) + kb * 4096 + hh * 2048;
+        kt[hh][db] = cat8(lds_read_tr4_at(t), lds_read_tr4_at((t ^ 32) + 1024));
       }
-    }
+  };
+  read_kv(0);
+  read_kt(0);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    // dS^T: lane = query, rows = keys kr + 8*(i/4) + i%4, kr = k0 + kb*32 + 4g
+    const int kr = k0 + kb * 32 + 4 * g;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      f32x16 st = f32x16{}, dpt = f32x16{};
+      const bool next_kb = (qb == QB - 1) && (kb + 1 < NKB);
+      const int base = sa_opaque(qw0 + qb * 32 + l32 - kr);
+      const int pb = prefix - kr;
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 st = f32x16{};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        st = mfma32x32x16(kf[s], qf[qb][s], st);
-        dpt = mfma32x32x16(vf[s], df[qb][s], dpt);
-      }
-      // dS^T: lane = query, rows = keys kr + 8*(i/4) + i%4, kr = k0 + kb*32 + 4g;
-      // hidden scores become -inf, so P' = 0 there (scale > 0)
-      if (MASK) {
-        const int kr = k0 + kb * 32 + 4 * g;
-        const int base = sa_opaque(qw0 + qb * 32 + l32 - kr);
-        mask_query_lane<true>(st, base, sa_opaque(prefix - kr), window);
-      }
-      float dsv[16];
+      for (int j = 0; j < 4; ++j) st = mfma32x32x16(kf[j], qf[qb][j], st);
+      __builtin_amdgcn_sched_barrier(0);
+      // P' = exp2(S*scale*log2e - L*log2e) (0 where hidden), a quarter after
+      // each dP^T MFMA
+      f32x16 dpt = f32x16{};
+      float pp[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(st[i], scale_log2, -l2[qb]));
-        dsv[i] = p * (dpt[i] - dd[qb]);
-      }
-      const bf16x8 d0 = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-      const bf16x8 d1 = to_bf16x8(dsv[8], dsv[9], dsv[10], dsv[11], dsv[12], dsv[13], dsv[14], dsv[15]);
+      for (int j = 0; j < 4; ++j) {
+        dpt = mfma32x32x16(vf[j], df[qb][j], dpt);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        acc[qb][db] = mfma32x32x16(d0, kt[0][db], acc[qb][db]);
-        acc[qb][db] = mfma32x32x16(d1, kt[1][db], acc[qb][db]);
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * j + e;
+          float p = fast_exp2(fmaf(st[i], scale_log2, -l2[qb]));
+          if (MASK) {
+            const int c = 8 * j + e;
+            p = sa_vis(base - c, c < pb ? SA_LIM_PREFIX : window) ? p : 0.0f;
+          }
+          pp[i] = sa_pin(p);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      if (next_kb) read_kv(kb + 1);   // this block's K and V operands are dead
+      // dS = P' (dP - D); dQ += dS K, one half of dS at a time
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float dsv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsv[e] = pp[8 * hh + e] * (dpt[8 * hh + e] - dd[qb]);
+        dsb[hh] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) acc[qb][db] = mfma32x32x16(dsb[hh], kt[hh][db], acc[qb][db]);
+      }
+      if (next_kb) read_kt(kb + 1);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 #ifndef SA_DQ_OCC
@@ -153,7 +191,7 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   constexpr int BQ = T::BQ;
   constexpr int BK = T::BK;
   constexpr int TILE_ELEMS = T::TILE_ELEMS;
-  __shared__ __attribute__((aligned(16))) bf16 smem[T::SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
+  __shared__ __attribute__((aligned(128))) bf16 smem[T::SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
 
   const int h = map_head(blockIdx.x, a.heads_q);
   const int z = blockIdx.y;
@@ -186,14 +224,17 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   const int n0 = seg[1] - seg[0];
   const int ntiles = n0 + (nseg > 1 ? seg[3] - seg[2] : 0);
 
-  // K / V tiles go straight from global memory into swizzled LDS tiles
+  // K / V tiles go straight from global memory into swizzled LDS tiles (the
+  // lane's row and chunk are recomputed per call: a few VALU instructions
+  // instead of registers held across the whole key loop)
   auto load_tile = [&](int t, int buf) {
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
     const int r0 = kt * BK;
+    const int ln = sa_opaque(lane), wv = sa_opaque(wave);
     tile_load_lds<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
-                             kv_row_stride, sv.len - r0, wave, lane);
+                             kv_row_stride, sv.len - r0, wv, ln);
     tile_load_lds<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
-                             kv_row_stride, sv.len - r0, wave, lane);
+                             kv_row_stride, sv.len - r0, wv, ln);
   };
 
   // the first K/V tile load goes out before the row loads below
@@ -249,12 +290,11 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
     const int k0 = kt * BK;
     const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
                                 : SA_TILE_SKIP;
-    const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
-    const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
+    const uint32_t ktile = lds_addr(smem + (2 * buf) * TILE_ELEMS);   // V tile follows
     if (cls == SA_TILE_FULL) {
-      tile_step<NKB, QB, false>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, QB, false>(ktile, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     } else if (cls == SA_TILE_PARTIAL) {
-      tile_step<NKB, QB, true>(ks, vs, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, QB, true>(ktile, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     }
     wait_all_mem();
     __syncthreads();

@@ -95,6 +95,14 @@ __device__ __forceinline__ int sa_opaque(int v) {
   return v;
 }
 
+// Pin a value to where it is computed: instruction selection otherwise places
+// side-effect-free arithmetic next to its first use, whatever sched_barrier
+// fences stand in between.
+__device__ __forceinline__ float sa_pin(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Mask one lane's 16 C-layout elements of a 32-key block when the lane holds
 // one query and element i holds key kr + c_i, c_i = 8*(i/4) + i%4, so that
 // q - k = base - c_i.  Hidden elements become -inf.  GENERAL: the block may
@@ -148,6 +156,40 @@ __device__ __forceinline__ int tile_off(int r, int c) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+// Operand addresses in a swizzled tile from one per-lane base each.  In bytes
+// from the tile start (checked exhaustively on the host):
+//   row reads, head-dim chunk 2s + g of row r:   tile_row_base(r, g) ^ (32 s)
+//   transpose reads at (r0, 32 db + c), r0 % 16 < 8, c < 32:
+//       row r0:      tile_tr_base(r0, c) ^ (64 db)
+//       row r0 + 8: (tile_tr_base(r0, c) ^ (64 db) ^ 32) + 1024
+//   16 m rows further down (either pattern): + 2048 m.
+// The tile's LDS address is a multiple of 128, so adding it before the XOR
+// keeps this exact: an operand address costs at most one v_xor, and row and
+// tile offsets fold into the instruction's immediate offset.
+__device__ __forceinline__ int tile_row_base(int r, int g) {
+  return r * 128 + ((g ^ tile_swz(r)) << 4);
+}
+__device__ __forceinline__ int tile_tr_base(int r0, int c) {
+  return r0 * 128 + (((c >> 3) ^ tile_swz(r0)) << 4) + 2 * (c & 7);
+}
+// LDS byte address of a pointer into shared memory
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)(const lds_void*)p;
+}
+// 16-byte and transposed 4 x 16-bit reads at an LDS byte address (restrict:
+// see lds_read_tr4)
+__device__ __forceinline__ bf16x8 lds_read8_p(const lds_bf16x8* __restrict__ p) { return *p; }
+__device__ __forceinline__ bf16x8 lds_read8(uint32_t a) {
+  return lds_read8_p((const lds_bf16x8*)(size_t)a);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr4_p(lds_s16x4* __restrict__ p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+}
+__device__ __forceinline__ bf16x4 lds_read_tr4_at(uint32_t a) {
+  return lds_read_tr4_p((lds_s16x4*)(size_t)a);
+}
 
 // Copy a ROWS x 64 bf16 tile from global memory straight into a swizzled LDS
 // tile (global_load_lds_dwordx4: lane i's 16 bytes land at lds_ptr + 16*i, so
