@@ -65,9 +65,9 @@ struct DkvArgs {
 };
 
 template <int BQ>
-struct __attribute__((aligned(16))) DkvSmem {
+struct __attribute__((aligned(128))) DkvSmem {
   bf16 qt[2][BQ * D];          // swizzled rows (tile_off)
-  bf16 dot[2][BQ * D];
+  bf16 dot[2][BQ * D];         // dot[b] starts 2 * BQ * D * 2 bytes after qt[b]
   float l2[2][BQ];
   float dd[2][BQ];
 };
@@ -89,7 +89,7 @@ struct __attribute__((aligned(16))) DkvSmem {
 // hold every part in place (the compiler may still order inside a part).
 // Live registers stay those of the plain order.
 template <int BQ, bool MASK>
-__device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const float* l2s,
+__device__ __forceinline__ void tile_step(uint32_t qtile, const float* l2s,
                                           const float* dds, const bf16x8 (&kf)[KB][4],
                                           const bf16x8 (&vf)[KB][4], f32x16 (&dk)[KB][2],
                                           f32x16 (&dv)[KB][2], int q0, int kw0, int window,
@@ -101,21 +101,28 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
   const int li = lane & 15;
   const int k = kw0 + l32;
   const int lim = k < prefix ? SA_LIM_PREFIX : window;
+  // LDS: the Q tile at byte address qtile, the dO tile DOFF bytes after it.
+  // One base register per read pattern (row reads, transpose reads),
+  // recomputed per tile: every other operand address is that base XOR a
+  // constant plus an immediate offset.
+  constexpr int DOFF = 2 * BQ * D * 2;
+  const uint32_t ra = (uint32_t)sa_opaque((int)qtile + tile_row_base(l32, g));
+  const uint32_t ta =
+      (uint32_t)sa_opaque((int)qtile + tile_tr_base(4 * g + (li >> 2), 16 * (grp & 1) + 4 * (li & 3)));
   // A operands of S = Q K^T and dP = dO V^T (query rows, head dim along k)
   bf16x8 qa[4], da[4];
   auto read_rows = [&](int qb) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      qa[s] = *(const bf16x8*)(qs + tile_off(qb * 32 + l32, 16 * s + 8 * g));
-      da[s] = *(const bf16x8*)(dos + tile_off(qb * 32 + l32, 16 * s + 8 * g));
+      qa[s] = lds_read8((ra ^ (32 * s)) + qb * 4096);
+      da[s] = lds_read8((ra ^ (32 * s)) + qb * 4096 + DOFF);
     }
   };
-  // B operand (query index along k) of a dV or dK MFMA: rows qb*32 + 16*hh +
-  // 8*(i/4) + 4g + i%4 ... of the row-major tile, columns db*32 + l32
-  auto read_tr = [&](const bf16* t, int qb, int hh, int db) {
-    const int r0 = qb * 32 + 16 * hh + 4 * g + (li >> 2);
-    const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
-    return cat8(lds_read_tr4(t + tile_off(r0, c0)), lds_read_tr4(t + tile_off(r0 + 8, c0)));
+  // B operand (query index along k) of a dV (TOFF = DOFF) or dK (TOFF = 0)
+  // MFMA: rows qb*32 + 16*hh + 4g + li/4 (+8), columns db*32 + 16*(grp&1) + 4*(li&3)
+  auto read_tr = [&](int toff, int qb, int hh, int db) {
+    const int o = toff + qb * 4096 + hh * 2048;   // folds into the immediate offset
+    return cat8(lds_read_tr4_at((ta ^ (64 * db)) + o), lds_read_tr4_at((ta ^ (64 * db + 32)) + o + 1024));
   };
   read_rows(0);
 
@@ -132,7 +139,7 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
     for (int j = 0; j < 4; ++j) {
       st = mfma32x32x16(qa[j], kf[0][j], st);
       l4[j] = *(const f32x4*)(l2s + qb * 32 + 8 * j + 4 * g);
-      dob[j >> 1][j & 1] = read_tr(dos, qb, j >> 1, j & 1);
+      dob[j >> 1][j & 1] = read_tr(DOFF, qb, j >> 1, j & 1);
     }
     __builtin_amdgcn_sched_barrier(0);
     // P' = exp2(S*scale*log2e - L*log2e), a quarter after each dP MFMA
@@ -156,7 +163,7 @@ __device__ __forceinline__ void tile_step(const bf16* qs, const bf16* dos, const
                                pp[o + 6], pp[o + 7]);
       }
       d4[j] = *(const f32x4*)(dds + qb * 32 + 8 * j + 4 * g);
-      qbt[j >> 1][j & 1] = read_tr(qs, qb, j >> 1, j & 1);
+      qbt[j >> 1][j & 1] = read_tr(0, qb, j >> 1, j & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     // dV += P'^T dO; dS = P' (dP - D), a quarter after each dV MFMA
@@ -347,10 +354,10 @@ __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
     const int cls = wave_active ? sa_tile_class(q0, q1, kw0, kw0 + KW - 1, a.window, a.prefix)
                                 : SA_TILE_SKIP;
     if (cls == SA_TILE_FULL) {
-      tile_step<BQ, false>(sm.qt[buf], sm.dot[buf], sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
+      tile_step<BQ, false>(lds_addr(sm.qt[buf]), sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
                        q0, kw0, a.window, a.prefix, a.scale_log2, lane);
     } else if (cls == SA_TILE_PARTIAL) {
-      tile_step<BQ, true>(sm.qt[buf], sm.dot[buf], sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
+      tile_step<BQ, true>(lds_addr(sm.qt[buf]), sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
                       q0, kw0, a.window, a.prefix, a.scale_log2, lane);
     }
     if (it + 1 < it_end) store_stats(buf ^ 1);
@@ -358,6 +365,13 @@ __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
     __syncthreads();
   }
 
+  // The epilogue reads the accumulators element by element; an asm operand
+  // holding each as one register tuple here keeps the register allocator
+  // from carrying a second, split copy through the loop (32 v_mov per tile).
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) asm volatile("" : "+v"(dk_acc[kb][db]), "+v"(dv_acc[kb][db]));
   // ---- C rows are keys kw0 + kb*32 + 8*(i/4) + 4g + i%4, column d = db*32 + l32
   if (wave_active) {
 #pragma unroll

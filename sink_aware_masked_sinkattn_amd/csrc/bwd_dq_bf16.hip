@@ -124,8 +124,9 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        const uint32_t t = (ta ^ (64 * db)) + kb * 4096 + hh * 2048;
-        kt[hh][db] = cat8(lds_read_tr4_at(t), lds_read_tr4_at((t ^ 32) + 1024));
+        const int o = kb * 4096 + hh * 2048;   // folds into the immediate offset
+        kt[hh][db] = cat8(lds_read_tr4_at((ta ^ (64 * db)) + o),
+                          lds_read_tr4_at((ta ^ (64 * db + 32)) + o + 1024));
       }
   };
   read_kv(0);

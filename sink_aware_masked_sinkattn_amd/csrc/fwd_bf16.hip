@@ -90,7 +90,7 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
 // One key tile (NKB blocks of 32 keys) against this wave's QB blocks of 32
 // query rows.  MASK: apply the element predicate (partial tiles only).
 template <int NKB, bool MASK>
-__device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const bf16x8 (&qf)[QB][4],
+__device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB][4],
                                           f32x16 (&acc)[QB][2], float (&m_run)[QB],
                                           float (&r_run)[QB], int qw0, int k0, int window,
                                           int prefix, float scale_log2, int lane) {
@@ -100,24 +100,30 @@ __device__ __forceinline__ void tile_step(const bf16* ks, const bf16* vs, const 
   const int li = lane & 15;
   // ---- operands of this tile, all issued up front so the LDS latency is
   // paid once: K (keys on m, head dim on k) and V^T (head dim on m, keys on
-  // k, by transpose reads)
+  // k, by transpose reads).  The K tile is at LDS byte address ktile, the V
+  // tile right after it; one base register per read pattern, recomputed per
+  // tile (every other address is that base XOR a constant plus an immediate).
+  constexpr int VOFF = NKB * 32 * 128;
+  const uint32_t ra = (uint32_t)sa_opaque((int)ktile + tile_row_base(l32, g));
+  const uint32_t ta =
+      (uint32_t)sa_opaque((int)ktile + VOFF + tile_tr_base(4 * g + (li >> 2), 16 * (grp & 1) + 4 * (li & 3)));
   bf16x8 kf[NKB][4];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) kf[kb][s] = *(const bf16x8*)(ks + tile_off(kb * 32 + l32, 16 * s + 8 * g));
+    for (int s = 0; s < 4; ++s) kf[kb][s] = lds_read8((ra ^ (32 * s)) + kb * 4096);
+  // V^T: rows kb*32 + 16*hh + 4g + li/4 (+8), columns db*32 + 16*(grp&1) + 4*(li&3)
   bf16x8 vt[2][NKB][2];   // [db][kb][hh]
 #pragma unroll
-  for (int db = 0; db < 2; ++db) {
-    const int c0 = db * 32 + 16 * (grp & 1) + 4 * (li & 3);
+  for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int r0 = kb * 32 + 16 * hh + 4 * g + (li >> 2);
-        vt[db][kb][hh] = cat8(lds_read_tr4(vs + tile_off(r0, c0)), lds_read_tr4(vs + tile_off(r0 + 8, c0)));
+        const int o = kb * 4096 + hh * 2048;   // folds into the immediate offset
+        vt[db][kb][hh] = cat8(lds_read_tr4_at((ta ^ (64 * db)) + o),
+                              lds_read_tr4_at((ta ^ (64 * db + 32)) + o + 1024));
       }
-  }
   // ---- S^T = K Q^T for both 32-key blocks and all query blocks: lane =
   // query, 16 keys per block in registers
   f32x16 st[NKB][QB];
@@ -196,7 +202,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   using T = FwdTiles<NKB>;
   constexpr int BK = T::BK;
   constexpr int TILE_ELEMS = T::TILE_ELEMS;
-  __shared__ __attribute__((aligned(16))) bf16 smem[T::SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
+  __shared__ __attribute__((aligned(128))) bf16 smem[T::SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
 
   const int h = map_head(blockIdx.x, a.heads_q);
   const int z = blockIdx.y;
@@ -275,12 +281,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     const int k0 = kt * BK;
     const int cls = wave_active ? sa_tile_class(qw0, qw1, k0, k0 + BK - 1, a.window, a.prefix)
                                 : SA_TILE_SKIP;
-    const bf16* ks = smem + (2 * buf) * TILE_ELEMS;
-    const bf16* vs = smem + (2 * buf + 1) * TILE_ELEMS;
+    const uint32_t ktile = lds_addr(smem + (2 * buf) * TILE_ELEMS);   // V tile follows
     if (cls == SA_TILE_FULL) {
-      tile_step<NKB, false>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, false>(ktile, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     } else if (cls == SA_TILE_PARTIAL) {
-      tile_step<NKB, true>(ks, vs, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, true>(ktile, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     }
     wait_all_mem();
     __syncthreads();
