@@ -316,12 +316,13 @@ __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
     *h = h_begin + (it - ti * a.group);
     *q0 = (qt_last - ti) * BQ;
   };
+  const TileLane tl = tile_lane(lane, q_row_stride * 2);
   auto load_tile = [&](int it, int buf) {
     int h, q0;
     tile_of(it, &h, &q0);
     const size_t off = ((size_t)sv.row_base + q0) * q_row_stride + (size_t)h * D;
-    tile_load_lds<BQ, WAVES>(sm.qt[buf], a.q + off, q_row_stride, sv.len - q0, wave, lane);
-    tile_load_lds<BQ, WAVES>(sm.dot[buf], a.dout + off, q_row_stride, sv.len - q0, wave, lane);
+    tile_load_lds_lane<BQ, WAVES>(sm.qt[buf], a.q + off, q_row_stride * 2, sv.len - q0, wave, tl);
+    tile_load_lds_lane<BQ, WAVES>(sm.dot[buf], a.dout + off, q_row_stride * 2, sv.len - q0, wave, tl);
     static_assert(2 * BQ <= 256, "L and D are staged by one thread per row");
     if (tid < 2 * BQ) {
       const int r = q0 + (tid & (BQ - 1));

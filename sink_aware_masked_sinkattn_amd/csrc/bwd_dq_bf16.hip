@@ -226,16 +226,16 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   const int ntiles = n0 + (nseg > 1 ? seg[3] - seg[2] : 0);
 
   // K / V tiles go straight from global memory into swizzled LDS tiles (the
-  // lane's row and chunk are recomputed per call: a few VALU instructions
-  // instead of registers held across the whole key loop)
+  // lane constants are recomputed per call: a few VALU instructions instead
+  // of registers held across the whole key loop)
   auto load_tile = [&](int t, int buf) {
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
     const int r0 = kt * BK;
-    const int ln = sa_opaque(lane), wv = sa_opaque(wave);
-    tile_load_lds<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
-                             kv_row_stride, sv.len - r0, wv, ln);
-    tile_load_lds<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
-                             kv_row_stride, sv.len - r0, wv, ln);
+    const TileLane tl = tile_lane(sa_opaque(lane), kv_row_stride * 2);
+    tile_load_lds_lane<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
+                                  kv_row_stride * 2, sv.len - r0, wave, tl);
+    tile_load_lds_lane<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
+                                  kv_row_stride * 2, sv.len - r0, wave, tl);
   };
 
   // the first K/V tile load goes out before the row loads below

@@ -214,5 +214,42 @@ __device__ __forceinline__ void tile_load_lds(bf16* lds_tile, const bf16* gbase,
   }
 }
 
+// Lane constants of the same copy with the address split in two (checked
+// against tile_load_lds on the host for every lane, block and row count):
+// lane i of an 8-row block reads tile row i/8 of the block; its chunk offset
+// for an even block is 16 * ((i%8) ^ tile_swz(i/8)), for an odd block that
+// XOR 32 (the swizzle of a row r + 8 is that of r XOR 2).
+struct TileLane {
+  int row_off;     // (lane / 8) * row_bytes
+  int chunk_off;   // 16 * ((lane % 8) ^ tile_swz(lane / 8))
+};
+__device__ __forceinline__ TileLane tile_lane(int lane, int row_bytes) {
+  TileLane t;
+  t.row_off = (lane >> 3) * row_bytes;
+  t.chunk_off = ((lane & 7) ^ tile_swz(lane >> 3)) << 4;
+  return t;
+}
+// tile_load_lds with the global address as a uniform part (tile base plus
+// the block's first row, clamped to the last valid row: scalar registers)
+// and a 32-bit lane offset (the lane's row, clamped the same way, plus its
+// chunk): two VALU instructions per 8-row block.  row_bytes is the global
+// row stride in bytes; the same rows-past-nvalid rule as tile_load_lds.
+template <int ROWS, int WAVES>
+__device__ __forceinline__ void tile_load_lds_lane(bf16* lds_tile, const bf16* gbase, int row_bytes,
+                                                   int nvalid, int wave, const TileLane& tl) {
+  constexpr int PER_WAVE = ROWS / (8 * WAVES);
+  static_assert(PER_WAVE * 8 * WAVES == ROWS, "tile rows must split into 8-row blocks per wave");
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+  for (int j = 0; j < PER_WAVE; ++j) {
+    const int blk = w * PER_WAVE + j;
+    const int r0 = min(blk * 8, nvalid - 1);
+    const int lim = max(nvalid - 1 - blk * 8, 0) * row_bytes;
+    const uint32_t off = (uint32_t)(min(tl.row_off, lim) + (tl.chunk_off ^ ((blk & 1) << 5)));
+    __builtin_amdgcn_global_load_lds((const void*)((const char*)gbase + (size_t)r0 * row_bytes + off),
+                                     (lds_void*)(lds_tile + blk * 512), 16, 0, 0);
+  }
+}
+
 // wait for every outstanding memory operation of this wave (vmcnt, lgkmcnt = 0)
 __device__ __forceinline__ void wait_all_mem() { __builtin_amdgcn_s_waitcnt(0); }

@@ -251,13 +251,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 
   // cooperative tile load: 512 chunks of 16 B per tensor, 2 per thread
   // K / V tiles go straight from global memory into swizzled LDS tiles
+  const TileLane tl = tile_lane(lane, kv_row_stride * 2);
   auto load_tile = [&](int t, int buf) {
     const int kt = t < n0 ? seg[0] + t : seg[2] + (t - n0);
     const int r0 = kt * BK;
-    tile_load_lds<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
-                             kv_row_stride, sv.len - r0, wave, lane);
-    tile_load_lds<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
-                             kv_row_stride, sv.len - r0, wave, lane);
+    tile_load_lds_lane<BK, WAVES>(smem + (2 * buf) * TILE_ELEMS, kbase + (size_t)r0 * kv_row_stride,
+                                  kv_row_stride * 2, sv.len - r0, wave, tl);
+    tile_load_lds_lane<BK, WAVES>(smem + (2 * buf + 1) * TILE_ELEMS, vbase + (size_t)r0 * kv_row_stride,
+                                  kv_row_stride * 2, sv.len - r0, wave, tl);
   };
 
   f32x16 acc[QB][2];
