@@ -69,7 +69,7 @@ struct __attribute__((aligned(128))) DkvSmem {
   bf16 qt[2][BQ * D];          // swizzled rows (tile_off)
   bf16 dot[2][BQ * D];         // dot[b] starts 2 * BQ * D * 2 bytes after qt[b]
   float l2[2][BQ];
-  float dd[2][BQ];
+  float dd[2][BQ];             // -D of the tile's rows
 };
 
 // One BQ-row query tile against this wave's 32 keys.  MASK: apply the
@@ -133,20 +133,23 @@ __device__ __forceinline__ void tile_step(uint32_t qtile, const float* l2s,
     const int base = sa_opaque(q0 + qb * 32 + 4 * g - k);
     __builtin_amdgcn_sched_barrier(0);
     f32x16 st = {};
-    f32x4 l4[4];
+    f32x4 l4[4], d4[4];
     bf16x8 dob[2][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       st = mfma32x32x16(qa[j], kf[0][j], st);
       l4[j] = *(const f32x4*)(l2s + qb * 32 + 8 * j + 4 * g);
+      d4[j] = *(const f32x4*)(dds + qb * 32 + 8 * j + 4 * g);
       dob[j >> 1][j & 1] = read_tr(DOFF, qb, j >> 1, j & 1);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // P' = exp2(S*scale*log2e - L*log2e), a quarter after each dP MFMA
-    f32x16 dp = {};
+    // P' = exp2(S*scale*log2e - L*log2e), a quarter after each dP MFMA.  The
+    // dP chain accumulates onto -D of each element's row, so it yields dP - D.
+    f32x16 dp;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dp[i] = d4[i >> 2][i & 3];
     float pp[16];
     bf16x8 pa[2], qbt[2][2];
-    f32x4 d4[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       dp = mfma32x32x16(da[j], vf[0][j], dp);
@@ -162,7 +165,6 @@ __device__ __forceinline__ void tile_step(uint32_t qtile, const float* l2s,
         pa[j >> 1] = to_bf16x8(pp[o], pp[o + 1], pp[o + 2], pp[o + 3], pp[o + 4], pp[o + 5],
                                pp[o + 6], pp[o + 7]);
       }
-      d4[j] = *(const f32x4*)(dds + qb * 32 + 8 * j + 4 * g);
       qbt[j >> 1][j & 1] = read_tr(0, qb, j >> 1, j & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -175,7 +177,7 @@ __device__ __forceinline__ void tile_step(uint32_t qtile, const float* l2s,
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 4 * j + e;
-        dsv[i] = pp[i] * (dp[i] - d4[j][e]);
+        dsv[i] = pp[i] * dp[i];
       }
       if (j & 1) {
         const int o = 8 * (j >> 1);
@@ -328,7 +330,7 @@ __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
       const int r = q0 + (tid & (BQ - 1));
       const size_t wi = (size_t)h * a.rows_total + sv.row_base + r;
       if (tid < BQ) lreg = (r < sv.len) ? a.l2_ws[wi] : INFINITY;
-      else lreg = (r < sv.len) ? a.d_ws[wi] : 0.0f;
+      else lreg = (r < sv.len) ? -a.d_ws[wi] : 0.0f;   // -D: the dP chain starts from it
     }
   };
   auto store_stats = [&](int buf) {
