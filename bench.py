@@ -25,6 +25,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -34,6 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "sink-attn fwd+bwd useful TFLOP/s and % bf16 MFMA peak at T=8192"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+NOMINAL_SCLK_GHZ = 2.4
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 WINDOW_INF = 2**31 - 1
 CPU_SAMPLE_HEADS = 4
@@ -106,6 +108,38 @@ def committed_traffic(kernel: str, workload: str):
     if not sha or not val or sha.group(1) != kernel_source_sha(kernel):
         return None
     return float(val.group(1))
+
+
+def committed_sclk(kernel: str, workload: str):
+    """Shader clock (GHz) under this workload, measured for `kernel` from the SQ counters of
+    the committed counter summary (SQ_BUSY_CYCLES per shader array over the kernel's time);
+    the row of the kernel's longest grid. None without such a summary."""
+    path = os.path.join(ROOT, "profiles", f"sq_counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    best = None
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) < 4 or cells[0] != kernel:
+            continue
+        try:
+            t_us, ghz = float(cells[2]), float(cells[3])
+        except ValueError:
+            continue
+        if best is None or t_us > best[0]:
+            best = (t_us, ghz)
+    return best[1] if best else None
+
+
+def compulsory_bytes(inp) -> tuple:
+    """HBM bytes the forward and the backward cannot avoid: forward reads Q, K, V and writes
+    O (bf16) and l (fp32); backward reads Q, K, V, dO (bf16), L and D (fp32) and writes dQ, dK,
+    dV (bf16)."""
+    q, k = inp.q.numel(), inp.k.numel()
+    rows = q // inp.q.shape[-1]               # (token, query head) rows
+    fwd = 2 * (q + 2 * k + q) + 4 * rows
+    bwd = 2 * (q + 2 * k + q) + 8 * rows + 2 * (q + 2 * k)
+    return fwd, bwd
 
 
 def cpu_baseline(layers, head_dim: int):
@@ -393,11 +427,18 @@ def main(argv=None):
     d = wl.head_dim
     per_layer = []
     for li, r in enumerate(runs):
-        ph = [sum(events[i][li][j].elapsed_time(events[i][li][j + 1]) for i in range(K)) / K
-              for j in range(5)]
+        per_it = [[events[i][li][j].elapsed_time(events[i][li][j + 1]) for j in range(5)]
+                  for i in range(K)]
+        ph = [sum(it[j] for it in per_it) / K for j in range(5)]
+        fwd_b, bwd_b = compulsory_bytes(r["inp"])
         per_layer.append({"window": r["inp"].window, "prefix": r["inp"].prefix,
                           "pairs": r["pairs"], "fwd_ms": ph[0], "bwd_prepare_ms": ph[1],
-                          "bwd_dq_ms": ph[2], "bwd_dkdv_ms": ph[3], "bwd_finish_ms": ph[4]})
+                          "bwd_dq_ms": ph[2], "bwd_dkdv_ms": ph[3], "bwd_finish_ms": ph[4],
+                          "median_ms": {"fwd": round(statistics.median(it[0] for it in per_it), 4),
+                                        "bwd": round(statistics.median(sum(it[1:]) for it in per_it), 4),
+                                        "total": round(statistics.median(sum(it) for it in per_it), 4)},
+                          "compulsory_gbs": {"fwd": round(fwd_b / (ph[0] * 1e-3) / 1e9, 1),
+                                             "bwd": round(bwd_b / (sum(ph[1:]) * 1e-3) / 1e9, 1)}})
     total_flops = sum(14 * d * r["pairs"] for r in runs)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
@@ -416,10 +457,17 @@ def main(argv=None):
     avg_ms = kern_time[dom] / launches
     achieved = kern_flops[dom] / launches / (avg_ms * 1e-3) / 1e12
     traffic = committed_traffic(dom, args.workload)
+    # the peak scales with the clock: 2516.6 TFLOP/s assumes 2.4 GHz, the measured shader
+    # clock under this load is lower (SQ counters of the committed counter summary)
+    sclk = committed_sclk(dom, args.workload)
+    peak_at_sclk = PEAK_BF16_TFLOPS * sclk / NOMINAL_SCLK_GHZ if sclk else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": dom, "avg_launch_ms": round(avg_ms, 4),
-                "algorithmic_flop_per_launch": kern_flops[dom] / launches}
+                "algorithmic_flop_per_launch": kern_flops[dom] / launches,
+                "sclk_ghz_measured": sclk,
+                "frac_at_measured_sclk": round(achieved / peak_at_sclk, 4) if sclk else None,
+                "sclk_source": f"profiles/sq_counters_{args.workload}.md" if sclk else None}
 
     # the full-causal layer alone (the target configuration)
     causal = [p for p in per_layer if p["window"] >= 8192 and p["prefix"] == 0]
@@ -459,6 +507,7 @@ def main(argv=None):
                               for (w, p) in wl.layers],
                    "parallelism": "single GPU"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "frac_of_peak_at_measured_sclk": round(value / peak_at_sclk, 4) if sclk else None,
         "useful_flop_per_step": total_flops,
         "full_causal_layer": causal_info,
         "per_layer_ms": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}

@@ -56,3 +56,31 @@ def test_decode_visible_count():
         for w in (0, 1, 5, 63, 2**31 - 1):
             for p in (0, 1, 4, 64, 100):
                 assert bench.decode_visible(n, w, p) == brute(n, w, p)
+
+
+def test_compulsory_bytes_target_layer():
+    # T=8192, Hq=64, Hkv=8, d=64: Q, K, V in and O out in bf16 plus l in fp32 is 153.1 MB for
+    # the forward; the backward reads Q, K, V, dO and L, D and writes dQ, dK, dV
+    inp = make_inputs(batch=1, seqlen=8192, heads_q=64, heads_kv=8, head_dim=64, window=128,
+                      prefix=4, seed=0, std=0.5, dtype="bf16")
+    q = 8192 * 64 * 64
+    k = 8192 * 8 * 64
+    rows = 8192 * 64
+    fwd, bwd = bench.compulsory_bytes(inp)
+    assert fwd == 2 * (q + k + k + q) + 4 * rows == 153_092_096
+    assert bwd == 2 * (q + k + k + q) + 4 * 2 * rows + 2 * (q + k + k)
+
+
+def test_committed_sclk_parses_summary(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "sq_counters_wl.md").write_text(
+        "| kernel | grid (threads) | time (us, profiled) | clock (GHz) | MFMA busy |\n"
+        "|---|---|---|---|---|\n"
+        "| kern_a | 100 | 50.0 | 1.95 | 10 % |\n"
+        "| kern_a | 200 | 900.5 | 1.81 | 40 % |\n"
+        "| kern_b | 100 | 2000.0 | 1.70 | 40 % |\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.committed_sclk("kern_a", "wl") == 1.81     # the longest grid of the kernel
+    assert bench.committed_sclk("kern_c", "wl") is None
+    assert bench.committed_sclk("kern_a", "other") is None
