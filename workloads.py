@@ -253,3 +253,100 @@ def decode_workload_inputs(name: str) -> list:
                                       prefix=p, seed=wl.seed, std=wl.std, gen=gen))
         out[-1].meta["workload"] = name
     return out
+
+
+# ---------------------------------------------------------------------------
+# GRPO token loss: packed per-token log-probs of a batch of rollout groups.
+# Rollouts alternate environment-observation spans (action mask 0: tool
+# outputs, user turns) with agent spans (mask 1: tokens the policy produced),
+# as in the multi-turn, tool-heavy trajectories the pages describe; rewards are
+# programmatic 0/1 outcomes.  Log-probs: old ~ -Exp(1) per token, the current
+# and the reference policy drift from it by small Gaussian log-ratios.
+@dataclass(frozen=True)
+class GrpoWorkload:
+    name: str
+    index: int                      # seed = 3000 + index
+    groups: int                     # prompts
+    group_size: int                 # rollouts per prompt (G)
+    lengths: Tuple[int, int]        # tokens per rollout ~ U[lo, hi]
+    agent_span: Tuple[int, int]     # optimised span lengths ~ U[lo, hi]
+    obs_span: Tuple[int, int]       # observation span lengths ~ U[lo, hi]
+    new_drift: float                # std of logp_new - logp_old
+    ref_drift: float                # std of logp_ref - logp_old
+    reward_p: float                 # P(R = 1)
+    eps_adv: float
+    eps_clip: float
+    beta: float
+    kl_mode: int
+
+    @property
+    def seed(self) -> int:
+        return 3000 + self.index
+
+
+GRPO_WORKLOADS = {
+    w.name: w
+    for w in [
+        # 64 prompts x 8 rollouts of 1k-8k tokens (about 2.4M packed tokens)
+        GrpoWorkload("grpo_64x8", 0, 64, 8, (1024, 8192), (16, 256), (32, 512), 0.1, 0.1, 0.4,
+                     1e-6, 0.2, 0.04, 0),
+    ]
+}
+
+
+@dataclass
+class GrpoInputs:
+    logp_new: torch.Tensor          # [N] fp32
+    logp_old: torch.Tensor          # [N] fp32
+    logp_ref: torch.Tensor          # [N] fp32
+    action_mask: torch.Tensor       # [N] uint8 (1 = optimised token)
+    rewards: torch.Tensor           # [B] fp32
+    cu_seqlens: torch.Tensor        # [B + 1] int32
+    group_size: int
+    eps_adv: float
+    eps_clip: float
+    beta: float
+    kl_mode: int
+    meta: dict = field(default_factory=dict)
+
+
+def make_grpo_inputs(*, lengths: Tuple[int, ...], group_size: int, seed: int,
+                     agent_span: Tuple[int, int] = (16, 256), obs_span: Tuple[int, int] = (32, 512),
+                     new_drift: float = 0.1, ref_drift: float = 0.1, reward_p: float = 0.4,
+                     eps_adv: float = 1e-6, eps_clip: float = 0.2, beta: float = 0.04,
+                     kl_mode: int = 0) -> GrpoInputs:
+    """Draw one batch of packed rollouts (rollout i has lengths[i] tokens)."""
+    gen = torch.Generator().manual_seed(seed)
+    n = int(sum(lengths))
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    if lengths:
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    old = -torch.empty(n, dtype=torch.float32).exponential_(1.0, generator=gen)
+    new = old + new_drift * torch.randn(n, generator=gen, dtype=torch.float32)
+    ref = old + ref_drift * torch.randn(n, generator=gen, dtype=torch.float32)
+    mask = torch.zeros(n, dtype=torch.uint8)
+    for i, length in enumerate(lengths):
+        pos, agent = int(cu[i]), False          # a rollout opens with an observation
+        end = pos + int(length)
+        while pos < end:
+            lo, hi = agent_span if agent else obs_span
+            span = int(torch.randint(lo, hi + 1, (1,), generator=gen))
+            if agent:
+                mask[pos:min(end, pos + span)] = 1
+            pos += span
+            agent = not agent
+    rewards = (torch.rand(len(lengths), generator=gen) < reward_p).to(torch.float32)
+    return GrpoInputs(logp_new=new, logp_old=old, logp_ref=ref, action_mask=mask,
+                      rewards=rewards, cu_seqlens=cu, group_size=int(group_size),
+                      eps_adv=eps_adv, eps_clip=eps_clip, beta=beta, kl_mode=kl_mode,
+                      meta={"seed": seed})
+
+
+def grpo_workload_inputs(name: str) -> GrpoInputs:
+    w = GRPO_WORKLOADS[name]
+    gen = torch.Generator().manual_seed(w.seed)
+    lengths = draw_lengths(gen, w.groups * w.group_size, *w.lengths)
+    return make_grpo_inputs(lengths=lengths, group_size=w.group_size, seed=w.seed + 1,
+                            agent_span=w.agent_span, obs_span=w.obs_span, new_drift=w.new_drift,
+                            ref_drift=w.ref_drift, reward_p=w.reward_p, eps_adv=w.eps_adv,
+                            eps_clip=w.eps_clip, beta=w.beta, kl_mode=w.kl_mode)
