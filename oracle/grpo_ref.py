@@ -23,7 +23,9 @@ inputs here are packed per-token log-probs of the current, old and reference
 policies, a per-token action mask and one reward per rollout.
 
 Readings where the pages leave a step open:
-  * std is the population standard deviation of the group's G rewards;
+  * std is the population standard deviation of the group's G rewards; a
+    reward equal to the group mean has advantage 0 (also for eps_A = 0 with
+    all G rewards equal, where eq. 3 reads 0 / 0);
   * the optimised tokens are those whose action mask is 1;
   * D_KL(pi_theta || pi_ref) is estimated per optimised token and averaged
     like the J term (same 1 / sum_i T_i): kl_mode 0 takes the log-ratio
@@ -61,7 +63,9 @@ def group_advantages(rewards, group_size: int, eps_adv: float) -> np.ndarray:
         r = r_all[m * g:(m + 1) * g]
         mu = r.sum() / g
         sigma = math.sqrt(((r - mu) ** 2).sum() / g)
-        adv[m * g:(m + 1) * g] = (r - mu) / (sigma + eps_adv)
+        # a reward equal to the group mean has advantage 0, also when eps_A = 0 and all G
+        # rewards are equal (eq. 3 would be 0 / 0 there; 0 is its limit for eps_A -> 0)
+        adv[m * g:(m + 1) * g] = np.where(r == mu, 0.0, (r - mu) / (sigma + eps_adv))
     return adv
 
 

@@ -16,6 +16,7 @@ def test_advantage_closed_form():
     assert np.allclose(adv, np.array([0.5, -0.5, -0.5, 0.5]) / (0.5 + 1e-6), rtol=0, atol=1e-15)
     # a group with equal rewards has no advantage (0 / (0 + eps))
     assert np.array_equal(oracle.group_advantages([3.0, 3.0, 3.0], 3, 1e-4), np.zeros(3))
+    assert np.array_equal(oracle.group_advantages([3.0, 3.0, 3.0], 3, 0.0), np.zeros(3))
 
 
 def test_advantage_matches_numpy_population_std():
