@@ -320,6 +320,119 @@ def run_decode(args) -> int:
     return 0
 
 
+GRPO_METRIC = "GRPO token loss + gradient: effective HBM GB/s of the compulsory bytes"
+
+
+def grpo_bytes(inp) -> int:
+    """Compulsory HBM bytes of one GRPO loss call: per token logp_new, logp_old (and logp_ref
+    with a KL term) and the action mask read, the gradient written; per rollout the reward
+    and the sequence offset read and the advantage written; the loss."""
+    n, b = inp.logp_new.numel(), inp.rewards.numel()
+    per_tok = 4 + 4 + (4 if inp.beta != 0.0 else 0) + 1 + 4
+    return n * per_tok + b * (4 + 4 + 4) + 4 + 4
+
+
+def grpo_cpu_baseline(inp, min_seconds: float = 10.0):
+    """The fp64 oracle's GRPO loss over the whole workload, repeated until about
+    `min_seconds` of CPU time."""
+    import oracle
+    args = (inp.logp_new.numpy(), inp.logp_old.numpy(), inp.logp_ref.numpy(),
+            inp.action_mask.numpy(), inp.rewards.numpy(), inp.cu_seqlens.numpy(),
+            inp.group_size, inp.eps_adv, inp.eps_clip, inp.beta, inp.kl_mode)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.grpo_loss(*args)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": grpo_bytes(inp) * reps / dt / 1e9, "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole workload ({inp.logp_new.numel()} tokens), fp64, {reps} "
+                      f"repetitions in {dt:.1f} s; GB/s of the same compulsory bytes",
+            "seconds": round(dt, 3)}
+
+
+def run_grpo(args) -> int:
+    """One step = one GRPO loss call (advantages, loss and per-token gradient) over the
+    packed batch; inputs resident, outputs and workspace preallocated.  value = compulsory
+    bytes / step time."""
+    import torch
+
+    from sink_aware_masked_sinkattn_amd import (load_library, make_grpo_problem,
+                                                sinkattn_grpo_loss,
+                                                sinkattn_grpo_workspace_size)
+    from workloads import GRPO_WORKLOADS, grpo_workload_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    load_library()
+    wl = GRPO_WORKLOADS[args.workload]
+    inp = grpo_workload_inputs(args.workload)
+    dev = torch.device("cuda:0")
+    t = {k: getattr(inp, k).to(dev) for k in ("logp_new", "logp_old", "logp_ref", "action_mask",
+                                              "rewards", "cu_seqlens")}
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    grad = torch.empty_like(t["logp_new"])
+    adv = torch.empty_like(t["rewards"])
+    pb = make_grpo_problem(inp.rewards.numel(), inp.group_size, inp.logp_new.numel(),
+                           inp.eps_adv, inp.eps_clip, inp.beta, inp.kl_mode)
+    ws = torch.empty(max(1, sinkattn_grpo_workspace_size(pb)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        sinkattn_grpo_loss(t["logp_new"], t["logp_old"], t["logp_ref"], t["action_mask"],
+                           t["rewards"], t["cu_seqlens"], inp.group_size, inp.eps_adv,
+                           inp.eps_clip, inp.beta, inp.kl_mode, loss=loss, grad=grad,
+                           advantages=adv, workspace=ws)
+        if ev:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+    per_call = [events[i][0].elapsed_time(events[i][1]) for i in range(K)]
+    avg_ms = sum(per_call) / K
+    nbytes = grpo_bytes(inp)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "grpo_group_stats + grpo_tokens (one sinkattn_grpo_loss call)",
+                "avg_launch_ms": round(avg_ms, 5), "median_call_ms":
+                    round(statistics.median(per_call), 5),
+                "algorithmic_bytes_per_launch": nbytes}
+    cpu = None if args.no_cpu_baseline else grpo_cpu_baseline(inp)
+    out = {
+        "metric": GRPO_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "groups": wl.groups, "group_size": wl.group_size,
+                   "rollout_lengths": list(wl.lengths), "tokens": inp.logp_new.numel(),
+                   "optimised_tokens": int(inp.action_mask.sum()), "beta": wl.beta,
+                   "kl_mode": wl.kl_mode, "eps_clip": wl.eps_clip, "parallelism": "single GPU"},
+        "tokens_per_s": round(inp.logp_new.numel() / (ms_per_step * 1e-3), 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -339,9 +452,11 @@ def main(argv=None):
               "is described in the design notes but not built.", file=sys.stderr)
         return 2
 
-    from workloads import DECODE_WORKLOADS
+    from workloads import DECODE_WORKLOADS, GRPO_WORKLOADS
     if args.workload in DECODE_WORKLOADS:
         return run_decode(args)
+    if args.workload in GRPO_WORKLOADS:
+        return run_grpo(args)
 
     import torch
 

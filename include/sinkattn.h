@@ -230,6 +230,58 @@ sinkattn_status sinkattn_decode(const sinkattn_decode_problem *problem, const vo
                                 float *lse, void *workspace, size_t workspace_bytes,
                                 void *stream);
 
+/*
+ * GRPO token loss and group-normalised advantage over a packed batch of
+ * rollout groups -- the step after the model in the same trainer (arXiv
+ * 2608.10357, section 4 "Training pipeline", paragraph "Policy update",
+ * eq. 3-7; eq. 3 also on the summary page).  Rollouts g*G .. g*G + G - 1 form
+ * group g (G = group_size, M = num_rollouts / G groups); rollout i holds the
+ * tokens [cu_seqlens[i], cu_seqlens[i + 1]) of the packed [N] arrays.
+ *   A_i  = (R_i - mean_g R) / (std_g R + eps_adv)    std over the group's G
+ *          rewards, population form; 0 where R_i equals the mean       (eq. 3)
+ *   rho  = exp(logp_new - logp_old)                                     (eq. 4)
+ *   J    = min(rho A_i, clip(rho, 1 - eps_clip, 1 + eps_clip) A_i)     (eq. 5, 6)
+ *   kl   = logp_new - logp_ref (kl_mode 0), or exp(r) - r - 1 with
+ *          r = logp_ref - logp_new (kl_mode 1)
+ *   L_g  = (-sum J + beta sum kl) / S_g over the group's optimised tokens
+ *          (action_mask != 0), S_g their number; L_g = 0 if S_g = 0     (eq. 7)
+ *   loss = (1 / M) sum_g L_g
+ * Outputs (device): *loss (fp32); grad [N] fp32 = d loss / d logp_new (0 on
+ * tokens that are not optimised); advantages [B] fp32 (may be NULL).  For the
+ * gradient the clip counts as active -- and the token's J term contributes 0
+ * -- when (A_i > 0 and logp_new - logp_old > log(1 + eps_clip)) or (A_i < 0
+ * and logp_new - logp_old < log(1 - eps_clip)), compared in fp32.
+ * Inputs (device): logp_new, logp_old fp32 [N]; logp_ref fp32 [N], may be
+ * NULL when beta == 0 (then ignored); action_mask uint8 [N], NULL for "every
+ * token optimised"; rewards fp32 [B]; cu_seqlens int32 [B + 1], nondecreasing
+ * from 0 to N (device memory, not checked; offsets outside [0, N] are
+ * clamped, never dereferenced).  Token arrays and grad 16-byte aligned,
+ * rewards / advantages / cu_seqlens / loss 4-byte aligned.  The workspace
+ * (caller-owned device memory of sinkattn_grpo_workspace_size bytes, 256-byte
+ * aligned) holds per-rollout values and per-workgroup partial sums; its
+ * contents on entry do not matter.  The result is deterministic: every
+ * reduction runs in a fixed order.  Validation happens on the host first.
+ */
+typedef struct {
+  int32_t num_rollouts;     /* B >= 0, a multiple of group_size */
+  int32_t group_size;       /* G in [1, 1024] */
+  int32_t total_tokens;     /* N >= 0 (0 when B == 0) */
+  int32_t kl_mode;          /* 0 or 1 */
+  float eps_adv;            /* eps_A >= 0 */
+  float eps_clip;           /* eps_c in [0, 1) */
+  float beta;               /* KL weight, finite */
+} sinkattn_grpo_problem;
+
+/* Bytes of device workspace sinkattn_grpo_loss needs (0 if the problem is invalid). */
+size_t sinkattn_grpo_workspace_size(const sinkattn_grpo_problem *problem);
+
+sinkattn_status sinkattn_grpo_loss(const sinkattn_grpo_problem *problem, const float *logp_new,
+                                   const float *logp_old, const float *logp_ref,
+                                   const uint8_t *action_mask, const float *rewards,
+                                   const int32_t *cu_seqlens, float *loss, float *grad,
+                                   float *advantages, void *workspace, size_t workspace_bytes,
+                                   void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,7 +65,8 @@ def group_advantages(rewards, group_size: int, eps_adv: float) -> np.ndarray:
         sigma = math.sqrt(((r - mu) ** 2).sum() / g)
         # a reward equal to the group mean has advantage 0, also when eps_A = 0 and all G
         # rewards are equal (eq. 3 would be 0 / 0 there; 0 is its limit for eps_A -> 0)
-        adv[m * g:(m + 1) * g] = np.where(r == mu, 0.0, (r - mu) / (sigma + eps_adv))
+        with np.errstate(divide="ignore", invalid="ignore"):
+            adv[m * g:(m + 1) * g] = np.where(r == mu, 0.0, (r - mu) / (sigma + eps_adv))
     return adv
 
 
@@ -124,20 +125,33 @@ def grpo_loss(logp_new, logp_old, logp_ref, action_mask, rewards, cu_seqlens: Se
             continue
         j_sum = 0.0
         kl_sum = 0.0
+        hi, lo = clip_thresholds(eps_clip)
         for i in rolls:
             a = adv[i]
-            for t in range(cu[i], cu[i + 1]):
-                if not mask[t]:
-                    continue
-                rho = math.exp(new[t] - old[t])                         # eq. 4
-                rho_bar = min(max(rho, 1.0 - eps_clip), 1.0 + eps_clip)  # eq. 5
-                j_sum += min(rho * a, rho_bar * a)                      # eq. 6
-                dj = 0.0 if clip_active(new[t], old[t], a, eps_clip) else a * rho
-                dkl = 0.0
-                if beta != 0.0:
-                    kl, dkl = kl_term(new[t], ref[t], kl_mode)
-                    kl_sum += kl
-                grad[t] = (-dj + beta * dkl) / (s_m * n_groups)
+            sl = slice(cu[i], cu[i + 1])
+            on = mask[sl]
+            nw, od = new[sl][on], old[sl][on]
+            rho = np.exp(nw - od)                                       # eq. 4
+            rho_bar = np.clip(rho, 1.0 - eps_clip, 1.0 + eps_clip)      # eq. 5
+            j_sum += np.minimum(rho * a, rho_bar * a).sum()             # eq. 6
+            # clip decision on the fp32 log-ratio (clip_active, elementwise)
+            d = nw.astype(np.float32) - od.astype(np.float32)
+            active = (d > hi) if a > 0 else ((d < lo) if a < 0 else np.zeros(d.shape, bool))
+            dj = np.where(active, 0.0, a * rho)
+            dkl = np.zeros_like(rho)
+            if beta != 0.0:
+                rf = ref[sl][on]
+                if kl_mode == 0:
+                    kl, dkl = nw - rf, np.ones_like(rho)
+                elif kl_mode == 1:
+                    r = rf - nw
+                    kl, dkl = np.exp(r) - r - 1.0, 1.0 - np.exp(r)
+                else:
+                    raise ValueError("kl_mode must be 0 or 1")
+                kl_sum += kl.sum()
+            g_roll = np.zeros(cu[i + 1] - cu[i])
+            g_roll[on] = (-dj + beta * dkl) / (s_m * n_groups)
+            grad[sl] = g_roll
         group_losses[m] = (-j_sum + beta * kl_sum) / s_m                # eq. 7
     loss = group_losses.mean() if n_groups else 0.0
     return loss, grad, adv, group_losses

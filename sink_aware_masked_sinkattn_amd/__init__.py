@@ -1,11 +1,13 @@
-"""Sink-aware masked attention for MI355X (gfx950): forward and backward.
+"""Sink-aware masked attention for MI355X (gfx950): forward, backward, rollout
+decode, and the GRPO token loss of the same trainer.
 
 The computation lives in ``libsinkattn.so`` (hand-written HIP kernels behind
 the C ABI of ``include/sinkattn.h``); this package only binds it.
 """
 from .binding import (BWD_ALL, BWD_DKDV, BWD_DQ, BWD_FINISH, BWD_PREPARE, WINDOW_INF,
-                      DecodeProblem, Problem, SinkAttnError, load_library, make_decode_problem,
-                      make_problem, sinkattn_bwd, sinkattn_bwd_phases,
+                      DecodeProblem, GrpoProblem, Problem, SinkAttnError, load_library,
+                      make_decode_problem, make_grpo_problem, make_problem, sinkattn_bwd,
+                      sinkattn_bwd_phases, sinkattn_grpo_loss, sinkattn_grpo_workspace_size,
                       sinkattn_bwd_workspace_size, sinkattn_decode,
                       sinkattn_decode_workspace_size, sinkattn_fwd, sinkattn_key_tile_segments,
                       sinkattn_tile_class, sinkattn_tile_config)
@@ -16,4 +18,5 @@ __all__ = [
     "sinkattn_fwd", "sinkattn_bwd", "sinkattn_bwd_phases", "sinkattn_bwd_workspace_size",
     "sinkattn_tile_class", "sinkattn_key_tile_segments", "sinkattn_tile_config",
     "DecodeProblem", "make_decode_problem", "sinkattn_decode", "sinkattn_decode_workspace_size",
+    "GrpoProblem", "make_grpo_problem", "sinkattn_grpo_loss", "sinkattn_grpo_workspace_size",
 ]

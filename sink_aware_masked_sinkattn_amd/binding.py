@@ -79,6 +79,18 @@ class DecodeProblem(ctypes.Structure):
     ]
 
 
+class GrpoProblem(ctypes.Structure):
+    _fields_ = [
+        ("num_rollouts", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("total_tokens", ctypes.c_int32),
+        ("kl_mode", ctypes.c_int32),
+        ("eps_adv", ctypes.c_float),
+        ("eps_clip", ctypes.c_float),
+        ("beta", ctypes.c_float),
+    ]
+
+
 _LIB = None
 
 
@@ -115,6 +127,11 @@ def load_library(path: str = LIB_PATH):
     lib.sinkattn_decode_workspace_size.restype = sz
     lib.sinkattn_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sinkattn_decode.restype = ctypes.c_int
+    gp = ctypes.POINTER(GrpoProblem)
+    lib.sinkattn_grpo_workspace_size.argtypes = [gp]
+    lib.sinkattn_grpo_workspace_size.restype = sz
+    lib.sinkattn_grpo_loss.argtypes = [gp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.sinkattn_grpo_loss.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -315,3 +332,59 @@ def sinkattn_decode(q, k_cache, v_cache, cache_seqlens, sinks, window: int, pref
         raise SinkAttnError(st, "sinkattn_decode", lib)
     return out, lse
 
+
+def make_grpo_problem(num_rollouts: int, group_size: int, total_tokens: int, eps_adv: float,
+                      eps_clip: float, beta: float, kl_mode: int = 0) -> GrpoProblem:
+    pb = GrpoProblem()
+    pb.num_rollouts, pb.group_size, pb.total_tokens = int(num_rollouts), int(group_size), \
+        int(total_tokens)
+    pb.kl_mode = int(kl_mode)
+    pb.eps_adv, pb.eps_clip, pb.beta = float(eps_adv), float(eps_clip), float(beta)
+    return pb
+
+
+def sinkattn_grpo_workspace_size(pb: GrpoProblem) -> int:
+    return int(load_library().sinkattn_grpo_workspace_size(ctypes.byref(pb)))
+
+
+def sinkattn_grpo_loss(logp_new, logp_old, logp_ref, action_mask, rewards, cu_seqlens,
+                       group_size: int, eps_adv: float, eps_clip: float, beta: float,
+                       kl_mode: int = 0, loss=None, grad=None, advantages=None, workspace=None,
+                       want_advantages: bool = True):
+    """GRPO token loss (eq. 3-7 of arXiv 2608.10357 section 4): returns (loss [1], grad [N],
+    advantages [B] or None), all fp32 GPU tensors.  logp_ref may be None when beta == 0,
+    action_mask (uint8) None for every token optimised."""
+    lib = load_library()
+    for t, n in ((logp_new, "logp_new"), (logp_old, "logp_old"), (rewards, "rewards"),
+                 (cu_seqlens, "cu_seqlens")):
+        _dev(t, n)
+    if logp_ref is not None:
+        _dev(logp_ref, "logp_ref")
+    if action_mask is not None:
+        _dev(action_mask, "action_mask")
+        if action_mask.dtype != torch.uint8:
+            raise ValueError("action_mask must be uint8")
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    for t, n in ((logp_new, "logp_new"), (logp_old, "logp_old"), (rewards, "rewards")):
+        if t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32")
+    pb = make_grpo_problem(cu_seqlens.numel() - 1, group_size, logp_new.numel(), eps_adv,
+                           eps_clip, beta, kl_mode)
+    dev = logp_new.device
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+    if grad is None:
+        grad = torch.empty_like(logp_new)
+    if advantages is None and want_advantages:
+        advantages = torch.empty(pb.num_rollouts, dtype=torch.float32, device=dev)
+    need = int(lib.sinkattn_grpo_workspace_size(ctypes.byref(pb)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.sinkattn_grpo_loss(ctypes.byref(pb), _ptr(logp_new), _ptr(logp_old), _ptr(logp_ref),
+                                _ptr(action_mask), _ptr(rewards), _ptr(cu_seqlens), _ptr(loss),
+                                _ptr(grad), _ptr(advantages), _ptr(workspace), workspace.numel(),
+                                _stream())
+    if st != 0:
+        raise SinkAttnError(st, "sinkattn_grpo_loss", lib)
+    return loss, grad, advantages

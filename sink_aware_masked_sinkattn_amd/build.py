@@ -19,7 +19,7 @@ OUT = os.path.join(HERE, "libsinkattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "bwd_dq_bf16.hip", "bwd_aux.hip",
-           "decode_bf16.hip",
+           "decode_bf16.hip", "grpo.hip",
            "fp32_kernels.hip"]
 
 ARCH = "gfx950"

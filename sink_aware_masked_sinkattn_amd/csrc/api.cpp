@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <cmath>
 #include <cstdint>
 
 #include "../../include/sinkattn.h"
@@ -54,6 +55,12 @@ int fwd_key_tile(int window);
 int dkdv_query_tile(int window);
 bool dq_clears_dkdv_accumulators();
 hipError_t launch_zero_f32_vec(float* p, long long n, hipStream_t stream);
+hipError_t launch_grpo(const float* logp_new, const float* logp_old, const float* logp_ref,
+                       const uint8_t* mask, const float* rewards, const int32_t* cu_seqlens,
+                       float* loss, float* grad, float* advantages, void* workspace,
+                       int num_rollouts, int group_size, int total_tokens, int kl_mode,
+                       float eps_adv, float eps_clip, float beta, hipStream_t stream);
+size_t grpo_workspace_bytes(int num_rollouts, int total_tokens);
 
 namespace {
 
@@ -344,6 +351,61 @@ sinkattn_status sinkattn_decode(const sinkattn_decode_problem* pb, const void* q
       (const bf16*)q, (const bf16*)k_cache, (const bf16*)v_cache, cache_seqlens, sinks, (bf16*)o,
       lse, (float*)workspace, pb->batch, pb->cache_capacity, pb->heads_q, pb->heads_kv, window,
       prefix, pb->softmax_scale, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+sinkattn_status check_grpo(const sinkattn_grpo_problem* pb) {
+  if (!pb) return SINKATTN_ERR_NULL_POINTER;
+  if (pb->num_rollouts < 0 || pb->total_tokens < 0 || pb->group_size < 1 ||
+      pb->group_size > 1024 || pb->num_rollouts % pb->group_size != 0 ||
+      (pb->num_rollouts == 0 && pb->total_tokens != 0) || (pb->kl_mode != 0 && pb->kl_mode != 1))
+    return SINKATTN_ERR_BAD_SHAPE;
+  if (!(pb->eps_adv >= 0.0f) || !std::isfinite(pb->eps_adv) || !(pb->eps_clip >= 0.0f) ||
+      !(pb->eps_clip < 1.0f) || !std::isfinite(pb->beta))
+    return SINKATTN_ERR_BAD_SHAPE;
+  return SINKATTN_OK;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t sinkattn_grpo_workspace_size(const sinkattn_grpo_problem* pb) {
+  if (check_grpo(pb) != SINKATTN_OK) return 0;
+  return round_up(grpo_workspace_bytes(pb->num_rollouts, pb->total_tokens));
+}
+
+sinkattn_status sinkattn_grpo_loss(const sinkattn_grpo_problem* pb, const float* logp_new,
+                                   const float* logp_old, const float* logp_ref,
+                                   const uint8_t* action_mask, const float* rewards,
+                                   const int32_t* cu_seqlens, float* loss, float* grad,
+                                   float* advantages, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  const sinkattn_status st = check_grpo(pb);
+  if (st != SINKATTN_OK) return st;
+  const bool tokens = pb->total_tokens > 0;
+  const bool rolls = pb->num_rollouts > 0;
+  if (!loss || !cu_seqlens || (tokens && (!logp_new || !logp_old || !grad)) ||
+      (rolls && !rewards) || (tokens && pb->beta != 0.0f && !logp_ref))
+    return SINKATTN_ERR_NULL_POINTER;
+  if ((tokens && (!aligned16(logp_new) || !aligned16(logp_old) || !aligned16(grad) ||
+                  (pb->beta != 0.0f && !aligned16(logp_ref)) ||
+                  (action_mask && !aligned16(action_mask)))) ||
+      (rolls && !aligned4(rewards)) || (advantages && !aligned4(advantages)) ||
+      !aligned4(cu_seqlens) || !aligned4(loss))
+    return SINKATTN_ERR_MISALIGNED;
+  const size_t need = grpo_workspace_bytes(pb->num_rollouts, pb->total_tokens);
+  if (!workspace || workspace_bytes < need) return SINKATTN_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SINKATTN_ERR_MISALIGNED;
+  return hip_status(launch_grpo(logp_new, logp_old, logp_ref, action_mask, rewards, cu_seqlens,
+                                loss, grad, advantages, workspace, pb->num_rollouts,
+                                pb->group_size, pb->total_tokens, pb->kl_mode, pb->eps_adv,
+                                pb->eps_clip, pb->beta, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

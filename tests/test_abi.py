@@ -210,3 +210,56 @@ def test_decode_pointer_and_workspace_checks():
     big = _lib().sinkattn_decode_workspace_size(ctypes.byref(_dproblem(batch=8, cache_capacity=8192,
                                                                       window=2**31 - 1, prefix=0)))
     assert big >= need
+
+
+def _gproblem(**kw):
+    d = dict(num_rollouts=16, group_size=8, total_tokens=1000, kl_mode=0, eps_adv=1e-6,
+             eps_clip=0.2, beta=0.04)
+    d.update(kw)
+    return binding.make_grpo_problem(d["num_rollouts"], d["group_size"], d["total_tokens"],
+                                     d["eps_adv"], d["eps_clip"], d["beta"], d["kl_mode"])
+
+
+def _grpo(pb, ws=A, ws_bytes=1 << 40, **ptrs):
+    p = {n: ptrs.get(n, A) for n in ("new", "old", "ref", "mask", "rew", "cu", "loss", "grad",
+                                      "adv")}
+    return _lib().sinkattn_grpo_loss(ctypes.byref(pb), p["new"], p["old"], p["ref"], p["mask"],
+                                     p["rew"], p["cu"], p["loss"], p["grad"], p["adv"], ws,
+                                     ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(num_rollouts=-8), dict(total_tokens=-1), dict(group_size=0), dict(group_size=1025,
+                                                                           num_rollouts=1025),
+    dict(num_rollouts=12),                      # not a multiple of the group size
+    dict(num_rollouts=0, total_tokens=5),       # tokens without rollouts
+    dict(kl_mode=2), dict(eps_adv=-1.0), dict(eps_adv=float("nan")), dict(eps_clip=1.0),
+    dict(eps_clip=-0.1), dict(beta=float("inf")),
+])
+def test_grpo_invalid_problem_rejected(kw):
+    pb = _gproblem(**kw)
+    assert _grpo(pb) == 2
+    assert _lib().sinkattn_grpo_workspace_size(ctypes.byref(pb)) == 0
+
+
+def test_grpo_pointer_and_workspace_checks():
+    pb = _gproblem()
+    need = _lib().sinkattn_grpo_workspace_size(ctypes.byref(pb))
+    assert need > 0 and need % 256 == 0
+    assert _lib().sinkattn_grpo_loss(None, A, A, A, A, A, A, A, A, A, A, need, None) == 1
+    for name in ("new", "old", "rew", "cu", "loss", "grad", "ref"):
+        assert _grpo(pb, **{name: None}) == 1, name
+    # no reference log-probs needed without a KL term
+    pb0 = _gproblem(beta=0.0)
+    assert _grpo(pb0, ref=None, ws=None) == 6
+    for name in ("new", "old", "grad", "ref", "mask"):
+        assert _grpo(pb, **{name: A + 4}) == 5, name
+    for name in ("rew", "cu", "loss", "adv"):
+        assert _grpo(pb, **{name: A + 2}) == 5, name
+    assert _grpo(pb, ws=None) == 6
+    assert _grpo(pb, ws_bytes=need - 1) == 6
+    assert _grpo(pb, ws=A + 64, ws_bytes=need) == 5
+    # the workspace grows with the rollouts and the tokens
+    big = _lib().sinkattn_grpo_workspace_size(ctypes.byref(_gproblem(num_rollouts=4096,
+                                                                     total_tokens=1 << 24)))
+    assert big > need

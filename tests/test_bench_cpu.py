@@ -84,3 +84,11 @@ def test_committed_sclk_parses_summary(tmp_path, monkeypatch):
     assert bench.committed_sclk("kern_a", "wl") == 1.81     # the longest grid of the kernel
     assert bench.committed_sclk("kern_c", "wl") is None
     assert bench.committed_sclk("kern_a", "other") is None
+
+
+def test_grpo_compulsory_bytes():
+    from workloads import make_grpo_inputs
+    inp = make_grpo_inputs(lengths=(10, 20, 30, 40), group_size=2, seed=1, beta=0.04)
+    assert bench.grpo_bytes(inp) == 100 * (4 + 4 + 4 + 1 + 4) + 4 * 12 + 8
+    inp0 = make_grpo_inputs(lengths=(10, 20), group_size=2, seed=1, beta=0.0)
+    assert bench.grpo_bytes(inp0) == 30 * 13 + 2 * 12 + 8
