@@ -132,17 +132,26 @@ __device__ __forceinline__ void tile_step(uint32_t qtile, const float* l2s,
     // is key k: q - k = base + 8*(i/4) + i%4
     const int base = sa_opaque(q0 + qb * 32 + 4 * g - k);
     __builtin_amdgcn_sched_barrier(0);
-    f32x16 st = {};
+    // L and -D of the block's rows first: LDS reads complete in issue order, so
+    // the dP chain (which starts from -D) then waits only for these, not for
+    // the transpose reads issued after them; the counter tracks at most 15
+    // reads, so the S chain's own operands must not sit behind more than that
     f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      d4[j] = *(const f32x4*)(dds + qb * 32 + 8 * j + 4 * g);
+      l4[j] = *(const f32x4*)(l2s + qb * 32 + 8 * j + 4 * g);
+    }
+    sa_mem_fence();
+    f32x16 st = {};
     bf16x8 dob[2][2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       st = mfma32x32x16(qa[j], kf[0][j], st);
-      l4[j] = *(const f32x4*)(l2s + qb * 32 + 8 * j + 4 * g);
-      d4[j] = *(const f32x4*)(dds + qb * 32 + 8 * j + 4 * g);
+      asm volatile("" : "+v"(st));   // keep the MFMA in this slot
       dob[j >> 1][j & 1] = read_tr(DOFF, qb, j >> 1, j & 1);
+      sa_mem_fence();
     }
-    __builtin_amdgcn_sched_barrier(0);
     // P' = exp2(S*scale*log2e - L*log2e), a quarter after each dP MFMA.  The
     // dP chain accumulates onto -D of each element's row, so it yields dP - D.
     f32x16 dp;

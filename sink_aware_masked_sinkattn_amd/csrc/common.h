@@ -103,6 +103,15 @@ __device__ __forceinline__ float sa_pin(float v) {
   return v;
 }
 
+// Scheduling fence that memory operations also respect: sched_barrier alone
+// acts in the machine scheduler only, after instruction selection may already
+// have moved side-effect-free LDS loads across it; the empty asm with a
+// memory clobber keeps them on their side (and emits no instruction).
+__device__ __forceinline__ void sa_mem_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Mask one lane's 16 C-layout elements of a 32-key block when the lane holds
 // one query and element i holds key kr + c_i, c_i = 8*(i/4) + i%4, so that
 // q - k = base - c_i.  Hidden elements become -inf.  GENERAL: the block may
