@@ -296,7 +296,7 @@ def run_decode(args) -> int:
     achieved = runs[dom]["bytes"] / (per_layer[dom]["ms"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "sinkattn_decode_split_bf16_d64 + sinkattn_decode_combine_bf16_d64 "
+                "kernel": "sinkattn_decode_stream_bf16_d64 + sinkattn_decode_combine_bf16_d64 "
                           f"(one sinkattn_decode call, layer {dom})",
                 "avg_launch_ms": per_layer[dom]["ms"],
                 "algorithmic_bytes_per_launch": runs[dom]["bytes"]}

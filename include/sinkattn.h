@@ -207,7 +207,7 @@ sinkattn_status sinkattn_tile_config(const sinkattn_problem *problem, int32_t *o
  * lse fp32 [batch, heads_q] (content-only log-sum-exp, natural log; may be
  * NULL).  heads_q / heads_kv must be at most 16.  The workspace (caller-owned
  * device memory of sinkattn_decode_workspace_size bytes, 256-byte aligned)
- * holds the per-split partial results; its contents on entry do not matter.
+ * holds per-block partial results; its contents on entry do not matter.
  * Validation happens on the host before any HIP call, as for sinkattn_fwd.
  */
 typedef struct {
