@@ -70,7 +70,7 @@ extern "C" {
 typedef enum {
   SINKATTN_OK = 0,
   SINKATTN_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
-  SINKATTN_ERR_BAD_SHAPE = 2,    /* negative size, Hq % Hkv != 0, N < 0 ... */
+  SINKATTN_ERR_BAD_SHAPE = 2,    /* negative size, Hq % Hkv != 0, N < 0, Hq * d > 2^24 ... */
   SINKATTN_ERR_BAD_MASK = 3,     /* window < 0 or prefix < 0 */
   SINKATTN_ERR_UNSUPPORTED = 4,  /* dtype / head_dim combination not built */
   SINKATTN_ERR_MISALIGNED = 5,   /* a tensor pointer is not 16-byte aligned */

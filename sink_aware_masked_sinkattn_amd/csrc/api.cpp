@@ -96,9 +96,10 @@ sinkattn_status check_problem(const sinkattn_problem* pb, Dims* dims) {
   } else {
     dims->rows = (long long)pb->batch * pb->seqlen;
   }
-  // 32-bit element offsets are used for row * stride products inside kernels
-  // only after widening to size_t; the per-row element count must fit int.
-  if ((long long)pb->heads_q * pb->head_dim > (1LL << 30)) return SINKATTN_ERR_BAD_SHAPE;
+  // Row * stride products inside kernels are widened to size_t, but a tile
+  // copy's lane offset (up to 8 rows of the row stride, in bytes) is 32-bit:
+  // heads * head_dim * 2 bytes * 8 rows must stay below 2^31.
+  if ((long long)pb->heads_q * pb->head_dim > (1LL << 24)) return SINKATTN_ERR_BAD_SHAPE;
   if (dims->rows > (1LL << 31) - 1) return SINKATTN_ERR_BAD_SHAPE;
   return SINKATTN_OK;
 }
@@ -134,7 +135,8 @@ sinkattn_status check_decode(const sinkattn_decode_problem* pb) {
   if (pb->head_dim != 64 || pb->heads_q / pb->heads_kv > 16) return SINKATTN_ERR_UNSUPPORTED;
   if (!(pb->softmax_scale > 0.0f) || pb->softmax_scale > 1.0e30f) return SINKATTN_ERR_BAD_SHAPE;
   if ((long long)pb->batch * pb->cache_capacity > (1LL << 31) - 1) return SINKATTN_ERR_BAD_SHAPE;
-  if ((long long)pb->heads_q * pb->head_dim > (1LL << 30)) return SINKATTN_ERR_BAD_SHAPE;
+  // as for the training problem: 8 cache rows of one sequence in bytes fit 2^31
+  if ((long long)pb->heads_q * pb->head_dim > (1LL << 24)) return SINKATTN_ERR_BAD_SHAPE;
   return SINKATTN_OK;
 }
 

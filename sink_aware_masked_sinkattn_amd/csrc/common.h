@@ -201,33 +201,28 @@ __device__ __forceinline__ bf16x4 lds_read_tr4_at(uint32_t a) {
 }
 
 // Copy a ROWS x 64 bf16 tile from global memory straight into a swizzled LDS
-// tile (global_load_lds_dwordx4: lane i's 16 bytes land at lds_ptr + 16*i, so
-// one instruction fills 8 rows; no VGPRs are used for the data).  Lane i of
-// an 8-row block fetches the global chunk that belongs at physical chunk i%8
-// of row i/8.  Rows at or past `nvalid` repeat row nvalid-1 (nvalid >= 1):
-// callers mask those rows out of every result.  Completion is tracked by
-// vmcnt: s_waitcnt vmcnt(0) before the barrier that publishes the tile.
-template <int ROWS, int WAVES>
-__device__ __forceinline__ void tile_load_lds(bf16* lds_tile, const bf16* gbase, size_t row_stride,
-                                              int nvalid, int wave, int lane) {
-  constexpr int PER_WAVE = ROWS / (8 * WAVES);
-  static_assert(PER_WAVE * 8 * WAVES == ROWS, "tile rows must split into 8-row blocks per wave");
-#pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
-    const int blk = wave * PER_WAVE + j;
-    const int r = blk * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ tile_swz(r);
-    const int rr = r < nvalid ? r : nvalid - 1;
-    __builtin_amdgcn_global_load_lds((const void*)(gbase + (size_t)rr * row_stride + c * 8),
-                                     (lds_void*)(lds_tile + blk * 512), 16, 0, 0);
-  }
-}
-
-// Lane constants of the same copy with the address split in two (checked
-// against tile_load_lds on the host for every lane, block and row count):
-// lane i of an 8-row block reads tile row i/8 of the block; its chunk offset
-// for an even block is 16 * ((i%8) ^ tile_swz(i/8)), for an odd block that
-// XOR 32 (the swizzle of a row r + 8 is that of r XOR 2).
+// tile with buffer_load_dwordx4 ... lds (lane i's 16 bytes land at the
+// block's LDS address + 16 i, so one instruction fills 8 rows; no VGPRs hold
+// the data).  Lane i of an 8-row block reads tile row i/8 of the block and
+// fetches the global chunk that belongs at physical chunk i%8 of that row.
+// Rows at or past `nvalid` repeat row nvalid-1 (nvalid >= 1): callers mask
+// those rows out of every result.  Completion is tracked by vmcnt:
+// s_waitcnt vmcnt(0) before the barrier that publishes the tile.
+//
+// The address is split in two: a uniform part (tile base plus the block's
+// first row, clamped to the last valid row) in the buffer descriptor, and a
+// 32-bit lane offset (the lane's row, clamped the same way, plus its chunk).
+// Lane constants (checked against the per-lane formula on the host for every
+// lane, block and row count): the chunk offset for an even block is
+// 16 * ((i%8) ^ tile_swz(i/8)), for an odd block that XOR 32 (the swizzle of
+// a row r + 8 is that of r XOR 2).
+//
+// The buffer form rather than global_load_lds: the compiler takes a pending
+// global_load_lds for a flat access to both memories and then makes every
+// later wait a wait for all loads (vmcnt(0), lgkmcnt(0)); with the buffer
+// form it keeps per-instruction counts, so LDS reads of the other tile
+// overlap the MFMAs that consume them.  The descriptor covers every byte
+// (num_records 2^32 - 1; offsets stay within 8 rows).
 struct TileLane {
   int row_off;     // (lane / 8) * row_bytes
   int chunk_off;   // 16 * ((lane % 8) ^ tile_swz(lane / 8))
@@ -238,11 +233,6 @@ __device__ __forceinline__ TileLane tile_lane(int lane, int row_bytes) {
   t.chunk_off = ((lane & 7) ^ tile_swz(lane >> 3)) << 4;
   return t;
 }
-// tile_load_lds with the global address as a uniform part (tile base plus
-// the block's first row, clamped to the last valid row: scalar registers)
-// and a 32-bit lane offset (the lane's row, clamped the same way, plus its
-// chunk): two VALU instructions per 8-row block.  row_bytes is the global
-// row stride in bytes; the same rows-past-nvalid rule as tile_load_lds.
 template <int ROWS, int WAVES>
 __device__ __forceinline__ void tile_load_lds_lane(bf16* lds_tile, const bf16* gbase, int row_bytes,
                                                    int nvalid, int wave, const TileLane& tl) {
@@ -255,8 +245,9 @@ __device__ __forceinline__ void tile_load_lds_lane(bf16* lds_tile, const bf16* g
     const int r0 = min(blk * 8, nvalid - 1);
     const int lim = max(nvalid - 1 - blk * 8, 0) * row_bytes;
     const uint32_t off = (uint32_t)(min(tl.row_off, lim) + (tl.chunk_off ^ ((blk & 1) << 5)));
-    __builtin_amdgcn_global_load_lds((const void*)((const char*)gbase + (size_t)r0 * row_bytes + off),
-                                     (lds_void*)(lds_tile + blk * 512), 16, 0, 0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const char*)gbase + (size_t)r0 * row_bytes), (short)0, -1, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_tile + blk * 512), 16, off, 0, 0, 0);
   }
 }
 

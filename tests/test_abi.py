@@ -82,6 +82,7 @@ def _bwd(pb, ws=A, ws_bytes=1 << 40, **ptrs):
     (dict(head_dim=128), 4),
     (dict(dtype=7), 4),
     (dict(dtype=binding.SINKATTN_FP32, head_dim=48), 4),
+    (dict(heads_q=(1 << 18) + 16, heads_kv=16), 2),   # Hq * d > 2^24
 ])
 def test_invalid_problem_rejected(kw, code):
     pb = _problem(**kw)
@@ -183,6 +184,7 @@ def _decode(pb, ws=A, ws_bytes=1 << 40, **ptrs):
     (dict(prefix=-1), 3),
     (dict(head_dim=128), 4),
     (dict(heads_q=32, heads_kv=1), 4),     # more than 16 query heads per kv head
+    (dict(heads_q=(1 << 18) + 16, heads_kv=(1 << 14) + 1), 2),   # Hq * d > 2^24
 ])
 def test_decode_invalid_problem_rejected(kw, code):
     pb = _dproblem(**kw)
