@@ -16,7 +16,10 @@
 // the sink scaling costs one extra exponential per row in the epilogue.
 //
 // Work decomposition (one workgroup = WAVES waves x QB*32 query rows of one
-// head; by default 4 waves x 32 rows, 3 waves per SIMD):
+// head; by default 4 waves x 32 rows, 3 waves per SIMD -- or, for windows
+// under 1024 with GQA groups of a multiple of 4, four query heads of one kv
+// group x the same 32 rows, so the workgroup loads the key tiles of 32 rows
+// (w/32 + 2 tiles) once for four heads and every wave uses every tile):
 //   * each wave owns QB 32-row MFMA blocks of query rows whose Q fragments
 //     stay in registers for the whole kernel; each key tile's K and V^T
 //     operands are read from LDS once, up front, and shared by the blocks;
@@ -197,28 +200,36 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
 #ifndef SA_FWD_OCC
 #define SA_FWD_OCC 3   // waves per SIMD the register budget is set for
 #endif
-template <int NKB>
+// HW: waves along heads.  HW = 1: the workgroup's waves take consecutive
+// row blocks of one head.  HW = 4 (short windows, GQA groups of a multiple
+// of 4): they take four query heads of one kv group on the same rows, so the
+// workgroup's key tiles are those of QB*32 rows only and every wave uses
+// every tile (the K/V tiles are shared by the four heads).
+template <int NKB, int HW>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   using T = FwdTiles<NKB>;
   constexpr int BK = T::BK;
   constexpr int TILE_ELEMS = T::TILE_ELEMS;
+  static_assert(WAVES % HW == 0, "the waves split into HW heads x row blocks");
+  constexpr int BQW = (WAVES / HW) * QB * 32;   // query rows per workgroup
   __shared__ __attribute__((aligned(128))) bf16 smem[T::SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
-
-  const int h = map_head(blockIdx.x, a.heads_q);
-  const int z = blockIdx.y;
-  const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
-  const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
-  const int q_start = qt * BQ;
-  if (q_start >= sv.len) return;
-  const int q_last = min(q_start + BQ - 1, sv.len - 1);
-  const int kvh = h / a.group;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  const int qw0 = q_start + wave * (QB * 32);
+  const int h = HW == 1 ? map_head(blockIdx.x, a.heads_q)
+                        : map_head(blockIdx.x, a.heads_q / HW) * HW + (wave % HW);
+  const int z = blockIdx.y;
+  const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
+  const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
+  const int q_start = qt * BQW;
+  if (q_start >= sv.len) return;
+  const int q_last = min(q_start + BQW - 1, sv.len - 1);
+  const int kvh = h / a.group;
+
+  const int qw0 = q_start + (wave / HW) * (QB * 32);
   const bool wave_active = qw0 < sv.len;
   const int qw1 = min(qw0 + QB * 32 - 1, sv.len - 1);
 
@@ -333,13 +344,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 }
 
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC, SA_FWD_OCC))) void sinkattn_fwd_bf16_d64(FwdArgs a) {
-  fwd_body<2>(a);
+  fwd_body<2, 1>(a);
 }
 #ifndef SA_FWD_OCC_K32
 #define SA_FWD_OCC_K32 4
 #endif
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC_K32, SA_FWD_OCC_K32))) void sinkattn_fwd_bf16_d64_k32(FwdArgs a) {
-  fwd_body<1>(a);
+  fwd_body<1, 1>(a);
+}
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC_K32, SA_FWD_OCC_K32))) void sinkattn_fwd_bf16_d64_k32h(FwdArgs a) {
+  fwd_body<1, 4>(a);
 }
 
 }  // namespace
@@ -360,11 +374,16 @@ hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, cons
   a.group = heads_q / heads_kv;
   a.window = window; a.prefix = prefix;
   a.lse_head_stride = cu_seqlens ? total_tokens : seqlen;
-  a.num_q_tiles = (seqlen + BQ - 1) / BQ;
   a.scale_log2 = scale * SA_LOG2E;
-  if (a.num_q_tiles == 0 || batch == 0 || heads_q == 0) return hipSuccess;
-  dim3 grid(heads_q, batch, a.num_q_tiles);
-  if (fwd_key_tile(window) == 32)
+  if (seqlen == 0 || batch == 0 || heads_q == 0) return hipSuccess;
+  // short windows with GQA groups of a multiple of 4: four heads per workgroup
+  const bool heads4 = fwd_key_tile(window) == 32 && a.group % 4 == 0;
+  const int rows = heads4 ? QB * 32 : BQ;
+  a.num_q_tiles = (seqlen + rows - 1) / rows;
+  dim3 grid(heads4 ? heads_q / 4 : heads_q, batch, a.num_q_tiles);
+  if (heads4)
+    hipLaunchKernelGGL(sinkattn_fwd_bf16_d64_k32h, grid, dim3(WAVES * 64), 0, stream, a);
+  else if (fwd_key_tile(window) == 32)
     hipLaunchKernelGGL(sinkattn_fwd_bf16_d64_k32, grid, dim3(WAVES * 64), 0, stream, a);
   else
     hipLaunchKernelGGL(sinkattn_fwd_bf16_d64, grid, dim3(WAVES * 64), 0, stream, a);

@@ -31,6 +31,7 @@ SMALL = [
     (1, 64, 2, 1, 16, 4, 1.0),
     (3, 129, 16, 2, 31, 2, 0.5),
     (1, 1, 2, 1, 0, 0, 1.0),
+    (2, 97, 8, 1, 0, 3, 1.0),      # four heads per forward workgroup, diagonal plus prefix
     # windows >= 1024 after clamping run the wide-tile kernels (64-key forward /
     # dQ tiles, 128-row dK/dV tiles); shorter ones the narrow-tile kernels
     (1, 1100, 4, 2, WINDOW_INF, 0, 0.5),
