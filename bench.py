@@ -52,19 +52,22 @@ KERNEL_FLOP_PER_PAIR = {"sinkattn_fwd_bf16_d64": 4, "sinkattn_bwd_dkdv_bf16_d64"
                         "sinkattn_bwd_dq_bf16_d64": 2}
 
 
-def kernel_variants(key_tile: int, query_tile: int) -> dict:
+def kernel_variants(key_tile: int, query_tile: int, group: int = 1) -> dict:
     """Names of the kernels one layer launches, per timed phase, for the tile
-    shapes the library reports (narrow tiles carry a suffix)."""
+    shapes the library reports (narrow tiles carry a suffix; the narrow
+    forward takes four query heads per workgroup when the GQA group size is a
+    multiple of 4, suffix _k32h)."""
     if query_tile != 128:
         raise ValueError(f"no dK/dV kernel with {query_tile}-row query tiles")
     k32 = "_k32" if key_tile == 32 else ""
-    return {"fwd_ms": "sinkattn_fwd_bf16_d64" + k32,
+    fwd = "_k32h" if key_tile == 32 and group % 4 == 0 else k32
+    return {"fwd_ms": "sinkattn_fwd_bf16_d64" + fwd,
             "bwd_dkdv_ms": "sinkattn_bwd_dkdv_bf16_d64",
             "bwd_dq_ms": "sinkattn_bwd_dq_bf16_d64" + k32}
 
 
 def kernel_base(name: str) -> str:
-    for suffix in ("_k32",):
+    for suffix in ("_k32h", "_k32"):
         if name.endswith(suffix):
             return name[:-len(suffix)]
     return name
@@ -497,7 +500,7 @@ def main(argv=None):
                       torch.empty_like(r["v"]), torch.empty_like(r["s"]))
         r["ws"] = torch.empty(sinkattn_bwd_workspace_size(pb), dtype=torch.uint8, device=dev)
         r["pairs"] = useful_pairs(inp)
-        r["kernels"] = kernel_variants(*sinkattn_tile_config(pb))
+        r["kernels"] = kernel_variants(*sinkattn_tile_config(pb), pb.heads_q // pb.heads_kv)
     torch.cuda.synchronize()
 
     def step(events=None):

@@ -270,7 +270,7 @@ __device__ __forceinline__ void single_unit(const DecArgs& a, DecSmem& sm, int b
     return;
   }
 
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 15;       // MFMA column: query head within the group
   const int grp = lane >> 4;       // 16-lane group
@@ -358,8 +358,10 @@ void sinkattn_decode_single_bf16_d64(DecArgs a) {
       const int mid = (lo + hi) >> 1;
       if (sm.ustart[mid] <= local) lo = mid; else hi = mid;
     }
-    const int within = local - sm.ustart[lo];
-    single_unit(a, sm, b_lo + lo, within);
+    // uniform by construction; readfirstlane lets the compiler keep the copy
+    // descriptors in scalar registers
+    const int within = __builtin_amdgcn_readfirstlane(local - sm.ustart[lo]);
+    single_unit(a, sm, __builtin_amdgcn_readfirstlane(b_lo + lo), within);
   }
 }
 

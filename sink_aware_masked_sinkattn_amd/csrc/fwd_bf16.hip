@@ -219,15 +219,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  const int h = HW == 1 ? map_head(blockIdx.x, a.heads_q)
-                        : map_head(blockIdx.x, a.heads_q / HW) * HW + (wave % HW);
+  // h0: the workgroup's first head (uniform); the HW heads share its kv head
+  const int h0 = HW == 1 ? map_head(blockIdx.x, a.heads_q) : map_head(blockIdx.x, a.heads_q / HW) * HW;
+  const int h = h0 + (HW == 1 ? 0 : wave % HW);
   const int z = blockIdx.y;
   const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
   const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
   const int q_start = qt * BQW;
   if (q_start >= sv.len) return;
   const int q_last = min(q_start + BQW - 1, sv.len - 1);
-  const int kvh = h / a.group;
+  const int kvh = h0 / a.group;
 
   const int qw0 = q_start + (wave / HW) * (QB * 32);
   const bool wave_active = qw0 < sv.len;

@@ -40,11 +40,16 @@ def test_kernel_variant_names():
     import bench
     wide = bench.kernel_variants(64, 128)
     narrow = bench.kernel_variants(32, 128)
+    heads4 = bench.kernel_variants(32, 128, 8)
     assert wide == {"fwd_ms": "sinkattn_fwd_bf16_d64", "bwd_dkdv_ms": "sinkattn_bwd_dkdv_bf16_d64",
                     "bwd_dq_ms": "sinkattn_bwd_dq_bf16_d64"}
-    for ph, name in narrow.items():
-        assert bench.kernel_base(name) == wide[ph]
-        assert bench.kernel_source_sha(name) == bench.kernel_source_sha(wide[ph])
+    assert narrow["fwd_ms"] == "sinkattn_fwd_bf16_d64_k32"
+    assert heads4["fwd_ms"] == "sinkattn_fwd_bf16_d64_k32h"
+    assert bench.kernel_variants(64, 128, 8) == wide
+    for variants in (narrow, heads4):
+        for ph, name in variants.items():
+            assert bench.kernel_base(name) == wide[ph]
+            assert bench.kernel_source_sha(name) == bench.kernel_source_sha(wide[ph])
 
 
 def test_decode_visible_count():
