@@ -17,9 +17,10 @@
 //   S^T = K Q^T and dP^T = V dO^T with one query per lane (C layout); Q and
 //   dO fragments stay in registers as the B operand; K and V tiles come
 //   from LDS as the A operand.  L and D are then per-lane scalars.  The C
-//   layout of dS^T (lane = query, 16 keys in registers) is exactly the A
-//   operand of dQ = dS K; the B operand (keys along k) is a transpose read
-//   of the row-major K tile.
+//   layout of dS^T (lane = query, 16 keys in registers) is exactly the B
+//   operand of dQ^T = K^T dS^T; the A operand (keys along k) is a transpose
+//   read of the row-major K tile.  dQ^T's C layout gives each lane runs of 4
+//   consecutive head dims of its query, stored 8 bytes at a time.
 #include "common.h"
 #include "mask_tiles.h"
 
@@ -116,7 +117,7 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
       vf[s] = lds_read8((ra ^ (32 * s)) + kb * 4096 + VOFF);
     }
   };
-  // B operand of dQ += dS K (keys on k, head dim on n): transpose reads of
+  // A operand of dQ^T += K^T dS^T (head dim on m, keys on k): transpose reads of
   // rows kb*32 + 16*hh + 4g + li/4 (+8), columns db*32 + 16*(grp&1) + 4*(li&3)
   bf16x8 kt[2][2];   // [hh][db]
   auto read_kt = [&](int kb) {
@@ -165,7 +166,8 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
         __builtin_amdgcn_sched_barrier(0);
       }
       if (next_kb) read_kv(kb + 1);   // this block's K and V operands are dead
-      // dS = P' (dP - D); dQ += dS K, one half of dS at a time
+      // dS = P' (dP - D); dQ^T += K^T dS^T, one half of dS at a time (dS^T in
+      // the C layout of S^T is already the B operand: keys on k, query on n)
       bf16x8 dsb[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -175,7 +177,7 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
         dsb[hh] = to_bf16x8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int db = 0; db < 2; ++db) acc[qb][db] = mfma32x32x16(dsb[hh], kt[hh][db], acc[qb][db]);
+        for (int db = 0; db < 2; ++db) acc[qb][db] = mfma32x32x16(kt[hh][db], dsb[hh], acc[qb][db]);
       }
       if (next_kb) read_kt(kb + 1);
     }
@@ -254,6 +256,7 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   bf16x8 qf[QB][4], df[QB][4];
   float l2[QB], dd[QB];
   const float sink = a.sinks[h];
+  const float sink2 = sink * SA_LOG2E;
   float ds_part = 0.0f;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -266,18 +269,25 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
       qf[qb][s] = ok ? *(const bf16x8*)(a.q + off) : bf16x8{};
       df[qb][s] = ok ? *(const bf16x8*)(a.dout + off) : bf16x8{};
       const bf16x8 of = ok ? *(const bf16x8*)(a.o + off) : bf16x8{};
+      // bf16 products are exact in fp32: v_dot2_f32_bf16 changes only the
+      // rounding order of the sum
 #pragma unroll
-      for (int j = 0; j < 8; ++j) dot += (float)of[j] * (float)df[qb][s][j];
+      for (int j = 0; j < 8; j += 2)
+        dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{of[j], of[j + 1]},
+                                              bf16x2{df[qb][s][j], df[qb][s][j + 1]}, dot, false);
     }
     dot = halves_sum(dot);
-    const float l = ok ? a.lse[sv.lse_base + (size_t)h * a.lse_head_stride + row] : 0.0f;
-    const float big_l = (sink == -INFINITY) ? l : fmaxf(l, sink) + log1pf(expf(-fabsf(l - sink)));
-    l2[qb] = ok ? big_l * SA_LOG2E : INFINITY;
+    // log2 units: L2 = log2(2^l2 + 2^s2) = max + log2(1 + 2^-|l2 - s2|)
+    const float lv2 = (ok ? a.lse[sv.lse_base + (size_t)h * a.lse_head_stride + row] : 0.0f) * SA_LOG2E;
+    const float big_l2 = (sink == -INFINITY)
+                             ? lv2
+                             : fmaxf(lv2, sink2) + fast_log2(1.0f + fast_exp2(-fabsf(lv2 - sink2)));
+    l2[qb] = ok ? big_l2 : INFINITY;
     dd[qb] = ok ? dot : 0.0f;
-    if (ok && g == 0) ds_part -= expf(sink - big_l) * dot;
+    if (ok && g == 0) ds_part -= fast_exp2(sink2 - big_l2) * dot;
   }
 
-  f32x16 acc[QB][2];   // dQ: C layout [m = query][n = d], lane = d
+  f32x16 acc[QB][2];   // dQ^T: C layout [m = d][n = query], lane = query
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) acc[qb][0] = acc[qb][1] = f32x16{};
 
@@ -301,17 +311,21 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
     __syncthreads();
   }
 
-  // ---- dQ = scale * acc, C layout rows = queries qb*32 + 8*(i/4) + 4g + i%4,
-  // column d = db*32 + l32.  Stage through LDS for row-contiguous stores.
+  // ---- dQ = scale * acc.  acc holds dQ^T: C layout rows = head dims
+  // db*32 + 8*(i/4) + 4g + i%4, column = query qb*32 + l32, so each lane
+  // holds runs of 4 consecutive head dims of its query.  Stage through LDS
+  // for row-contiguous stores.
   bf16* os = smem + wave * (QB * 32) * OROW;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = qb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-        os[r * OROW + db * 32 + l32] = (bf16)(acc[qb][db][i] * a.scale);
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = db * 32 + 8 * i4 + 4 * g;
+        *(bf16x4*)(os + (qb * 32 + l32) * OROW + d) =
+            to_bf16x4(acc[qb][db][4 * i4] * a.scale, acc[qb][db][4 * i4 + 1] * a.scale,
+                      acc[qb][db][4 * i4 + 2] * a.scale, acc[qb][db][4 * i4 + 3] * a.scale);
       }
   __builtin_amdgcn_s_waitcnt(0);
   __builtin_amdgcn_wave_barrier();
