@@ -32,6 +32,11 @@ SMALL = [
     (3, 129, 16, 2, 31, 2, 0.5),
     (1, 1, 2, 1, 0, 0, 1.0),
     (2, 97, 8, 1, 0, 3, 1.0),      # four heads per forward workgroup, diagonal plus prefix
+    # key block 0 split over several dK/dV work units (atomic flushes), the
+    # later query tiles seeing only its prefix keys, p up to 32
+    (1, 640, 8, 1, 100, 4, 0.5),
+    (2, 700, 16, 2, 64, 16, 0.5),
+    (1, 900, 8, 2, 40, 32, 0.5),
     # windows >= 1024 after clamping run the wide-tile kernels (64-key forward /
     # dQ tiles, 128-row dK/dV tiles); shorter ones the narrow-tile kernels
     (1, 1100, 4, 2, WINDOW_INF, 0, 0.5),
@@ -55,6 +60,7 @@ def test_bf16_small(case):
     ((512, 1, 77), WINDOW_INF, 0),
     ((200, 300), 128, 16),
     ((1100, 37, 0, 1030), WINDOW_INF, 5),
+    ((700, 300, 900), 50, 8),      # several dK/dV units per key block in the long sequences
 ])
 def test_bf16_varlen_small(lengths, w, p):
     inp = make_inputs(batch=0, seqlen=0, heads_q=8, heads_kv=2, head_dim=64, window=w, prefix=p,
