@@ -45,6 +45,10 @@ KERNEL_SOURCES = {
     "sinkattn_fwd_bf16_d64": ["fwd_bf16.hip", "common.h", "mask_tiles.h"],
     "sinkattn_bwd_dkdv_bf16_d64": ["bwd_bf16.hip", "common.h", "mask_tiles.h"],
     "sinkattn_bwd_dq_bf16_d64": ["bwd_dq_bf16.hip", "common.h", "mask_tiles.h"],
+    # the kernels of one library call, whose HBM traffic the decode and GRPO
+    # lines report together
+    "sinkattn_decode_call": ["decode_bf16.hip", "common.h", "mask_tiles.h"],
+    "sinkattn_grpo_call": ["grpo.hip"],
 }
 # useful FLOP per visible pair of each kernel (d = head dim): forward QK^T and PV;
 # dK/dV kernel S, dP, dV, dK; dQ kernel dQ (its recomputed S and dP are not useful work)
@@ -227,6 +231,20 @@ def decode_cpu_baseline(layers, min_seconds: float = 10.0):
             "seconds": round(dt, 3)}
 
 
+def copy_probe(dev) -> None:
+    """Copy a COPY_PROBE_BYTES buffer device to device three times: the
+    reference that scales the hardware byte counters (FETCH_SIZE, WRITE_SIZE)
+    of the same run to bytes."""
+    import torch
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run_decode(args) -> int:
     """One step = one decode call per layer of a decode workload (one new token
     for every sequence of the batch); inputs resident, outputs and workspace
@@ -297,12 +315,17 @@ def run_decode(args) -> int:
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(range(len(runs)), key=lambda i: per_layer[i]["ms"])
     achieved = runs[dom]["bytes"] / (per_layer[dom]["ms"] * 1e-3) / 1e9
+    # HBM bytes of one call of the dominant layer from the committed counter
+    # summary (None if it was taken on other kernel sources)
+    traffic = committed_traffic("sinkattn_decode_call", args.workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "kernel": "sinkattn_decode_stream_bf16_d64 + sinkattn_decode_combine_bf16_d64 "
                           f"(one sinkattn_decode call, layer {dom})",
                 "avg_launch_ms": per_layer[dom]["ms"],
                 "algorithmic_bytes_per_launch": runs[dom]["bytes"]}
+    if args.copy_probe:
+        copy_probe(dev)
     cpu = None if args.no_cpu_baseline else decode_cpu_baseline(layers)
     out = {
         "metric": DECODE_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -412,12 +435,16 @@ def run_grpo(args) -> int:
     nbytes = grpo_bytes(inp)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    traffic = committed_traffic("sinkattn_grpo_call", args.workload)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "grpo_group_stats + grpo_tokens (one sinkattn_grpo_loss call)",
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                "kernel": "grpo_rollout_stats + grpo_tokens + grpo_loss_sum "
+                          "(one sinkattn_grpo_loss call)",
                 "avg_launch_ms": round(avg_ms, 5), "median_call_ms":
                     round(statistics.median(per_call), 5),
                 "algorithmic_bytes_per_launch": nbytes}
+    if args.copy_probe:
+        copy_probe(dev)
     cpu = None if args.no_cpu_baseline else grpo_cpu_baseline(inp)
     out = {
         "metric": GRPO_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -602,13 +629,7 @@ def main(argv=None):
                        "bwd_tflops": round(10 * d * p["pairs"] / (t_bwd * 1e-3) / 1e12, 2)}
 
     if args.copy_probe:
-        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_probe(dev)
 
     cpu = None
     if not args.no_cpu_baseline:

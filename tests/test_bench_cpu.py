@@ -97,3 +97,23 @@ def test_grpo_compulsory_bytes():
     assert bench.grpo_bytes(inp) == 100 * (4 + 4 + 4 + 1 + 4) + 4 * 12 + 8
     inp0 = make_grpo_inputs(lengths=(10, 20), group_size=2, seed=1, beta=0.0)
     assert bench.grpo_bytes(inp0) == 30 * 13 + 2 * 12 + 8
+
+
+def test_committed_traffic_summaries_parse():
+    # every committed counter summary names a known source list and carries the
+    # fields bench.py reads; when its hash matches the sources, bench.py reports it
+    import glob
+    import os
+    import re
+    files = glob.glob(os.path.join(bench.ROOT, "profiles", "*_traffic.md"))
+    assert files
+    for path in files:
+        txt = open(path).read()
+        key = re.search(r"^kernel:\s*(\S+)", txt, re.M).group(1)
+        assert key in bench.KERNEL_SOURCES, path
+        workload = os.path.basename(path)[len(key) + 1:-len("_traffic.md")]
+        val = float(re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt).group(1))
+        assert val > 0
+        got = bench.committed_traffic(key, workload)
+        sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt).group(1)
+        assert (got == val) == (sha == bench.kernel_source_sha(key)), path
