@@ -56,22 +56,32 @@ KERNEL_FLOP_PER_PAIR = {"sinkattn_fwd_bf16_d64": 4, "sinkattn_bwd_dkdv_bf16_d64"
                         "sinkattn_bwd_dq_bf16_d64": 2}
 
 
-def kernel_variants(key_tile: int, query_tile: int, group: int = 1) -> dict:
+def dq_window_kernel(seqlen: int, group: int, window: int, prefix: int) -> bool:
+    """Whether the library runs its resident-tile window dQ kernel (suffix _win):
+    the same test as the host launcher -- GQA groups of a multiple of 4, 32-key
+    tiles (w < 1024) and at most 6 key tiles per 32-row block, i.e.
+    ceil(min(p, T) / 32) + ceil(w / 32) + 1 <= 6."""
+    if group % 4 or window >= 1024:
+        return False
+    return (min(prefix, seqlen) + 31) // 32 + (window + 31) // 32 + 1 <= 6
+
+
+def kernel_variants(key_tile: int, query_tile: int, group: int = 1, win_dq: bool = False) -> dict:
     """Names of the kernels one layer launches, per timed phase, for the tile
     shapes the library reports (narrow tiles carry a suffix; the narrow
     forward takes four query heads per workgroup when the GQA group size is a
-    multiple of 4, suffix _k32h)."""
+    multiple of 4, suffix _k32h; win_dq: the resident-tile window dQ kernel)."""
     if query_tile != 128:
         raise ValueError(f"no dK/dV kernel with {query_tile}-row query tiles")
     k32 = "_k32" if key_tile == 32 else ""
     fwd = "_k32h" if key_tile == 32 and group % 4 == 0 else k32
     return {"fwd_ms": "sinkattn_fwd_bf16_d64" + fwd,
             "bwd_dkdv_ms": "sinkattn_bwd_dkdv_bf16_d64",
-            "bwd_dq_ms": "sinkattn_bwd_dq_bf16_d64" + k32}
+            "bwd_dq_ms": "sinkattn_bwd_dq_bf16_d64" + ("_win" if win_dq else k32)}
 
 
 def kernel_base(name: str) -> str:
-    for suffix in ("_k32h", "_k32"):
+    for suffix in ("_k32h", "_k32", "_win"):
         if name.endswith(suffix):
             return name[:-len(suffix)]
     return name
@@ -527,7 +537,11 @@ def main(argv=None):
                       torch.empty_like(r["v"]), torch.empty_like(r["s"]))
         r["ws"] = torch.empty(sinkattn_bwd_workspace_size(pb), dtype=torch.uint8, device=dev)
         r["pairs"] = useful_pairs(inp)
-        r["kernels"] = kernel_variants(*sinkattn_tile_config(pb), pb.heads_q // pb.heads_kv)
+        group = pb.heads_q // pb.heads_kv
+        # the library clamps w and p to the (longest) sequence length
+        r["kernels"] = kernel_variants(*sinkattn_tile_config(pb), group,
+                                       dq_window_kernel(pb.seqlen, group, min(inp.window, pb.seqlen),
+                                                        min(inp.prefix, pb.seqlen)))
     torch.cuda.synchronize()
 
     def step(events=None):

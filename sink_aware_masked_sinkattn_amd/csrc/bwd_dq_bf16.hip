@@ -380,6 +380,187 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_D
   dq_body<1, SA_DQ_QB_K32>(a);
 }
 
+// ---------------------------------------------------------------------------
+// Short windows with GQA groups of a multiple of 4: one workgroup per
+// (32-row query block, kv head).  The block's key tiles (prefix and window,
+// at most WIN_TILES tiles of 32 keys) are copied into LDS once and stay
+// resident; the four waves then take the group's query heads in turn (wave
+// w: heads w, w + 4, ...), each running the whole key-tile list from LDS
+// with no further copies, waits or barriers.  The K/V tiles are so loaded
+// once for all the group's heads, not once per head, and the tile loop has
+// no per-tile latency.  Same arithmetic per tile as the streaming kernels.
+constexpr int WIN_TILES = 6;
+struct __attribute__((aligned(128))) DqWinSmem {
+  bf16 kv[WIN_TILES][2][32 * D];    // K then V of each tile (swizzled rows, tile_off)
+  bf16 stage[WAVES][32 * OROW];     // each wave's dQ rows, for row-contiguous stores
+};
+
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
+  __shared__ DqWinSmem sm;
+  // consecutive workgroups go to consecutive XCDs: with 8 kv heads each XCD
+  // keeps one kv head and its L2
+  const int kvh = blockIdx.x;
+  const int z = blockIdx.y;
+  const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
+  const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
+  const int q_start = qt * 32;
+  if (q_start >= sv.len) return;
+  const int q_last = min(q_start + 31, sv.len - 1);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int q_row_stride = a.heads_q * D;
+  const int kv_row_stride = a.heads_kv * D;
+  const bf16* kbase = a.k + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
+  const bf16* vbase = a.v + (size_t)sv.row_base * kv_row_stride + (size_t)kvh * D;
+
+  // the block's key tiles, all copied up front (ntiles <= WIN_TILES: the
+  // host launches this kernel only when every block's list fits)
+  int seg[4];
+  const int nseg = sa_key_tile_segments(q_start, q_last, a.window, a.prefix, 32, seg);
+  const int n0 = seg[1] - seg[0];
+  const int ntiles = n0 + (nseg > 1 ? seg[3] - seg[2] : 0);
+  const TileLane tl = tile_lane(lane, kv_row_stride * 2);
+  for (int t = 0; t < ntiles; ++t) {
+    const int r0 = (t < n0 ? seg[0] + t : seg[2] + (t - n0)) * 32;
+    tile_load_lds_lane<32, WAVES>(sm.kv[t][0], kbase + (size_t)r0 * kv_row_stride,
+                                  kv_row_stride * 2, sv.len - r0, wave, tl);
+    tile_load_lds_lane<32, WAVES>(sm.kv[t][1], vbase + (size_t)r0 * kv_row_stride,
+                                  kv_row_stride * 2, sv.len - r0, wave, tl);
+  }
+  wait_all_mem();
+  __syncthreads();
+
+  const int row = q_start + l32;
+  const bool ok = row < sv.len;
+  // a head's rows (Q, dO, O fragments, l): loaded one head ahead, so their
+  // latency overlaps the previous head's tile loop
+  struct HeadRows {
+    bf16x8 q[4], d[4], o[4];
+    float l;
+  };
+  // rows past the end read the last row (no branches around the loads, so
+  // the compiler can count them); they get L = +inf below, so P' = dS = 0
+  // there and their dQ is not stored
+  const int row_c = ok ? row : sv.len - 1;
+  auto load_rows = [&](int h, HeadRows& hr) {
+    const size_t qoff = (size_t)sv.row_base * q_row_stride + (size_t)h * D;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const size_t off = qoff + (size_t)row_c * q_row_stride + 16 * s + 8 * g;
+      hr.q[s] = *(const bf16x8*)(a.q + off);
+      hr.d[s] = *(const bf16x8*)(a.dout + off);
+      hr.o[s] = *(const bf16x8*)(a.o + off);
+    }
+    hr.l = a.lse[sv.lse_base + (size_t)h * a.lse_head_stride + row_c];
+  };
+  HeadRows nxt;
+  if (wave < a.group) load_rows(kvh * a.group + wave, nxt);
+  for (int hi = wave; hi < a.group; hi += WAVES) {
+    const int h = kvh * a.group + hi;
+    const size_t qoff = (size_t)sv.row_base * q_row_stride + (size_t)h * D;
+    const HeadRows cur = nxt;
+    // Q, dO fragments (B operands) and the row statistics, as in dq_body:
+    //   D = rowsum(dO * O),  L = logaddexp(l, s_h),  ds_h -= exp(s_h - L) D
+    bf16x8 qf[1][4], df[1][4];
+    float l2[1], dd[1];
+    const float sink = a.sinks[h];
+    const float sink2 = sink * SA_LOG2E;
+    float dot = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qf[0][s] = cur.q[s];
+      df[0][s] = cur.d[s];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2)
+        dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{cur.o[s][j], cur.o[s][j + 1]},
+                                              bf16x2{cur.d[s][j], cur.d[s][j + 1]}, dot, false);
+    }
+    dot = halves_sum(dot);
+    const float lv2 = cur.l * SA_LOG2E;
+    const float big_l2 = (sink == -INFINITY)
+                             ? lv2
+                             : fmaxf(lv2, sink2) + fast_log2(1.0f + fast_exp2(-fabsf(lv2 - sink2)));
+    l2[0] = ok ? big_l2 : INFINITY;
+    dd[0] = ok ? dot : 0.0f;
+    float ds_part = (ok && g == 0) ? -fast_exp2(sink2 - big_l2) * dot : 0.0f;
+    // the next head's rows go out now, after this head's have been consumed:
+    // the statistics are pinned ahead of the loads, so the one wait for this
+    // head's rows comes before them and the loads stay in flight through
+    // the tile loop
+    asm volatile("" : "+v"(l2[0]), "+v"(dd[0]), "+v"(ds_part));
+    __builtin_amdgcn_sched_barrier(0);
+    if (hi + WAVES < a.group) load_rows(h + WAVES, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x16 acc[1][2];   // dQ^T: C layout [m = d][n = query], lane = query
+    acc[0][0] = acc[0][1] = f32x16{};
+    for (int t = 0; t < ntiles; ++t) {
+      const int k0 = (t < n0 ? seg[0] + t : seg[2] + (t - n0)) * 32;
+      const int cls = sa_tile_class(q_start, q_last, k0, k0 + 31, a.window, a.prefix);
+      const uint32_t ktile = lds_addr(sm.kv[t][0]);   // V tile follows
+      if (cls == SA_TILE_FULL)
+        tile_step<1, 1, false>(ktile, qf, df, l2, dd, acc, q_start, k0, a.window, a.prefix,
+                               a.scale_log2, lane);
+      else if (cls == SA_TILE_PARTIAL)
+        tile_step<1, 1, true>(ktile, qf, df, l2, dd, acc, q_start, k0, a.window, a.prefix,
+                              a.scale_log2, lane);
+    }
+
+    // dQ = scale * acc through this wave's staging rows (runs of 4 head dims
+    // per lane), then row-contiguous 16-byte stores
+    bf16* os = sm.stage[wave];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = db * 32 + 8 * i4 + 4 * g;
+        *(bf16x4*)(os + l32 * OROW + d) =
+            to_bf16x4(acc[0][db][4 * i4] * a.scale, acc[0][db][4 * i4 + 1] * a.scale,
+                      acc[0][db][4 * i4 + 2] * a.scale, acc[0][db][4 * i4 + 3] * a.scale);
+      }
+    // LDS writes done (lgkmcnt 0; the next head's row loads stay in flight)
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    bf16* obase = a.dq + qoff;
+#pragma unroll
+    for (int it = 0; it < (32 * D) / (64 * 8); ++it) {   // 64 lanes x 16 B per iteration
+      const int chunk = it * 64 + lane;
+      const int r = chunk >> 3;
+      const int c = (chunk & 7) * 8;
+      if (q_start + r < sv.len)
+        *(uint4*)(obase + (size_t)(q_start + r) * q_row_stride + c) = *(const uint4*)(os + r * OROW + c);
+    }
+    // the staging rows are rewritten for the next head only after these reads
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    // row statistics for the dK/dV kernel, and this wave's share of ds_h
+    if (ok && g == 0) {
+      const size_t wi = (size_t)h * a.rows_total + sv.row_base + row;
+      a.d_ws[wi] = dd[0];
+      a.l2_ws[wi] = l2[0];
+    }
+#pragma unroll
+    for (int w = 1; w < 64; w <<= 1) ds_part += __shfl_xor(ds_part, w);
+    if (lane == 0) unsafeAtomicAdd(a.dsinks + h, ds_part);
+  }
+  // clear the fp32 dK / dV accumulators of the block's rows for this kv head
+  // (the dK/dV kernel adds into them)
+  if (SA_DQ_ZERO_ACC) {
+    const int nrows = q_last - q_start + 1;
+    for (int i = tid; i < nrows * (D / 4); i += WAVES * 64) {
+      const int r = q_start + i / (D / 4);
+      const size_t e = ((size_t)(sv.row_base + r) * a.heads_kv + kvh) * D + 4 * (i % (D / 4));
+      *(float4*)(a.dk_acc + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+      *(float4*)(a.dv_acc + e) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
 }  // namespace
 
 int fwd_key_tile(int window);
@@ -387,6 +568,19 @@ int fwd_key_tile(int window);
 // Whether the dQ kernel clears the fp32 dK/dV accumulators (else the caller
 // must before the dK/dV kernel runs).
 bool dq_clears_dkdv_accumulators() { return SA_DQ_ZERO_ACC != 0; }
+
+// Whether the resident-tile window kernel runs: GQA groups of a multiple of
+// 4 (four waves take the group's heads) and a key-tile list of at most
+// WIN_TILES tiles for every 32-row block.  A block [q0, q0 + 31] (q0 a
+// multiple of 32) lists at most ceil(min(p, T) / 32) prefix tiles and
+// floor(q1 / 32) - floor(max(0, q0 - w) / 32) + 1 <= ceil(w / 32) + 1
+// window tiles.
+bool dq_window_kernel(int seqlen, int group, int window, int prefix) {
+  if (group % 4 != 0 || fwd_key_tile(window) != 32) return false;
+  const long long pre = ((long long)(prefix < seqlen ? prefix : seqlen) + 31) / 32;
+  const long long win = ((long long)window + 31) / 32 + 1;
+  return pre + win <= WIN_TILES;
+}
 
 hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
                                   const bf16* o, const float* lse, const float* sinks,
@@ -404,11 +598,17 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
   a.group = heads_q / heads_kv; a.window = window; a.prefix = prefix;
   a.rows_total = rows_total;
   const bool k32 = fwd_key_tile(window) == 32;
-  const int BQ = k32 ? DqTiles<1, SA_DQ_QB_K32>::BQ : DqTiles<2, SA_DQ_QB>::BQ;
-  a.num_q_tiles = (seqlen + BQ - 1) / BQ;
   a.scale_log2 = scale * SA_LOG2E;
   a.scale = scale;
-  if (a.num_q_tiles == 0 || batch == 0) return hipSuccess;
+  if (seqlen == 0 || batch == 0) return hipSuccess;
+  if (dq_window_kernel(seqlen, a.group, window, prefix)) {
+    a.num_q_tiles = (seqlen + 31) / 32;
+    hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64_win, dim3(heads_kv, batch, a.num_q_tiles),
+                       dim3(WAVES * 64), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int BQ = k32 ? DqTiles<1, SA_DQ_QB_K32>::BQ : DqTiles<2, SA_DQ_QB>::BQ;
+  a.num_q_tiles = (seqlen + BQ - 1) / BQ;
   dim3 grid(heads_q, batch, a.num_q_tiles);
   if (k32)
     hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64_k32, grid, dim3(WAVES * 64), 0, stream, a);

@@ -46,7 +46,15 @@ def test_kernel_variant_names():
     assert narrow["fwd_ms"] == "sinkattn_fwd_bf16_d64_k32"
     assert heads4["fwd_ms"] == "sinkattn_fwd_bf16_d64_k32h"
     assert bench.kernel_variants(64, 128, 8) == wide
-    for variants in (narrow, heads4):
+    win = bench.kernel_variants(32, 128, 8, True)
+    assert win["bwd_dq_ms"] == "sinkattn_bwd_dq_bf16_d64_win"
+    # the resident-tile window dQ kernel: groups of a multiple of 4, at most 6 key tiles
+    assert bench.dq_window_kernel(8192, 8, 128, 4) and bench.dq_window_kernel(8192, 4, 128, 16)
+    assert not bench.dq_window_kernel(8192, 2, 128, 4)      # group not a multiple of 4
+    assert not bench.dq_window_kernel(8192, 8, 160, 4)      # 1 + 5 + 1 = 7 tiles
+    assert not bench.dq_window_kernel(8192, 8, 128, 33)     # two prefix tiles
+    assert not bench.dq_window_kernel(8192, 8, 1024, 0)     # wide tiles
+    for variants in (narrow, heads4, win):
         for ph, name in variants.items():
             assert bench.kernel_base(name) == wide[ph]
             assert bench.kernel_source_sha(name) == bench.kernel_source_sha(wide[ph])
