@@ -185,6 +185,34 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// The backward's row statistics for one query row, from this lane's half
+// of its dO and O (head dims 16s + 8g .. +7) and its forward l:
+//   D = rowsum(dO * O),  L = logaddexp(l, s_h)  (log2 units: L * log2 e),
+//   and the row's term of ds_h, -exp(s_h - L) D (counted by the g == 0 half).
+// bf16 products are exact in fp32, so v_dot2_f32_bf16 changes only the
+// rounding order of D.  Rows past the end (ok false) get L = +inf and D = 0.
+__device__ __forceinline__ void row_stats(const bf16x8 (&o)[4], const bf16x8 (&dout)[4], float l,
+                                          float sink, bool ok, int g, float& l2, float& dd,
+                                          float& ds) {
+  float dot = 0.0f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; j += 2)
+      dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{o[s][j], o[s][j + 1]},
+                                            bf16x2{dout[s][j], dout[s][j + 1]}, dot, false);
+  dot = halves_sum(dot);
+  // L2 = log2(2^l2 + 2^s2) = max + log2(1 + 2^-|l2 - s2|)
+  const float lv2 = l * SA_LOG2E;
+  const float sink2 = sink * SA_LOG2E;
+  const float big_l2 = (sink == -INFINITY)
+                           ? lv2
+                           : fmaxf(lv2, sink2) + fast_log2(1.0f + fast_exp2(-fabsf(lv2 - sink2)));
+  l2 = ok ? big_l2 : INFINITY;
+  dd = ok ? dot : 0.0f;
+  ds = (ok && g == 0) ? -fast_exp2(sink2 - big_l2) * dot : 0.0f;
+}
+
 #ifndef SA_DQ_OCC
 #define SA_DQ_OCC 2   // waves per SIMD the register budget is set for
 #endif
@@ -256,35 +284,23 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   bf16x8 qf[QB][4], df[QB][4];
   float l2[QB], dd[QB];
   const float sink = a.sinks[h];
-  const float sink2 = sink * SA_LOG2E;
   float ds_part = 0.0f;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw0 + qb * 32 + l32;
     const bool ok = row < sv.len;
-    float dot = 0.0f;
+    bf16x8 of[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const size_t off = qoff + (size_t)row * q_row_stride + 16 * s + 8 * g;
       qf[qb][s] = ok ? *(const bf16x8*)(a.q + off) : bf16x8{};
       df[qb][s] = ok ? *(const bf16x8*)(a.dout + off) : bf16x8{};
-      const bf16x8 of = ok ? *(const bf16x8*)(a.o + off) : bf16x8{};
-      // bf16 products are exact in fp32: v_dot2_f32_bf16 changes only the
-      // rounding order of the sum
-#pragma unroll
-      for (int j = 0; j < 8; j += 2)
-        dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{of[j], of[j + 1]},
-                                              bf16x2{df[qb][s][j], df[qb][s][j + 1]}, dot, false);
+      of[s] = ok ? *(const bf16x8*)(a.o + off) : bf16x8{};
     }
-    dot = halves_sum(dot);
-    // log2 units: L2 = log2(2^l2 + 2^s2) = max + log2(1 + 2^-|l2 - s2|)
-    const float lv2 = (ok ? a.lse[sv.lse_base + (size_t)h * a.lse_head_stride + row] : 0.0f) * SA_LOG2E;
-    const float big_l2 = (sink == -INFINITY)
-                             ? lv2
-                             : fmaxf(lv2, sink2) + fast_log2(1.0f + fast_exp2(-fabsf(lv2 - sink2)));
-    l2[qb] = ok ? big_l2 : INFINITY;
-    dd[qb] = ok ? dot : 0.0f;
-    if (ok && g == 0) ds_part -= fast_exp2(sink2 - big_l2) * dot;
+    const float l = ok ? a.lse[sv.lse_base + (size_t)h * a.lse_head_stride + row] : 0.0f;
+    float ds;
+    row_stats(of, df[qb], l, sink, ok, g, l2[qb], dd[qb], ds);
+    ds_part += ds;
   }
 
   f32x16 acc[QB][2];   // dQ^T: C layout [m = d][n = query], lane = query
@@ -464,30 +480,15 @@ void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
     const int h = kvh * a.group + hi;
     const size_t qoff = (size_t)sv.row_base * q_row_stride + (size_t)h * D;
     const HeadRows cur = nxt;
-    // Q, dO fragments (B operands) and the row statistics, as in dq_body:
-    //   D = rowsum(dO * O),  L = logaddexp(l, s_h),  ds_h -= exp(s_h - L) D
+    // Q, dO fragments (B operands) and the row statistics
     bf16x8 qf[1][4], df[1][4];
-    float l2[1], dd[1];
-    const float sink = a.sinks[h];
-    const float sink2 = sink * SA_LOG2E;
-    float dot = 0.0f;
+    float l2[1], dd[1], ds_part;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       qf[0][s] = cur.q[s];
       df[0][s] = cur.d[s];
-#pragma unroll
-      for (int j = 0; j < 8; j += 2)
-        dot = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{cur.o[s][j], cur.o[s][j + 1]},
-                                              bf16x2{cur.d[s][j], cur.d[s][j + 1]}, dot, false);
     }
-    dot = halves_sum(dot);
-    const float lv2 = cur.l * SA_LOG2E;
-    const float big_l2 = (sink == -INFINITY)
-                             ? lv2
-                             : fmaxf(lv2, sink2) + fast_log2(1.0f + fast_exp2(-fabsf(lv2 - sink2)));
-    l2[0] = ok ? big_l2 : INFINITY;
-    dd[0] = ok ? dot : 0.0f;
-    float ds_part = (ok && g == 0) ? -fast_exp2(sink2 - big_l2) * dot : 0.0f;
+    row_stats(cur.o, cur.d, cur.l, a.sinks[h], ok, g, l2[0], dd[0], ds_part);
     // the next head's rows go out now, after this head's have been consumed:
     // the statistics are pinned ahead of the loads, so the one wait for this
     // head's rows comes before them and the loads stay in flight through
