@@ -83,6 +83,30 @@ def test_decode_lengths_clamped_to_capacity():
     check(o, lse, ro, rl, "clamped", scaled=True)
 
 
+def test_decode_many_sequences():
+    # more sequences than one LDS scan window holds (1024): the single-pass
+    # kernel walks its unit list window by window; lengths 0 .. capacity
+    g = torch.Generator().manual_seed(5)
+    lengths = tuple(int(x) for x in torch.randint(0, 97, (1100,), generator=g))
+    inp = make_decode_inputs(lengths=lengths, capacity=96, heads_q=4, heads_kv=1, head_dim=64,
+                             window=WINDOW_INF, prefix=0, seed=17, std=1.0)
+    o, lse = run_decode_gpu(inp)
+    ro, rl = run_decode_oracle(inp)
+    check(o, lse, ro, rl, "1100 sequences", scaled=True)
+
+
+def test_decode_stream_wide_batch():
+    # the stream kernel near its batch bound (batch * heads_kv just under 1024):
+    # many segments, blocks crossing sequence boundaries, some empty caches
+    g = torch.Generator().manual_seed(6)
+    lengths = tuple(int(x) for x in torch.randint(0, 600, (127,), generator=g))
+    inp = make_decode_inputs(lengths=lengths, capacity=600, heads_q=64, heads_kv=8, head_dim=64,
+                             window=WINDOW_INF, prefix=0, seed=18, std=1.0)
+    o, lse = run_decode_gpu(inp)
+    ro, rl = run_decode_oracle(inp)
+    check(o, lse, ro, rl, "127 sequences x 8 kv heads", scaled=True)
+
+
 @pytest.mark.parametrize("w,p", [(WINDOW_INF, 0), (128, 4), (9, 70)])
 def test_decode_matches_training_forward_row(w, p):
     # the rollout engine must reproduce the trainer's probabilities: decode
