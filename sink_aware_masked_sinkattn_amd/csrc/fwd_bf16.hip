@@ -16,10 +16,11 @@
 // the sink scaling costs one extra exponential per row in the epilogue.
 //
 // Work decomposition (one workgroup = WAVES waves x QB*32 query rows of one
-// head; by default 4 waves x 32 rows, 3 waves per SIMD -- or, for windows
-// under 1024 with GQA groups of a multiple of 4, four query heads of one kv
-// group x the same 32 rows, so the workgroup loads the key tiles of 32 rows
-// (w/32 + 2 tiles) once for four heads and every wave uses every tile):
+// head: 4 waves x 64 rows at 2 waves per SIMD for 64-key tiles, 4 waves x 32
+// rows for 32-key tiles -- or, for windows under 1024 with GQA groups of a
+// multiple of 4, four query heads of one kv group x the same 32 rows, so the
+// workgroup loads the key tiles of 32 rows (w/32 + 2 tiles) once for four
+// heads and every wave uses every tile):
 //   * each wave owns QB 32-row MFMA blocks of query rows whose Q fragments
 //     stay in registers for the whole kernel; each key tile's K and V^T
 //     operands are read from LDS once, up front, and shared by the blocks;
@@ -41,26 +42,28 @@
 namespace {
 
 constexpr int D = 64;
+// 32-row query blocks per wave of the 64-key-tile kernel: two, so every K
+// and V^T operand read from LDS (and the per-tile softmax bookkeeping) serves
+// 64 rows (0.619 -> 0.604 ms for a causal T=8192 layer against one block at 3
+// waves per SIMD).  The 32-key-tile kernels keep one block per wave.
 #ifndef SA_FWD_QB
-#define SA_FWD_QB 1
+#define SA_FWD_QB 2
 #endif
 #ifndef SA_FWD_WAVES
 #define SA_FWD_WAVES 4
 #endif
-constexpr int QB = SA_FWD_QB;          // 32-row query blocks per wave
 constexpr int WAVES = SA_FWD_WAVES;    // waves per workgroup
-constexpr int BQ = WAVES * QB * 32;      // query rows per workgroup
 // Key tiles hold NKB blocks of 32 keys: 64-key tiles in general, 32-key
 // tiles for short windows, where a 32-row query block needs only w + 32 keys
 // and wider tiles would mostly compute masked pairs.
 constexpr int OROW = D + 8;              // padded row of the epilogue staging buffer
-constexpr int STAGE_ELEMS = WAVES * QB * 32 * OROW;
 // LDS: two K/V tile pairs during the key loop; afterwards the same memory
 // stages each wave's output rows (padded) for row-contiguous stores.
-template <int NKB>
+template <int NKB, int QB>
 struct FwdTiles {
   static constexpr int BK = 32 * NKB;                 // key rows per LDS tile
   static constexpr int TILE_ELEMS = BK * D;           // swizzled rows (tile_off)
+  static constexpr int STAGE_ELEMS = WAVES * QB * 32 * OROW;
   static constexpr int SMEM_ELEMS = (4 * TILE_ELEMS > STAGE_ELEMS) ? 4 * TILE_ELEMS : STAGE_ELEMS;
   static_assert(SMEM_ELEMS >= 4 * TILE_ELEMS && SMEM_ELEMS >= STAGE_ELEMS, "LDS sizing");
 };
@@ -92,7 +95,7 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
 
 // One key tile (NKB blocks of 32 keys) against this wave's QB blocks of 32
 // query rows.  MASK: apply the element predicate (partial tiles only).
-template <int NKB, bool MASK>
+template <int NKB, int QB, bool MASK>
 __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB][4],
                                           f32x16 (&acc)[QB][2], float (&m_run)[QB],
                                           float (&r_run)[QB], int qw0, int k0, int window,
@@ -198,16 +201,16 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
 }
 
 #ifndef SA_FWD_OCC
-#define SA_FWD_OCC 3   // waves per SIMD the register budget is set for
+#define SA_FWD_OCC 2   // waves per SIMD the 64-key kernel's register budget is set for
 #endif
 // HW: waves along heads.  HW = 1: the workgroup's waves take consecutive
 // row blocks of one head.  HW = 4 (short windows, GQA groups of a multiple
 // of 4): they take four query heads of one kv group on the same rows, so the
 // workgroup's key tiles are those of QB*32 rows only and every wave uses
 // every tile (the K/V tiles are shared by the four heads).
-template <int NKB, int HW>
+template <int NKB, int HW, int QB>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
-  using T = FwdTiles<NKB>;
+  using T = FwdTiles<NKB, QB>;
   constexpr int BK = T::BK;
   constexpr int TILE_ELEMS = T::TILE_ELEMS;
   static_assert(WAVES % HW == 0, "the waves split into HW heads x row blocks");
@@ -296,9 +299,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
                                 : SA_TILE_SKIP;
     const uint32_t ktile = lds_addr(smem + (2 * buf) * TILE_ELEMS);   // V tile follows
     if (cls == SA_TILE_FULL) {
-      tile_step<NKB, false>(ktile, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, QB, false>(ktile, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     } else if (cls == SA_TILE_PARTIAL) {
-      tile_step<NKB, true>(ktile, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, QB, true>(ktile, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     }
     wait_all_mem();
     __syncthreads();
@@ -306,7 +309,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 
   // ---- epilogue: O = acc / (r + exp(s - m)), l = ln(2) * (m + log2 r)
   // Stage each wave's 64 x 64 output through LDS for row-contiguous stores.
-  bf16* os = smem + wave * (QB * 32) * OROW;   // 64 rows x OROW per wave (fits in 4 tiles)
+  bf16* os = smem + wave * (QB * 32) * OROW;   // QB*32 rows x OROW per wave
   const float sink_l2 = a.sinks[h] * SA_LOG2E;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -345,16 +348,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 }
 
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC, SA_FWD_OCC))) void sinkattn_fwd_bf16_d64(FwdArgs a) {
-  fwd_body<2, 1>(a);
+  fwd_body<2, 1, SA_FWD_QB>(a);
 }
 #ifndef SA_FWD_OCC_K32
 #define SA_FWD_OCC_K32 4
 #endif
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC_K32, SA_FWD_OCC_K32))) void sinkattn_fwd_bf16_d64_k32(FwdArgs a) {
-  fwd_body<1, 1>(a);
+  fwd_body<1, 1, 1>(a);
 }
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC_K32, SA_FWD_OCC_K32))) void sinkattn_fwd_bf16_d64_k32h(FwdArgs a) {
-  fwd_body<1, 4>(a);
+  fwd_body<1, 4, 1>(a);
 }
 
 }  // namespace
@@ -379,12 +382,13 @@ hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, cons
   if (seqlen == 0 || batch == 0 || heads_q == 0) return hipSuccess;
   // short windows with GQA groups of a multiple of 4: four heads per workgroup
   const bool heads4 = fwd_key_tile(window) == 32 && a.group % 4 == 0;
-  const int rows = heads4 ? QB * 32 : BQ;
+  const bool k32 = fwd_key_tile(window) == 32;
+  const int rows = heads4 ? 32 : (k32 ? WAVES * 32 : WAVES * SA_FWD_QB * 32);
   a.num_q_tiles = (seqlen + rows - 1) / rows;
   dim3 grid(heads4 ? heads_q / 4 : heads_q, batch, a.num_q_tiles);
   if (heads4)
     hipLaunchKernelGGL(sinkattn_fwd_bf16_d64_k32h, grid, dim3(WAVES * 64), 0, stream, a);
-  else if (fwd_key_tile(window) == 32)
+  else if (k32)
     hipLaunchKernelGGL(sinkattn_fwd_bf16_d64_k32, grid, dim3(WAVES * 64), 0, stream, a);
   else
     hipLaunchKernelGGL(sinkattn_fwd_bf16_d64, grid, dim3(WAVES * 64), 0, stream, a);
