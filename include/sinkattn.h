@@ -132,13 +132,16 @@ sinkattn_status sinkattn_bwd(const sinkattn_problem *problem, const void *q,
  * sink gradient dsinks (of "GPT-OSS Agentic RL training: a practical
  * retrospective", FlashAttention v3 implementation section) are computed in
  * PREPARE for fp32 and inside DQ for bf16.
- *   PREPARE: clears dsinks (fp32: and runs the row pass);
- *   DQ:      dQ, written to dq (bf16: also the row statistics, dsinks, and
- *            clearing the fp32 dK/dV workspace accumulators);
+ *   PREPARE: fp32: clears dsinks and runs the row pass; bf16: nothing
+ *            (except clearing dsinks for an empty problem);
+ *   DQ:      dQ, written to dq (bf16: also the row statistics, each
+ *            workgroup's part of dsinks into the workspace, and clearing the
+ *            fp32 dK/dV workspace accumulators);
  *   DKDV:    dK, dV from the recomputed probabilities exp(S - L) (bf16: into
  *            the fp32 workspace accumulators; fp32: into dk, dv);
- *   FINISH:  scales and converts the dK/dV accumulators into dk, dv (bf16;
- *            nothing to do for fp32).
+ *   FINISH:  bf16: scales and converts the dK/dV accumulators into dk, dv,
+ *            and writes dsinks as the sum of DQ's parts, added in a fixed
+ *            order (so dsinks is the same on every call); fp32: nothing.
  * sinkattn_bwd(...) == sinkattn_bwd_phases(SINKATTN_BWD_ALL, ...).
  */
 enum {

@@ -24,10 +24,11 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                     hipStream_t stream);
 hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
                                   const bf16* o, const float* lse, const float* sinks,
-                                  float* dsinks, float* l_ws, float* d_ws, float* dk_acc,
+                                  float* ds_part, int ds_stride, float* l_ws, float* d_ws, float* dk_acc,
                                   float* dv_acc, bf16* dq, const int* cu_seqlens, int batch,
                                   int seqlen, int rows_total, int heads_q, int heads_kv, int window,
                                   int prefix, float scale, hipStream_t stream);
+int dq_query_tile(int seqlen, int group, int window, int prefix);
 hipError_t launch_fwd_f32(int head_dim, const float* q, const float* k, const float* v,
                           const float* sinks, float* o, float* lse, const int* cu_seqlens,
                           int batch, int seqlen, int total_tokens, int heads_q, int heads_kv,
@@ -43,7 +44,9 @@ hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const v
                           int batch, int seqlen, int rows_total, int heads_q, int heads_kv,
                           int lse_head_stride, hipStream_t stream);
 hipError_t launch_convert(int dtype_is_f32, const float* dk_acc, const float* dv_acc, void* dk,
-                          void* dv, long long n_kv, float scale, hipStream_t stream);
+                          void* dv, long long n_kv, float scale, const float* ds_part,
+                          int ds_used, int ds_stride, int heads, float* dsinks,
+                          hipStream_t stream);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
 hipError_t launch_decode_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                   const int* cache_seqlens, const float* sinks, bf16* o,
@@ -105,7 +108,8 @@ sinkattn_status check_problem(const sinkattn_problem* pb, Dims* dims) {
 }
 
 struct Workspace {
-  size_t d_off, l_off, dk_off, dv_off, total;
+  size_t d_off, l_off, dk_off, dv_off, ds_off, total;
+  int ds_stride;   // slots per head for the parts of ds_h (bf16)
 };
 
 Workspace workspace_layout(const sinkattn_problem* pb, const Dims& dims) {
@@ -114,11 +118,17 @@ Workspace workspace_layout(const sinkattn_problem* pb, const Dims& dims) {
   const size_t stat = round_up(rows * (size_t)pb->heads_q * sizeof(float));
   const bool accum = pb->dtype == SINKATTN_BF16;   // fp32 path writes outputs directly
   const size_t kvacc = accum ? round_up(rows * pb->heads_kv * pb->head_dim * sizeof(float)) : 0;
+  // per-workgroup parts of ds_h: one slot per (sequence, 32-row block) and
+  // head, enough for every dQ kernel's query tiles
+  const long long blocks32 = (long long)pb->batch * ((pb->seqlen + 31) / 32);
+  w.ds_stride = accum ? (int)blocks32 : 0;
+  const size_t ds = accum ? round_up((size_t)blocks32 * pb->heads_q * sizeof(float)) : 0;
   w.d_off = 0;
   w.l_off = stat;
   w.dk_off = 2 * stat;
   w.dv_off = w.dk_off + kvacc;
-  w.total = w.dv_off + kvacc;
+  w.ds_off = w.dv_off + kvacc;
+  w.total = w.ds_off + ds;
   return w;
 }
 
@@ -242,7 +252,9 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
   }
   // ---- validation done; device work from here on
   hipError_t e = hipSuccess;
-  if (phases & SINKATTN_BWD_PREPARE) {
+  // dsinks: fp32 accumulates into it (cleared here); bf16 forms it in FINISH
+  // from the dQ kernel's per-workgroup parts (an empty problem: cleared here)
+  if ((phases & SINKATTN_BWD_PREPARE) && (pb->dtype == SINKATTN_FP32 || empty)) {
     e = launch_zero_f32(dsinks, pb->heads_q, s);
     if (e != hipSuccess) return hip_status(e);
   }
@@ -254,6 +266,7 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
   const bool is_f32 = pb->dtype == SINKATTN_FP32;
   float* dk_acc = is_f32 ? nullptr : (float*)(ws + wl.dk_off);
   float* dv_acc = is_f32 ? nullptr : (float*)(ws + wl.dv_off);
+  float* ds_part = is_f32 ? nullptr : (float*)(ws + wl.ds_off);
   const int window = pb->window > pb->seqlen ? pb->seqlen : pb->window;
   const int prefix = pb->prefix > pb->seqlen ? pb->seqlen : pb->prefix;
   const int rows = (int)dims.rows;
@@ -274,7 +287,7 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
   }
   if (!is_f32 && (phases & SINKATTN_BWD_DQ)) {
     e = launch_bwd_dq_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
-                               (const bf16*)o, lse, sinks, dsinks, l_ws, d_ws, dk_acc, dv_acc,
+                               (const bf16*)o, lse, sinks, ds_part, wl.ds_stride, l_ws, d_ws, dk_acc, dv_acc,
                                (bf16*)dq, pb->cu_seqlens, pb->batch, pb->seqlen, rows,
                                pb->heads_q, pb->heads_kv, window, prefix, pb->softmax_scale, s);
     if (e != hipSuccess) return hip_status(e);
@@ -296,8 +309,11 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
     if (e != hipSuccess) return hip_status(e);
   }
   if ((phases & SINKATTN_BWD_FINISH) && !is_f32) {
+    // the slots the dQ kernel wrote: batch * its query tiles per sequence
+    const int qtile = dq_query_tile(pb->seqlen, pb->heads_q / pb->heads_kv, window, prefix);
+    const int ds_used = pb->batch * ((pb->seqlen + qtile - 1) / qtile);
     e = launch_convert(0, dk_acc, dv_acc, dk, dv, (long long)rows * pb->heads_kv * pb->head_dim,
-                       pb->softmax_scale, s);
+                       pb->softmax_scale, ds_part, ds_used, wl.ds_stride, pb->heads_q, dsinks, s);
   }
   return hip_status(e);
 }

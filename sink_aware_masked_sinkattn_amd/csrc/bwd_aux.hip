@@ -195,7 +195,25 @@ __device__ __forceinline__ void store4<float>(float* dst, float4 v) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void sinkattn_convert(const float* dk_acc, const float* dv_acc,
-                                                        T* dk, T* dv, long long n_kv4, float scale) {
+                                                        T* dk, T* dv, long long n_kv4, float scale,
+                                                        const float* ds_part, int ds_used,
+                                                        int ds_stride, int heads, float* dsinks) {
+  // workgroup h < heads also forms ds_h from the dQ kernel's per-workgroup
+  // parts: each thread adds slots tid, tid + 256, ... in order, then the 256
+  // thread sums are added in thread order -- the same order every call
+  if ((int)blockIdx.x < heads) {
+    __shared__ float red[256];
+    const float* src = ds_part + (size_t)blockIdx.x * ds_stride;
+    float t = 0.0f;
+    for (int i = threadIdx.x; i < ds_used; i += 256) t += src[i];
+    red[threadIdx.x] = t;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) dsinks[blockIdx.x] = red[0];
+  }
   const long long stride = (long long)gridDim.x * blockDim.x;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n_kv4; i += stride) {
     float4 x = ((const float4*)dk_acc)[i];
@@ -262,18 +280,24 @@ hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const v
   return hipGetLastError();
 }
 
+// heads > 0: also dsinks[h] = sum of ds_part[h * ds_stride + 0 .. ds_used).
 hipError_t launch_convert(int dtype_is_f32, const float* dk_acc, const float* dv_acc, void* dk,
-                          void* dv, long long n_kv, float scale, hipStream_t stream) {
+                          void* dv, long long n_kv, float scale, const float* ds_part,
+                          int ds_used, int ds_stride, int heads, float* dsinks,
+                          hipStream_t stream) {
   const long long n4 = n_kv / 4;
-  if (n4 == 0) return hipSuccess;
+  if (n4 == 0 && heads <= 0) return hipSuccess;
   long long blocks = (n4 + 255) / 256;
   if (blocks > 256 * 16) blocks = 256 * 16;
+  if (blocks < heads) blocks = heads;
   if (dtype_is_f32) {
     hipLaunchKernelGGL(sinkattn_convert<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       dk_acc, dv_acc, (float*)dk, (float*)dv, n4, scale);
+                       dk_acc, dv_acc, (float*)dk, (float*)dv, n4, scale, ds_part, ds_used,
+                       ds_stride, heads, dsinks);
   } else {
     hipLaunchKernelGGL(sinkattn_convert<bf16>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       dk_acc, dv_acc, (bf16*)dk, (bf16*)dv, n4, scale);
+                       dk_acc, dv_acc, (bf16*)dk, (bf16*)dv, n4, scale, ds_part, ds_used,
+                       ds_stride, heads, dsinks);
   }
   return hipGetLastError();
 }

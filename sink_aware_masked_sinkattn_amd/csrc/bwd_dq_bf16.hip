@@ -63,7 +63,10 @@ struct DqArgs {
   const bf16* o;
   const float* lse;       // forward log-sum-exp (natural log, content keys only)
   const float* sinks;
-  float* dsinks;          // accumulated into (cleared beforehand)
+  float* ds_part;         // [Hq, ds_stride] this launch's per-workgroup parts of ds_h:
+                          // slot z * num_q_tiles + qt of each head (the finish
+                          // kernel adds a head's slots in index order)
+  int ds_stride;
   float* l2_ws;           // [Hq, rows] L in log2 units (L * log2 e), written here
   float* d_ws;            // [Hq, rows] D, written here
   float* dk_acc;          // [rows, Hkv, D] fp32 dK / dV accumulators, zeroed here
@@ -229,7 +232,11 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
   const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
   const int q_start = qt * BQ;
-  if (q_start >= sv.len) return;
+  const size_t ds_slot = (size_t)h * a.ds_stride + (size_t)z * a.num_q_tiles + qt;
+  if (q_start >= sv.len) {   // no rows here: this workgroup's part of ds_h is 0
+    if (threadIdx.x == 0) a.ds_part[ds_slot] = 0.0f;
+    return;
+  }
   const int q_last = min(q_start + BQ - 1, sv.len - 1);
   const int kvh = h / a.group;
 
@@ -366,9 +373,19 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
       a.l2_ws[wi] = l2[qb];
     }
   }
+  // this workgroup's part of ds_h: its waves' sums in wave order, into its
+  // slot (no atomics: the finish kernel adds the slots in a fixed order)
+  __shared__ float ds_red[WAVES];
 #pragma unroll
   for (int w = 1; w < 64; w <<= 1) ds_part += __shfl_xor(ds_part, w);
-  if (lane == 0 && wave_active) unsafeAtomicAdd(a.dsinks + h, ds_part);
+  if (lane == 0) ds_red[wave] = wave_active ? ds_part : 0.0f;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) t += ds_red[w];
+    a.ds_part[ds_slot] = t;
+  }
   // Zero this workgroup's share of the fp32 dK / dV accumulators (the dK/dV
   // kernel adds into them): rows of the tile congruent to h mod group, so the
   // group's query heads split the kv head's rows between them.
@@ -421,7 +438,12 @@ void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
   const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
   const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
   const int q_start = qt * 32;
-  if (q_start >= sv.len) return;
+  const size_t ds_slot = (size_t)z * a.num_q_tiles + qt;   // + h * ds_stride
+  if (q_start >= sv.len) {   // no rows here: the group's parts of ds_h are 0
+    for (int i = threadIdx.x; i < a.group; i += WAVES * 64)
+      a.ds_part[(size_t)(kvh * a.group + i) * a.ds_stride + ds_slot] = 0.0f;
+    return;
+  }
   const int q_last = min(q_start + 31, sv.len - 1);
 
   const int tid = threadIdx.x;
@@ -545,9 +567,10 @@ void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
       a.d_ws[wi] = dd[0];
       a.l2_ws[wi] = l2[0];
     }
+    // this head's part of ds_h from this block: one wave per head, its slot
 #pragma unroll
     for (int w = 1; w < 64; w <<= 1) ds_part += __shfl_xor(ds_part, w);
-    if (lane == 0) unsafeAtomicAdd(a.dsinks + h, ds_part);
+    if (lane == 0) a.ds_part[(size_t)h * a.ds_stride + ds_slot] = ds_part;
   }
   // clear the fp32 dK / dV accumulators of the block's rows for this kv head
   // (the dK/dV kernel adds into them)
@@ -583,15 +606,22 @@ bool dq_window_kernel(int seqlen, int group, int window, int prefix) {
   return pre + win <= WIN_TILES;
 }
 
+// Rows per query tile of the dQ kernel the launcher picks (the sink
+// gradient's slots per head are batch * ceil(seqlen / rows)).
+int dq_query_tile(int seqlen, int group, int window, int prefix) {
+  if (dq_window_kernel(seqlen, group, window, prefix)) return 32;
+  return fwd_key_tile(window) == 32 ? DqTiles<1, SA_DQ_QB_K32>::BQ : DqTiles<2, SA_DQ_QB>::BQ;
+}
+
 hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
                                   const bf16* o, const float* lse, const float* sinks,
-                                  float* dsinks, float* l_ws, float* d_ws, float* dk_acc,
+                                  float* ds_part, int ds_stride, float* l_ws, float* d_ws, float* dk_acc,
                                   float* dv_acc, bf16* dq, const int* cu_seqlens, int batch,
                                   int seqlen, int rows_total, int heads_q, int heads_kv, int window,
                                   int prefix, float scale, hipStream_t stream) {
   DqArgs a;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.o = o; a.lse = lse; a.sinks = sinks;
-  a.dsinks = dsinks; a.l2_ws = l_ws; a.d_ws = d_ws; a.dk_acc = dk_acc; a.dv_acc = dv_acc;
+  a.ds_part = ds_part; a.ds_stride = ds_stride; a.l2_ws = l_ws; a.d_ws = d_ws; a.dk_acc = dk_acc; a.dv_acc = dv_acc;
   a.dq = dq;
   a.lse_head_stride = cu_seqlens ? rows_total : seqlen;
   a.cu_seqlens = cu_seqlens;
