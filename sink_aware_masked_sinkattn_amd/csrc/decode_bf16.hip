@@ -28,11 +28,14 @@
 //  * single pass (every sequence's visible keys fit one workgroup, e.g.
 //    short windows): a workgroup (4 waves) takes one (sequence, kv head),
 //    the waves' (m, r, acc) merge in LDS and the sink is applied there;
-//  * stream (long caches): the chunks of all (sequence, kv head) segments
-//    form one flat list and every wave of the grid takes an equal run of it,
-//    so no wave waits for another and all finish together; each wave writes
-//    one partial per segment it touches and a second kernel merges a
-//    segment's partials and applies the sink:
+//  * stream (long caches): each (sequence, kv head) segment's chunks are cut
+//    into blocks of at most qc chunks (qc chosen on the device so the blocks
+//    fit the grid), listed by sequence, block and kv head; wave w takes
+//    block w, so waves carry equal work, neighbouring waves read the same
+//    cache rows for neighbouring kv heads, and the next chunk's loads
+//    overlap the current one's arithmetic.  Each wave writes its block's
+//    partial (m, r, acc); a second kernel merges a segment's blocks and
+//    applies the sink:
 //      O = acc / (r + exp(s_h - m)),  l = m + log r    (log2 units inside).
 // The decode step is bound by HBM (each visible K/V row is read once); the
 // MFMA work is small next to it.
