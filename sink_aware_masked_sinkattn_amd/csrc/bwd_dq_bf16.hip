@@ -21,6 +21,13 @@
 //   operand of dQ^T = K^T dS^T; the A operand (keys along k) is a transpose
 //   read of the row-major K tile.  dQ^T's C layout gives each lane runs of 4
 //   consecutive head dims of its query, stored 8 bytes at a time.
+//
+// Short windows with GQA groups of a multiple of 4 run a variant that keeps
+// a 32-row block's key tiles resident in LDS for all the group's heads
+// (sinkattn_bwd_dq_bf16_d64_win, below).  Every kernel here also writes the
+// backward's row statistics (D, L) for the dK/dV kernel and its parts of the
+// sink gradient ds_h into per-workgroup slots (no atomics; the finish kernel
+// adds them in a fixed order).
 #include "common.h"
 #include "mask_tiles.h"
 
