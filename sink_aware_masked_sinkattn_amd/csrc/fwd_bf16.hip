@@ -29,7 +29,8 @@
 //     V row-major and read transposed with ds_read_tr16_b64;
 //   * S^T = K Q^T puts one query per lane (C layout), so the row max / sum
 //     need only a 32-lane swap, and the probabilities convert in registers
-//     into the B operand of O^T += V^T P^T;
+//     into the B operand of O^T += V^T P^T (with 64-key tiles a 16x16x32
+//     MFMA against a 0/1 selector also forms the row sums from them);
 //   * each wave classifies every key tile against its own rows: skipped
 //     tiles cost nothing, full tiles run mask-free, partial tiles apply the
 //     element predicate;
@@ -86,6 +87,25 @@ struct FwdArgs {
   float scale_log2;          // softmax_scale * log2(e)
 };
 
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// A operand of the 16x16x32 MFMA that sums probabilities per query.  Fed a
+// P^T register of the 32x32 layout (lane l: query l%32 and 8 of the 16 keys
+// of a k-step, which 8 set by l/32), the 16x16x32 product reads lane l as
+// column l%16 of k-group l/16, so k-groups {0,2} carry queries 0..15 and
+// {1,3} queries 16..31.  Ones in A rows m = 0, 4, 8, 12 over the k-groups of
+// parity (m/4)%2 put the sum for query n + 16*((m/4)%2) at row m, column n;
+// since the C layout gives lane l rows 4*(l/16)+i of column l%16, register 0
+// of every lane ends up holding the sum for that lane's own query.
+__device__ __forceinline__ bf16x8 row_sum_selector(int lane) {
+  const int m = lane & 15;
+  const bool one = (m & 3) == 0 && ((m >> 2) & 1) == ((lane >> 4) & 1);
+  const bf16 v = one ? (bf16)1.0f : (bf16)0.0f;
+  return bf16x8{v, v, v, v, v, v, v, v};
+}
+
 __device__ __forceinline__ int map_head(int x, int heads_q) {
   // consecutive workgroups land on consecutive XCDs (8): give XCD c the
   // contiguous head range [c*Hq/8, (c+1)*Hq/8) so a kv-group stays in one L2
@@ -98,8 +118,15 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
 template <int NKB, int QB, bool MASK>
 __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB][4],
                                           f32x16 (&acc)[QB][2], float (&m_run)[QB],
-                                          float (&r_run)[QB], int qw0, int k0, int window,
+                                          f32x4 (&rsum)[QB], bf16x8 rsel, int qw0, int k0, int window,
                                           int prefix, float scale_log2, int lane) {
+  // Row sums of the probabilities: for 64-key tiles on the matrix cores, from
+  // the same bf16 P^T registers the PV product uses (8 small MFMAs instead of
+  // 64 fp32 adds per lane; this kernel is VALU-bound), so the denominator is
+  // the sum of exactly the weights applied to V.  The 32-key kernels run at 4
+  // waves per SIMD and have no registers for the extra accumulators; they add
+  // in fp32 per lane (register 0 of rsum, a partial over this lane's keys).
+  constexpr bool MSUM = NKB == 2;
   const int l32 = lane & 31;
   const int g = lane >> 5;
   const int grp = lane >> 4;
@@ -168,7 +195,7 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
       const float m_new = fmaxf(m_run[qb], mx);
       const float corr = fast_exp2(m_run[qb] - m_new);
       m_run[qb] = m_new;
-      r_run[qb] *= corr;
+      rsum[qb][0] *= corr;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -182,12 +209,12 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         p[i] = fast_exp2(fmaf(st[kb][qb][i], scale_log2, -m_use));
-        rs += p[i];
+        if (!MSUM) rs += p[i];
       }
       pf[kb][qb][0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
       pf[kb][qb][1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
     }
-    r_run[qb] += rs;
+    if (!MSUM) rsum[qb][0] += rs;
   }
   // ---- O^T += V^T P^T
 #pragma unroll
@@ -198,6 +225,14 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32x32x16(vt[db][kb][hh], pf[kb][qb][hh], acc[qb][db]);
+  if (MSUM) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) rsum[qb] = mfma16x16x32(rsel, pf[kb][qb][hh], rsum[qb]);
+  }
 }
 
 #ifndef SA_FWD_OCC
@@ -277,14 +312,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   };
 
   f32x16 acc[QB][2];
-  float m_run[QB], r_run[QB];
+  f32x4 rsum[QB];
+  float m_run[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     acc[qb][0] = f32x16{};
     acc[qb][1] = f32x16{};
+    rsum[qb] = f32x4{};
     m_run[qb] = -1.0e30f;   // finite start: exp2(S - m) never sees (-inf) - (-inf)
-    r_run[qb] = 0.0f;
   }
+  const bf16x8 rsel = row_sum_selector(lane);
 
   load_tile(0, 0);
   wait_all_mem();
@@ -299,9 +336,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
                                 : SA_TILE_SKIP;
     const uint32_t ktile = lds_addr(smem + (2 * buf) * TILE_ELEMS);   // V tile follows
     if (cls == SA_TILE_FULL) {
-      tile_step<NKB, QB, false>(ktile, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, QB, false>(ktile, qf, acc, m_run, rsum, rsel, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     } else if (cls == SA_TILE_PARTIAL) {
-      tile_step<NKB, QB, true>(ktile, qf, acc, m_run, r_run, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, QB, true>(ktile, qf, acc, m_run, rsum, rsel, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     }
     wait_all_mem();
     __syncthreads();
@@ -313,7 +350,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   const float sink_l2 = a.sinks[h] * SA_LOG2E;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float r_tot = halves_sum(r_run[qb]);
+    const float r_tot = NKB == 2 ? rsum[qb][0] : halves_sum(rsum[qb][0]);
     const float denom = r_tot + fast_exp2(sink_l2 - m_run[qb]);
     const float inv = 1.0f / denom;
     const int qrow = qw0 + qb * 32 + l32;

@@ -24,10 +24,15 @@ import torch
 import oracle
 from sink_aware_masked_sinkattn_amd import sinkattn_bwd, sinkattn_fwd
 
+# bf16 l: the training forward's denominator is the fp32 sum of the
+# bf16-rounded (RNE) probabilities that also weight V, each within 2^-9 of
+# its value, so l = m + ln(sum) is within ln(1 + 2^-9) = 1.951e-3.  The decode
+# kernels sum in fp32 and keep the tighter bound.
 TOL = {
     "fp32": {"o": 1e-5, "lse": 1e-5, "dq": 1e-5, "dk": 1e-5, "dv": 1e-5, "ds": 1e-5},
-    "bf16": {"o": 2e-2, "lse": 1e-3, "dq": 2e-2, "dk": 2e-2, "dv": 2e-2, "ds": 2e-2},
+    "bf16": {"o": 2e-2, "lse": 2e-3, "dq": 2e-2, "dk": 2e-2, "dv": 2e-2, "ds": 2e-2},
 }
+DECODE_LSE_TOL = 1e-3
 
 
 def log(msg: str):

@@ -4,14 +4,16 @@ train-inference consistency the rollout engine needs: decode on a cache of n
 tokens equals row n - 1 of the training forward kernel.
 
 Tolerances as in tests/parity_util.py: O max-abs <= 2e-2 (max(2e-2,
-max|ref|/64) for inputs outside the named workloads), lse <= 1e-3.
+max|ref|/64) for inputs outside the named workloads), lse <= 1e-3 (the decode
+kernels sum the probabilities in fp32); against the training forward, the
+forward's bf16 bound on l (2e-3).
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from parity_util import TOL, log
+from parity_util import DECODE_LSE_TOL, TOL, log
 from sink_aware_masked_sinkattn_amd import sinkattn_decode, sinkattn_fwd
 from workloads import (DECODE_WORKLOADS, WINDOW_INF, decode_workload_inputs, make_decode_inputs,
                        make_inputs)
@@ -45,7 +47,7 @@ def check(o, lse, ro, rl, label, scaled):
     err_l = float(np.abs(lse[fin] - rl[fin]).max()) if fin.any() else 0.0
     log(f"{label}: max|dO| {err_o:.3g} (tol {tol_o:.3g}), max|dl| {err_l:.3g}")
     assert err_o <= tol_o, label
-    assert err_l <= TOL["bf16"]["lse"], label
+    assert err_l <= DECODE_LSE_TOL, label
 
 
 SMALL = [
@@ -131,7 +133,7 @@ def test_decode_matches_training_forward_row(w, p):
         worst_l = max(worst_l, float((l_dec[b] - l_fw[0, :, n - 1]).abs().max()))
     log(f"decode vs forward row (w={w}, p={p}): max|dO| {worst_o:.3g}, max|dl| {worst_l:.3g}")
     assert worst_o <= TOL["bf16"]["o"]
-    assert worst_l <= TOL["bf16"]["lse"]
+    assert worst_l <= TOL["bf16"]["lse"]   # the forward's l carries the looser bound
 
 
 @pytest.mark.slow
