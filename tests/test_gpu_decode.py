@@ -6,7 +6,7 @@ tokens equals row n - 1 of the training forward kernel.
 Tolerances as in tests/parity_util.py: O max-abs <= 2e-2 (max(2e-2,
 max|ref|/64) for inputs outside the named workloads), lse <= 1e-3 (the decode
 kernels sum the probabilities in fp32); against the training forward, the
-forward's bf16 bound on l (2e-3).
+forward's bf16 bound on l (4e-3).
 """
 import numpy as np
 import pytest

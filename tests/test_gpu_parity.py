@@ -40,6 +40,9 @@ SMALL = [
     # windows >= 1024 after clamping run the wide-tile kernels (64-key forward /
     # dQ tiles, 128-row dK/dV tiles); shorter ones the narrow-tile kernels
     (1, 1100, 4, 2, WINDOW_INF, 0, 0.5),
+    # large logits: frequent lazy rescales of the 64-key forward's output and
+    # matrix-core row sums, probabilities spread over many binades
+    (1, 1100, 4, 2, WINDOW_INF, 0, 2.0),
     (1, 1090, 4, 1, 1030, 70, 0.5),
     (2, 1200, 4, 2, 2000, 3, 0.5),
 ]
