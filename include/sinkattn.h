@@ -100,10 +100,10 @@ typedef struct {
 /*
  * Forward.  Reads q, k, v, sinks; writes o and (if lse != NULL) lse.
  * lse may be NULL when no backward will follow (inference).  For bf16 with
- * 64-key tiles (min(w, seqlen) >= 1024; seqlen is the padded length for
- * varlen) the softmax denominator is the
- * sum of the bf16-rounded probabilities that weight V, so lse is within
- * ln(1 + 2^-8) = 3.9e-3 of its exact value; the other paths sum in fp32.
+ * 64-key tiles (min(w, seqlen) >= 1024, seqlen as in sinkattn_problem) the
+ * softmax denominator is the sum of the bf16-rounded probabilities that
+ * weight V, so lse is within ln(1 + 2^-8) = 3.9e-3 of its exact value; the
+ * other paths sum in fp32.
  */
 sinkattn_status sinkattn_fwd(const sinkattn_problem *problem, const void *q,
                              const void *k, const void *v, const float *sinks,
