@@ -38,11 +38,14 @@ Readings where the pages leave a step open:
     input that depends on theta).  J is continuous in rho but its derivative
     jumps where the clip becomes active: the clip counts as active when
     (A > 0 and rho > 1 + eps_c) or (A < 0 and rho < 1 - eps_c), and then
-    dJ/dlogp = 0, else dJ/dlogp = A rho.  That decision is taken the way the
-    kernel takes it, in its precision: the fp32 difference
-    logp_theta - logp_old against the fp32 thresholds log(1 + eps_c) and
-    log(1 - eps_c) (an exact difference for the close log-probs of one token).
-    The loss value itself is the literal min of eq. 6, in fp64.
+    dJ/dlogp = 0, else dJ/dlogp = A rho.  The decision is taken on the given
+    log-probabilities in exact arithmetic: rho > 1 + eps_c is
+    logp_theta - logp_old > log(1 + eps_c), with the difference of the two
+    (fp32) inputs formed in fp64, where it is exact, and the bound
+    log1p(eps_c) in fp64 (within one fp64 ulp of log(1 + eps_c); a
+    difference that lands inside that ulp is not a case any fp32 input
+    reaches except by construction).  The loss value itself is the literal
+    min of eq. 6, in fp64.
 """
 from __future__ import annotations
 
@@ -71,14 +74,14 @@ def group_advantages(rewards, group_size: int, eps_adv: float) -> np.ndarray:
 
 
 def clip_thresholds(eps_clip: float):
-    """The fp32 log-domain clip bounds the decision is taken against: log(1 +- eps_c)."""
-    return np.float32(math.log1p(eps_clip)), np.float32(math.log1p(-eps_clip))
+    """The log-domain clip bounds log(1 + eps_c) and log(1 - eps_c), in fp64."""
+    return math.log1p(eps_clip), math.log1p(-eps_clip)
 
 
 def clip_active(logp_new: float, logp_old: float, adv: float, eps_clip: float) -> bool:
     """Whether the clipped term of eq. 6 is the strictly smaller one (see the header)."""
     hi, lo = clip_thresholds(eps_clip)
-    d = np.float32(np.float32(logp_new) - np.float32(logp_old))
+    d = float(logp_new) - float(logp_old)
     return bool((adv > 0 and d > hi) or (adv < 0 and d < lo))
 
 
@@ -134,8 +137,8 @@ def grpo_loss(logp_new, logp_old, logp_ref, action_mask, rewards, cu_seqlens: Se
             rho = np.exp(nw - od)                                       # eq. 4
             rho_bar = np.clip(rho, 1.0 - eps_clip, 1.0 + eps_clip)      # eq. 5
             j_sum += np.minimum(rho * a, rho_bar * a).sum()             # eq. 6
-            # clip decision on the fp32 log-ratio (clip_active, elementwise)
-            d = nw.astype(np.float32) - od.astype(np.float32)
+            # clip decision on the exact log-ratio (clip_active, elementwise)
+            d = nw - od
             active = (d > hi) if a > 0 else ((d < lo) if a < 0 else np.zeros(d.shape, bool))
             dj = np.where(active, 0.0, a * rho)
             dkl = np.zeros_like(rho)

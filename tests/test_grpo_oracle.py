@@ -2,6 +2,7 @@
 "Policy update", eq. 3-7) against what the equations and the mathematics fix: closed forms,
 numpy's population standard deviation, central finite differences of the loss, and the
 structure of the batch (mask, groups).  CPU only."""
+import decimal
 import math
 
 import numpy as np
@@ -156,18 +157,65 @@ def test_batch_is_mean_of_groups():
         assert np.allclose(gm / 3, grad[sl], rtol=1e-13, atol=0)
 
 
-def test_clip_decision_in_fp32_log_domain():
-    hi, lo = oracle.clip_thresholds(0.2)
-    assert hi == np.float32(math.log(1.2)) and lo == np.float32(math.log(0.8))
-    # just above / below the upper bound, decided on the fp32 difference
-    above = float(np.nextafter(hi, np.float32(1)))
-    assert oracle.clip_active(above, 0.0, 1.0, 0.2)
-    assert not oracle.clip_active(float(hi), 0.0, 1.0, 0.2)
-    assert not oracle.clip_active(above, 0.0, -1.0, 0.2)
-    below = float(np.nextafter(lo, np.float32(-1)))
-    assert oracle.clip_active(below, 0.0, -1.0, 0.2)
-    assert not oracle.clip_active(below, 0.0, 1.0, 0.2)
-    assert not oracle.clip_active(5.0, 0.0, 0.0, 0.2)
+def _exact_clip_active(new32, old32, adv, eps):
+    """rho > 1 + eps (A > 0) or rho < 1 - eps (A < 0) decided with 60-digit decimals:
+    the fp32 inputs are exact binary fractions and log(1 +- eps) is evaluated to far
+    beyond any fp32 or fp64 rounding (eq. 5-6 of the "Policy update" paragraph)."""
+    with decimal.localcontext() as ctx:
+        ctx.prec = 60
+        d = decimal.Decimal(float(new32)) - decimal.Decimal(float(old32))
+        e = decimal.Decimal(float(eps))
+        hi = (1 + e).ln()
+        lo = (1 - e).ln()
+        return bool((adv > 0 and d > hi) or (adv < 0 and d < lo))
+
+
+def test_clip_decision_is_exact_near_the_threshold():
+    f32 = np.float32
+    fp32_disagrees = 0
+    for eps in (0.25, float(f32(0.2)), 0.125, float(f32(0.28))):
+        cases = []
+        for bound in (math.log1p(eps), math.log1p(-eps)):
+            b32 = f32(bound)
+            # fp32 log-probs bracketing the bound, as the difference from logp_old = 0 ...
+            for x in (np.nextafter(b32, f32(-1)), b32, np.nextafter(b32, f32(1))):
+                cases.append((f32(x), f32(0.0)))
+            # ... and from a logp_old of another magnitude, where the fp32 difference rounds
+            for old in (f32(-1e-3), f32(-3.7), f32(-0.0625)):
+                new = f32(float(old) + bound)
+                for x in (np.nextafter(new, f32(-10)), new, np.nextafter(new, f32(10))):
+                    cases.append((f32(x), old))
+        for new, old in cases:
+            for adv in (1.0, -1.0, 0.0):
+                want = _exact_clip_active(new, old, adv, eps)
+                assert oracle.clip_active(float(new), float(old), adv, eps) == want, \
+                    (eps, float(new), float(old), adv)
+                d32 = f32(new - old)
+                hi32, lo32 = f32(math.log1p(eps)), f32(math.log1p(-eps))
+                fp32_rule = bool((adv > 0 and d32 > hi32) or (adv < 0 and d32 < lo32))
+                fp32_disagrees += fp32_rule != want
+    # the straddling cases include ones that a decision in fp32 gets wrong
+    assert fp32_disagrees > 0
+
+
+def test_clip_straddling_rollout_by_hand():
+    # one group of two rollouts (rewards 1, 0: A = +1, -1 for eps_A = 0), beta = 0,
+    # eps_c = 1/4: the clip bound is log(5/4) = 0.22314355131420976.  Rollout 0 holds two
+    # tokens 2^-23 on either side of it (logp_old = 0); rollout 1 one token well inside.
+    # By eq. 6: J = min(rho A, clip(rho) A); dJ/dlogp = A rho where the clip is inactive,
+    # 0 where active; the loss gradient is -dJ/dlogp / S with S = 3 optimised tokens.
+    below, above = 0.22314355131420976 - 2.0 ** -23, 0.22314355131420976 + 2.0 ** -23
+    new = np.array([below, above, 0.1], np.float32)
+    old = np.zeros(3, np.float32)
+    loss, grad, adv, _ = oracle.grpo_loss(new, old, None, None, [1.0, 0.0], [0, 2, 3], 2,
+                                          0.0, 0.25, 0.0)
+    assert list(adv) == [1.0, -1.0]
+    rho = np.exp(new.astype(np.float64))
+    assert math.isclose(grad[0], -rho[0] / 3, rel_tol=1e-15)   # below the bound: A rho
+    assert grad[1] == 0.0                                        # above it: clipped
+    assert math.isclose(grad[2], rho[2] / 3, rel_tol=1e-15)    # A = -1, rho inside the band
+    j = rho[0] + 1.25 - rho[2]
+    assert math.isclose(loss, -j / 3, rel_tol=1e-15)
 
 
 def test_token_counts_are_optimised_tokens():
