@@ -118,6 +118,125 @@ def attend_head_grad(q, k, v, sink: float, window: int, prefix: int, scale: floa
     return dq, dk, dv, dsink
 
 
+def _candidate_keys(r_lo: int, r_hi: int, n: int, window: int, prefix: int) -> np.ndarray:
+    """Every key that a row in [r_lo, r_hi] may see: the prefix keys [0, min(p, r_hi + 1))
+    and the window keys [max(0, r_lo - w), r_hi] ([SUM] mask).  A superset; the mask
+    itself is applied to every (row, key) pair afterwards."""
+    pre = np.arange(min(prefix, r_hi + 1, n))
+    win = np.arange(max(0, r_lo - window), min(r_hi, n - 1) + 1)
+    return np.union1d(pre, win)
+
+
+def rows_head(q, k, v, sink: float, window: int, prefix: int, scale: float, rows,
+              do=None, chunk: int = 256):
+    """Forward (and, with ``do``, dq and the row statistics) of one sequence and one
+    query head at the given query rows only.
+
+    The same definition as ``attend_head`` / ``attend_head_grad`` restricted to those
+    rows: each row attends to its visible keys ([SUM] mask), gathered from the
+    candidate range of its chunk of rows, so the cost is that of the visible pairs of
+    the chosen rows.  Returns a dict with o [R, d], l [R] and, with do, dq [R, d],
+    big_l [R] (logaddexp(l, s)) and d_row [R] (dO . O).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, d = q.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    out = {"o": np.zeros((rows.size, d)), "l": np.zeros(rows.size)}
+    if do is not None:
+        do = np.asarray(do, dtype=np.float64)
+        out.update(dq=np.zeros((rows.size, d)), big_l=np.zeros(rows.size),
+                   d_row=np.zeros(rows.size))
+    order = np.argsort(rows, kind="stable")
+    for c0 in range(0, rows.size, chunk):
+        sel = order[c0:c0 + chunk]
+        r = rows[sel]
+        cand = _candidate_keys(int(r.min()), int(r.max()), n, window, prefix)
+        vis = (cand[None, :] <= r[:, None]) & (
+            (r[:, None] - cand[None, :] <= window) | (cand[None, :] < prefix))
+        s_mat = np.where(vis, scale * (q[r] @ k[cand].T), -np.inf)
+        rowmax = s_mat.max(axis=1)
+        e = np.exp(s_mat - rowmax[:, None])
+        z = e.sum(axis=1)
+        l = rowmax + np.log(z)
+        alpha = 1.0 / (1.0 + np.exp(np.float64(sink) - l))
+        o = alpha[:, None] * ((e @ v[cand]) / z[:, None])
+        out["o"][sel] = o
+        out["l"][sel] = l
+        if do is not None:
+            big_l = np.logaddexp(l, np.float64(sink))
+            p_prime = np.exp(s_mat - big_l[:, None])
+            d_row = np.sum(do[r] * o, axis=1)
+            ds_mat = p_prime * (do[r] @ v[cand].T - d_row[:, None])
+            out["dq"][sel] = scale * (ds_mat @ k[cand])
+            out["big_l"][sel] = big_l
+            out["d_row"][sel] = d_row
+    return out
+
+
+def key_grads_head(q, k, v, sink: float, window: int, prefix: int, scale: float, do, keys,
+                   chunk: int = 256, row_stats=None):
+    """dk and dv of one sequence and one query head at the given key positions only.
+
+    The rows that can see any of the keys are evaluated in full with ``rows_head`` (their
+    l, O, L = logaddexp(l, s) and D = dO . O over all their visible keys); then, chunk by
+    chunk of keys, on the rows that can see the chunk: P' = exp(S - L),
+    dS = P' (dO . v - D), dk_j = scale sum_i dS_ij q_i and dv_j = sum_i P'_ij dO_i -- the
+    chain rule of the module docstring restricted to the chosen keys.  ``row_stats``:
+    the result of ``rows_head`` with ``do`` over every row 0 .. n-1 of the same
+    inputs, to reuse instead of recomputing.  Returns (dk [K, d], dv [K, d]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n, d = q.shape
+    keys = np.asarray(keys, dtype=np.int64)
+    dk = np.zeros((keys.size, d))
+    dv = np.zeros((keys.size, d))
+    if keys.size == 0:
+        return dk, dv
+
+    def rows_seeing(j_lo, j_hi):
+        # rows i >= j_lo with i - j <= w for some key j <= j_hi, or every later row
+        # when a prefix key is among them
+        return j_lo, (n - 1 if j_lo < prefix else min(n - 1, j_hi + window))
+
+    if row_stats is not None:
+        r_lo, st = 0, row_stats
+    else:
+        r_lo, r_hi = rows_seeing(int(keys.min()), int(keys.max()))
+        st = rows_head(q, k, v, sink, window, prefix, scale, np.arange(r_lo, r_hi + 1),
+                       do=do, chunk=chunk)
+    order = np.argsort(keys, kind="stable")
+    for c0 in range(0, keys.size, chunk):
+        sel = order[c0:c0 + chunk]
+        j = keys[sel]
+        a, b = rows_seeing(int(j.min()), int(j.max()))
+        rows = np.arange(a, b + 1)
+        big_l = st["big_l"][rows - r_lo]
+        d_row = st["d_row"][rows - r_lo]
+        vis = (j[None, :] <= rows[:, None]) & (
+            (rows[:, None] - j[None, :] <= window) | (j[None, :] < prefix))
+        s_mat = np.where(vis, scale * (q[rows] @ k[j].T), -np.inf)
+        p_prime = np.exp(s_mat - big_l[:, None])
+        ds_mat = p_prime * (do[rows] @ v[j].T - d_row[:, None])
+        dk[sel] = scale * (ds_mat.T @ q[rows])
+        dv[sel] = p_prime.T @ do[rows]
+    return dk, dv
+
+
+def sink_grad_head(q, k, v, sink: float, window: int, prefix: int, scale: float, do) -> float:
+    """ds of one sequence and one query head: -sum_i exp(s - L_i) D_i over all its rows
+    ([RETRO] per-head sink gradient), with every row evaluated by ``rows_head``."""
+    n = np.asarray(q).shape[0]
+    if n == 0:
+        return 0.0
+    st = rows_head(q, k, v, sink, window, prefix, scale, np.arange(n), do=do)
+    return -float(np.sum(np.exp(np.float64(sink) - st["big_l"]) * st["d_row"]))
+
+
 def _sequences(q, cu_seqlens):
     """Yield (batch_index_or_None, row_slice) for each sequence."""
     if cu_seqlens is None:

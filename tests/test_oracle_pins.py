@@ -147,6 +147,59 @@ def test_backward_equals_explicit_sink_autograd(n, d, w, p):
     np.testing.assert_allclose(ds, sa.grad.item(), rtol=1e-10, atol=1e-12)
 
 
+# ------------------------------------- row- and key-restricted forms
+# rows_head / key_grads_head / sink_grad_head evaluate the same definition at
+# chosen rows or keys only (what full-size GPU comparisons use); pinned here
+# to the explicit-sink formulation and its fp64 autograd, on every row and key
+# and on subsets, with small chunks so that the per-chunk candidate ranges are
+# exercised.
+
+RESTRICTED = [
+    # n, d, w, p
+    (23, 4, 2, 3),
+    (30, 8, 0, 0),
+    (30, 8, WINDOW_INF, 0),
+    (17, 5, 1, 40),
+    (40, 3, 6, 1),
+    (25, 4, 9, 25),
+    (1, 4, 0, 0),
+]
+
+
+@pytest.mark.parametrize("n,d,w,p", RESTRICTED)
+def test_restricted_forms_equal_explicit_sink_autograd(n, d, w, p):
+    g = torch.Generator().manual_seed(300 + n * d + p)
+    q, k, v, do = (torch.randn(n, d, generator=g, dtype=torch.float64) for _ in range(4))
+    sink = -0.4
+    scale = 1.0 / math.sqrt(d)
+    qa, ka, va, sa = (t.clone().requires_grad_(True) for t in (q, k, v,
+                                                               torch.tensor(sink, dtype=torch.float64)))
+    out = _explicit_sink_attention(qa, ka, va, sa, w, p, scale)
+    (out * do).sum().backward()
+    vis = _mask_from_ranges(n, w, p)
+    scores = scale * (q @ k.T).numpy()
+    l_ref = np.array([np.log(np.exp(scores[r][vis[r]]).sum()) for r in range(n)])
+    rng = np.random.default_rng(n + p)
+    qn, kn, vn, don = (t.numpy() for t in (q, k, v, do))
+    for rows in (np.arange(n), rng.choice(n, size=max(1, n // 3), replace=False)):
+        st = oracle.rows_head(qn, kn, vn, sink, w, p, scale, rows, do=don, chunk=4)
+        np.testing.assert_allclose(st["o"], out.detach().numpy()[rows], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(st["l"], l_ref[rows], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(st["dq"], qa.grad.numpy()[rows], rtol=1e-10, atol=1e-12)
+    for keys in (np.arange(n), np.arange(max(0, n - 5), n), np.arange(0, min(n, 3)),
+                 np.sort(rng.choice(n, size=max(1, n // 4), replace=False))):
+        dk, dv = oracle.key_grads_head(qn, kn, vn, sink, w, p, scale, don, keys, chunk=4)
+        np.testing.assert_allclose(dk, ka.grad.numpy()[keys], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv, va.grad.numpy()[keys], rtol=1e-10, atol=1e-12)
+        every = oracle.rows_head(qn, kn, vn, sink, w, p, scale, np.arange(n), do=don, chunk=5)
+        dk2, dv2 = oracle.key_grads_head(qn, kn, vn, sink, w, p, scale, don, keys, chunk=3,
+                                         row_stats=every)
+        np.testing.assert_allclose(dk2, ka.grad.numpy()[keys], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dv2, va.grad.numpy()[keys], rtol=1e-10, atol=1e-12)
+    ds = oracle.sink_grad_head(qn, kn, vn, sink, w, p, scale, don)
+    np.testing.assert_allclose(ds, sa.grad.item(), rtol=1e-10, atol=1e-12)
+
+
 # ------------------------------------------- reduction to plain attention
 
 @pytest.mark.parametrize("sink", [float("-inf"), -1.0e4])
