@@ -53,9 +53,13 @@
  *   - cu_seqlens contents are a caller contract, not checked: cu[0] = 0,
  *     non-decreasing, cu[batch] = total_tokens, every length <= seqlen.
  *   - No global mutable state: concurrent calls on different streams are safe.
- *   - The forward and dQ are bitwise reproducible.  ds_h (float atomics over
- *     waves) and, for long key ranges, dK/dV (float atomics over work chunks)
- *     are reproducible to rounding, not bitwise.
+ *   - Reproducibility.  bf16: o, lse, dq and dsinks are bitwise the same on
+ *     every call (dsinks is added from per-workgroup parts in a fixed order);
+ *     dk and dv are too where a kv block's work is one unit, and where it is
+ *     cut into several units (long key ranges, prefix keys) those add with
+ *     float atomics and agree to rounding only.  fp32: dsinks adds with float
+ *     atomics and agrees to rounding only; the other outputs are bitwise
+ *     the same.
  */
 #ifndef SINKATTN_H
 #define SINKATTN_H
@@ -99,11 +103,11 @@ typedef struct {
 
 /*
  * Forward.  Reads q, k, v, sinks; writes o and (if lse != NULL) lse.
- * lse may be NULL when no backward will follow (inference).  For bf16 with
- * 64-key tiles (min(w, seqlen) >= 1024, seqlen as in sinkattn_problem) the
- * softmax denominator is the sum of the bf16-rounded probabilities that
- * weight V, so lse is within ln(1 + 2^-8) = 3.9e-3 of its exact value; the
- * other paths sum in fp32.
+ * lse may be NULL when no backward will follow (inference).  lse is an
+ * fp32-accumulated log-sum-exp of the bf16 (or fp32) inputs: for bf16 the
+ * probabilities are added in fp32, or (64-key tiles, min(w, seqlen) >= 1024)
+ * as fp16 copies on the matrix cores, which keeps lse within
+ * ln(1 + 2^-11) = 4.9e-4 of the log of their fp32 sum.
  */
 sinkattn_status sinkattn_fwd(const sinkattn_problem *problem, const void *q,
                              const void *k, const void *v, const float *sinks,

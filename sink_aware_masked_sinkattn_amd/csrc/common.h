@@ -21,6 +21,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -74,6 +77,18 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
   bf16x4 lo = __builtin_shufflevector(b0, b1, 0, 1, 2, 3);
   bf16x4 hi = __builtin_shufflevector(b2, b3, 0, 1, 2, 3);
   return cat8(lo, hi);
+}
+// 8 fp32 -> 8 fp16, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ f16x8 to_f16x8(float a0, float a1, float a2, float a3, float a4,
+                                          float a5, float a6, float a7) {
+  f32x2 p0 = {a0, a1}, p1 = {a2, a3}, p2 = {a4, a5}, p3 = {a6, a7};
+  f16x2 b0 = __builtin_convertvector(p0, f16x2);
+  f16x2 b1 = __builtin_convertvector(p1, f16x2);
+  f16x2 b2 = __builtin_convertvector(p2, f16x2);
+  f16x2 b3 = __builtin_convertvector(p3, f16x2);
+  f16x4 lo = __builtin_shufflevector(b0, b1, 0, 1, 2, 3);
+  f16x4 hi = __builtin_shufflevector(b2, b3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 __device__ __forceinline__ bf16x4 to_bf16x4(float a0, float a1, float a2, float a3) {
   f32x2 p0 = {a0, a1}, p1 = {a2, a3};

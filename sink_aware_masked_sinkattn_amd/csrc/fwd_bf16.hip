@@ -30,7 +30,7 @@
 //   * S^T = K Q^T puts one query per lane (C layout), so the row max / sum
 //     need only a 32-lane swap, and the probabilities convert in registers
 //     into the B operand of O^T += V^T P^T (with 64-key tiles a 16x16x32
-//     MFMA against a 0/1 selector also forms the row sums from them);
+//     MFMA against a 0/1 selector also forms the row sums from fp16 copies);
 //   * each wave classifies every key tile against its own rows: skipped
 //     tiles cost nothing, full tiles run mask-free, partial tiles apply the
 //     element predicate;
@@ -87,8 +87,8 @@ struct FwdArgs {
   float scale_log2;          // softmax_scale * log2(e)
 };
 
-__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 // A operand of the 16x16x32 MFMA that sums probabilities per query.  Fed a
@@ -99,11 +99,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 // parity (m/4)%2 put the sum for query n + 16*((m/4)%2) at row m, column n;
 // since the C layout gives lane l rows 4*(l/16)+i of column l%16, register 0
 // of every lane ends up holding the sum for that lane's own query.
-__device__ __forceinline__ bf16x8 row_sum_selector(int lane) {
+// The probabilities enter this product as fp16 (11-bit significand, RNE):
+// each is within 2^-11 of its value, so l = m + ln(sum) is within
+// ln(1 + 2^-11) = 4.9e-4 of the log of the fp32 sum; with bf16 copies (the
+// ones that weight V) the bound would be ln(1 + 2^-8) = 3.9e-3.
+__device__ __forceinline__ f16x8 row_sum_selector(int lane) {
   const int m = lane & 15;
   const bool one = (m & 3) == 0 && ((m >> 2) & 1) == ((lane >> 4) & 1);
-  const bf16 v = one ? (bf16)1.0f : (bf16)0.0f;
-  return bf16x8{v, v, v, v, v, v, v, v};
+  const _Float16 v = one ? (_Float16)1.0f : (_Float16)0.0f;
+  return f16x8{v, v, v, v, v, v, v, v};
 }
 
 __device__ __forceinline__ int map_head(int x, int heads_q) {
@@ -118,14 +122,14 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
 template <int NKB, int QB, bool MASK>
 __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB][4],
                                           f32x16 (&acc)[QB][2], float (&m_run)[QB],
-                                          f32x4 (&rsum)[QB], bf16x8 rsel, int qw0, int k0, int window,
+                                          f32x4 (&rsum)[QB], f16x8 rsel, int qw0, int k0, int window,
                                           int prefix, float scale_log2, int lane) {
   // Row sums of the probabilities: for 64-key tiles on the matrix cores, from
-  // the same bf16 P^T registers the PV product uses (8 small MFMAs instead of
-  // 64 fp32 adds per lane; this kernel is VALU-bound), so the denominator is
-  // the sum of exactly the weights applied to V.  The 32-key kernels run at 4
-  // waves per SIMD and have no registers for the extra accumulators; they add
-  // in fp32 per lane (register 0 of rsum, a partial over this lane's keys).
+  // fp16 copies of the P^T registers the PV product uses (8 small MFMAs and 32
+  // packing converts instead of 64 fp32 adds per lane; this kernel is
+  // VALU-bound).  The 32-key kernels run at 4 waves per SIMD and have no
+  // registers for the extra accumulators; they add in fp32 per lane
+  // (register 0 of rsum, a partial over this lane's keys).
   constexpr bool MSUM = NKB == 2;
   const int l32 = lane & 31;
   const int g = lane >> 5;
@@ -183,6 +187,7 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
   }
   // ---- online softmax in the log2 domain, lazily rescaled
   bf16x8 pf[NKB][QB][2];
+  f16x8 hf[NKB][QB][2];   // fp16 copies of the probabilities for the row sums
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     float mx = st[0][qb][0];
@@ -213,6 +218,10 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
       }
       pf[kb][qb][0] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
       pf[kb][qb][1] = to_bf16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+      if (MSUM) {
+        hf[kb][qb][0] = to_f16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+        hf[kb][qb][1] = to_f16x8(p[8], p[9], p[10], p[11], p[12], p[13], p[14], p[15]);
+      }
     }
     if (!MSUM) rsum[qb][0] += rs;
   }
@@ -231,7 +240,7 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) rsum[qb] = mfma16x16x32(rsel, pf[kb][qb][hh], rsum[qb]);
+        for (int qb = 0; qb < QB; ++qb) rsum[qb] = mfma16x16x32_f16(rsel, hf[kb][qb][hh], rsum[qb]);
   }
 }
 
@@ -321,7 +330,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     rsum[qb] = f32x4{};
     m_run[qb] = -1.0e30f;   // finite start: exp2(S - m) never sees (-inf) - (-inf)
   }
-  const bf16x8 rsel = row_sum_selector(lane);
+  const f16x8 rsel = row_sum_selector(lane);
 
   load_tile(0, 0);
   wait_all_mem();

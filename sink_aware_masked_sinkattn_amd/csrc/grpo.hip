@@ -15,7 +15,8 @@
 // starts in, stages the next 256 rollout boundaries, advantages and token
 // weights 1 / (M S_g) in LDS (S_g summed from the group's counts), issues all
 // its loads (float4 per lane: a wave moves 1 KB per load) before the
-// arithmetic, finds each token's rollout by a binary search in LDS, and
+// arithmetic, finds each token's rollout by walking the LDS table forward
+// (tokens come in increasing order, so the position only moves ahead), and
 // writes the gradient and its loss partial.  grpo_loss_sum adds the partials
 // in index order, so the loss does not depend on which workgroups finish
 // first.

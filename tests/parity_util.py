@@ -6,7 +6,7 @@ Tolerances (written here once, used by every parity test):
   bf16 path : max |gpu - oracle| <= 2e-2 on O, dQ, dK, dV (the named
               workloads, whose inputs are 0.5 N(0,1));
               ds norm-wise relative max_h|d_h| / max_h|ref_h| <= 2e-2;
-              l max-abs <= 4e-3 (training forward, see TOL), 1e-3 (decode).
+              l max-abs <= 1e-3 (forward and decode).
 Extra bf16 cases outside the named workloads (other value scales, more
 extreme masks) use max(2e-2, max|ref| / 64) on O, dQ, dK, dV: a bf16 result
 of magnitude M carries up to M * 2^-8 from its final rounding alone, and the
@@ -24,14 +24,14 @@ import torch
 import oracle
 from sink_aware_masked_sinkattn_amd import sinkattn_bwd, sinkattn_fwd
 
-# bf16 l: the training forward's denominator is the fp32 sum of the
-# bf16-rounded (RNE, 8-bit significand) probabilities that also weight V,
-# each within 2^-8 of its value, so l = m + ln(sum) is within
-# ln(1 + 2^-8) = 3.90e-3 (reached in rows one key dominates).  The decode
-# kernels sum in fp32 and keep the tighter bound.
+# bf16 l carries no stated tolerance; the reading here is 1e-3 absolute for
+# an fp32-accumulated log-sum-exp of the given bf16 inputs.  Every bf16 path
+# meets it: the 32-key kernels and decode add the probabilities in fp32; the
+# 64-key forward adds fp16 copies of them (each within 2^-11 of its value,
+# so l is within ln(1 + 2^-11) = 4.9e-4 of the fp32 sum's log).
 TOL = {
     "fp32": {"o": 1e-5, "lse": 1e-5, "dq": 1e-5, "dk": 1e-5, "dv": 1e-5, "ds": 1e-5},
-    "bf16": {"o": 2e-2, "lse": 4e-3, "dq": 2e-2, "dk": 2e-2, "dv": 2e-2, "ds": 2e-2},
+    "bf16": {"o": 2e-2, "lse": 1e-3, "dq": 2e-2, "dk": 2e-2, "dv": 2e-2, "ds": 2e-2},
 }
 DECODE_LSE_TOL = 1e-3
 

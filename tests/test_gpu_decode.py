@@ -5,8 +5,10 @@ tokens equals row n - 1 of the training forward kernel.
 
 Tolerances as in tests/parity_util.py: O max-abs <= 2e-2 (max(2e-2,
 max|ref|/64) for inputs outside the named workloads), lse <= 1e-3 (the decode
-kernels sum the probabilities in fp32); against the training forward, the
-forward's bf16 bound on l (4e-3).
+kernels sum the probabilities in fp32); against the training forward the
+same 1e-3 on l, on sequences that run the forward's 32-key kernels (fp32 row
+sums) and on sequences of 1024 tokens or more that run its 64-key kernel
+(fp16 row sums).
 """
 import numpy as np
 import pytest
@@ -109,15 +111,21 @@ def test_decode_stream_wide_batch():
     check(o, lse, ro, rl, "127 sequences x 8 kv heads", scaled=True)
 
 
-@pytest.mark.parametrize("w,p", [(WINDOW_INF, 0), (128, 4), (9, 70)])
-def test_decode_matches_training_forward_row(w, p):
+@pytest.mark.parametrize("t,lengths,w,p", [
+    (600, (600, 257, 1), WINDOW_INF, 0),
+    (600, (600, 257, 1), 128, 4),
+    (600, (600, 257, 1), 9, 70),
+    # min(w, n) >= 1024: the forward's 64-key kernel (row sums on the matrix cores)
+    (1300, (1300, 1100, 257), WINDOW_INF, 0),
+    (1300, (1300, 1100, 1025), 1100, 16),
+])
+def test_decode_matches_training_forward_row(t, lengths, w, p):
     # the rollout engine must reproduce the trainer's probabilities: decode
     # over the first n tokens of a sequence equals row n - 1 of the forward
     # kernel run on those tokens
-    t, hq, hkv = 600, 16, 2
-    tr = make_inputs(batch=3, seqlen=t, heads_q=hq, heads_kv=hkv, head_dim=64, window=w,
-                     prefix=p, seed=41, std=0.5, dtype="bf16")
-    lengths = [600, 257, 1]
+    hq, hkv = 16, 2
+    tr = make_inputs(batch=len(lengths), seqlen=t, heads_q=hq, heads_kv=hkv, head_dim=64,
+                     window=w, prefix=p, seed=41 + t, std=0.5, dtype="bf16")
     dev = torch.device("cuda:0")
     q_dec = torch.stack([tr.q[b, n - 1] for b, n in enumerate(lengths)])
     o_dec, l_dec = sinkattn_decode(q_dec.to(dev), tr.k.to(dev), tr.v.to(dev),
@@ -131,9 +139,10 @@ def test_decode_matches_training_forward_row(w, p):
                                   tr.scale)
         worst_o = max(worst_o, float((o_dec[b].float() - o_fw[0, n - 1].float()).abs().max()))
         worst_l = max(worst_l, float((l_dec[b] - l_fw[0, :, n - 1]).abs().max()))
-    log(f"decode vs forward row (w={w}, p={p}): max|dO| {worst_o:.3g}, max|dl| {worst_l:.3g}")
+    log(f"decode vs forward row (T={t}, w={w}, p={p}): max|dO| {worst_o:.3g}, "
+        f"max|dl| {worst_l:.3g}")
     assert worst_o <= TOL["bf16"]["o"]
-    assert worst_l <= TOL["bf16"]["lse"]   # the forward's l carries the looser bound
+    assert worst_l <= TOL["bf16"]["lse"]
 
 
 @pytest.mark.slow
