@@ -5,13 +5,15 @@ Small cases span several query and key tiles of both tile configurations
 (narrow tiles for windows under 1024, wide ones otherwise) with ragged tails, every mask regime
 (plain causal, window, prefix, window+prefix, w=0, prefix past the end), GQA
 and varlen packing with empty, single-token and tile-edge lengths.  The
-named workloads run at their full sizes, compared on whole GQA groups.
+named workloads run at their full sizes and are compared on every head (see
+the section on them below).
 """
 import numpy as np
 import pytest
 import torch
 
-from parity_util import compare, log, run_gpu, run_oracle
+import oracle
+from parity_util import TOL, compare, log, run_gpu, run_oracle
 from workloads import WINDOW_INF, WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -102,22 +104,146 @@ def test_workload_tiny_fp32():
     compare(run_gpu(inp), run_oracle(inp), "fp32", inp, label="tiny_fp32")
 
 
+# Full-size comparisons of the named workloads.  The GPU runs every head in the
+# launch configuration the benchmark times; the oracle then checks every head:
+#   * short-window layers (w=128): every row of every head (o, lse, dq, ds) and,
+#     for every kv group, dk/dv at the prefix keys, keys around a 128-key dK/dV
+#     block edge mid-sequence and the last keys; groups 0 and 7 at every key;
+#   * full-causal layers: every head at sampled rows (tile edges, the prefix,
+#     the last rows, random rows) and every kv group's last keys (few rows see
+#     them); groups 0 and 7 in full with the dense oracle (every row and key,
+#     ds of their heads).
+# The short-window references use the oracle's row/key-restricted forms (the
+# same definition over each row's visible band; pinned in
+# test_oracle_pins.py), the dense ones oracle.forward / oracle.backward.
+
+NAMED_LAYERS = [("gqa_swa_4096", 0), ("gqa_causal_4096", 0), ("long_8192", 0), ("long_8192", 1)]
+_FULL = {}
+
+
+def _full(name, layer):
+    """GPU outputs of a named workload layer at full size (one layer cached at a time)."""
+    key = (name, layer)
+    if key not in _FULL:
+        _FULL.clear()
+        inp = workload_inputs(name)[layer]
+        log(f"{name} layer {layer}: GPU run (full size, every head)")
+        _FULL[key] = (inp, run_gpu(inp))
+    return _FULL[key]
+
+
 def _group_heads(inp, kv):
     return list(range(kv * inp.group, (kv + 1) * inp.group))
 
 
+def _np_head(t, b, h):
+    return t[b, :, h].to(torch.float64).numpy()
+
+
+def _sample_rows(n, prefix, seed):
+    edges = {0, 1, 2, 3, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 512, 513,
+             n // 2 - 1, n // 2, n - 257, n - 256, n - 129, n - 128, n - 65, n - 64, n - 33,
+             n - 32, n - 3, n - 2, n - 1}
+    if prefix:
+        edges |= {prefix - 1, prefix, prefix + 1}
+    rnd = np.random.default_rng(seed).choice(n, size=min(n, 32), replace=False)
+    return np.unique(np.array([r for r in edges if 0 <= r < n] + list(rnd), dtype=np.int64))
+
+
+def _sample_keys(n, window, prefix):
+    keys = set(range(max(0, n - 64), n))
+    if window < n:   # short window: few rows see any key, so more blocks are cheap
+        keys |= set(range(min(prefix, n)))
+        keys |= set(range(max(0, n // 2 - 40), min(n, n // 2 + 40)))
+        keys |= {j for j in (126, 127, 128, 129, 254, 255, 256, 257) if j < n}
+    return np.array(sorted(keys), dtype=np.int64)
+
+
+class _Errs:
+    """Running max-abs errors per output, asserted at the end against the bf16 tolerances."""
+
+    def __init__(self, label):
+        self.label, self.e = label, {}
+
+    def add(self, name, gpu, ref):
+        assert np.all(np.isfinite(gpu)), f"{self.label} {name}: non-finite GPU values"
+        err = float(np.max(np.abs(gpu - ref))) if np.size(ref) else 0.0
+        self.e[name] = max(self.e.get(name, 0.0), err)
+
+    def check(self, ds_gpu=None, ds_ref=None):
+        if ds_ref is not None:
+            self.e["ds"] = float(np.max(np.abs(ds_gpu - ds_ref)) / np.max(np.abs(ds_ref)))
+        log(f"  {self.label} errors: " + ", ".join(f"{n}={e:.3g}" for n, e in self.e.items()))
+        for n, e in self.e.items():
+            assert e <= TOL["bf16"][n], f"{self.label} {n}: error {e:.3g} > {TOL['bf16'][n]}"
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("name,layer,kv", [("gqa_swa_4096", 0, 3), ("gqa_causal_4096", 0, 5),
-                                           ("long_8192", 0, 1), ("long_8192", 1, 6)])
-def test_workload_full_size(name, layer, kv):
-    """Full-size run of the workload (every head computed on the GPU, in the
-    same launch configuration the benchmark times); the oracle recomputes one
-    whole GQA group (8 query heads + their kv head) for the comparison."""
-    inp = workload_inputs(name)[layer]
+@pytest.mark.parametrize("name,layer", NAMED_LAYERS)
+def test_workload_every_head(name, layer):
+    """Every query head and every kv group of the layer against the oracle (see above)."""
+    inp, gpu = _full(name, layer)
+    n, hq, hkv = inp.q.shape[1], inp.q.shape[2], inp.k.shape[2]
+    w, p, sc = inp.window, inp.prefix, inp.scale
+    short = w < n
+    rows = np.arange(n) if short else _sample_rows(n, p, seed=hq + n)
+    keys = _sample_keys(n, w, p)
+    errs = _Errs(f"{name}[{layer}] every head, {rows.size} rows, {keys.size} keys per kv group")
+    ds_ref = np.zeros(hq)
+    dk_ref = np.zeros((hkv, keys.size, inp.q.shape[3]))
+    dv_ref = np.zeros_like(dk_ref)
+    for h in range(hq):
+        kv = h // inp.group
+        q, k, v, do = (_np_head(t, 0, i) for t, i in ((inp.q, h), (inp.k, kv), (inp.v, kv),
+                                                       (inp.do, h)))
+        s = float(inp.sinks[h])
+        st = oracle.rows_head(q, k, v, s, w, p, sc, rows, do=do)
+        errs.add("o", gpu["o"][0, rows, h], st["o"])
+        errs.add("lse", gpu["lse"][0, h, rows], st["l"])
+        errs.add("dq", gpu["dq"][0, rows, h], st["dq"])
+        if short:
+            ds_ref[h] = -float(np.sum(np.exp(s - st["big_l"]) * st["d_row"]))
+        dkh, dvh = oracle.key_grads_head(q, k, v, s, w, p, sc, do, keys,
+                                         row_stats=st if short else None)
+        dk_ref[kv] += dkh
+        dv_ref[kv] += dvh
+    for kv in range(hkv):
+        errs.add("dk", gpu["dk"][0, keys, kv], dk_ref[kv])
+        errs.add("dv", gpu["dv"][0, keys, kv], dv_ref[kv])
+    errs.check(gpu["ds"] if short else None, ds_ref if short else None)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,layer,kv", [(nm, ly, kv) for nm, ly in NAMED_LAYERS for kv in (0, 7)])
+def test_workload_whole_group(name, layer, kv):
+    """One whole GQA group (8 query heads and their kv head) at every row and key,
+    including the sink gradient of its heads."""
+    inp, gpu = _full(name, layer)
     heads = _group_heads(inp, kv)
-    log(f"{name} layer {layer}: GPU run")
-    gpu = run_gpu(inp)
-    log(f"{name} layer {layer}: oracle on heads {heads}")
+    n = inp.q.shape[1]
+    if inp.window < n:
+        errs = _Errs(f"{name}[{layer}] kv{kv}")
+        w, p, sc = inp.window, inp.prefix, inp.scale
+        k, v = _np_head(inp.k, 0, kv), _np_head(inp.v, 0, kv)
+        dk_ref = np.zeros((n, inp.q.shape[3]))
+        dv_ref = np.zeros_like(dk_ref)
+        ds_ref = np.zeros(len(heads))
+        for i, h in enumerate(heads):
+            q, do = _np_head(inp.q, 0, h), _np_head(inp.do, 0, h)
+            s = float(inp.sinks[h])
+            st = oracle.rows_head(q, k, v, s, w, p, sc, np.arange(n), do=do)
+            errs.add("o", gpu["o"][0, :, h], st["o"])
+            errs.add("lse", gpu["lse"][0, h], st["l"])
+            errs.add("dq", gpu["dq"][0, :, h], st["dq"])
+            ds_ref[i] = -float(np.sum(np.exp(s - st["big_l"]) * st["d_row"]))
+            dkh, dvh = oracle.key_grads_head(q, k, v, s, w, p, sc, do, np.arange(n), row_stats=st)
+            dk_ref += dkh
+            dv_ref += dvh
+        errs.add("dk", gpu["dk"][0, :, kv], dk_ref)
+        errs.add("dv", gpu["dv"][0, :, kv], dv_ref)
+        errs.check(gpu["ds"][heads], ds_ref)
+        return
+    log(f"{name} layer {layer}: dense oracle on heads {heads}")
     ref = run_oracle(inp, heads=heads)
     compare(gpu, ref, "bf16", inp, heads=heads, label=f"{name}[{layer}] kv{kv}")
 
@@ -135,35 +261,66 @@ def _varlen_state():
     return _VARLEN
 
 
+VARLEN_GROUPS = (2, 7)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("seq", list(range(8)))
 def test_workload_varlen_per_sequence(seq):
-    """Packed GRPO group (8 rollouts): the whole pack runs on the GPU in one
-    call; the oracle checks one sequence per test on GQA group kv=2."""
-    st = _varlen_state()
-    inp = st["inp"]
-    kv = 2
-    heads = _group_heads(inp, kv)
+    """Packed GRPO group (8 rollouts): the whole pack runs on the GPU in one call.  Per
+    sequence the oracle checks every head at sampled rows, every kv group at sampled
+    keys, and GQA groups 2 and 7 at every row and key (with their sink gradient,
+    summed over the sequences once all eight have run)."""
+    st_all = _varlen_state()
+    inp, gpu = st_all["inp"], st_all["gpu"]
     cu = inp.cu_seqlens.numpy()
-    r = slice(int(cu[seq]), int(cu[seq + 1]))
-    sub = make_inputs(batch=1, seqlen=int(cu[seq + 1] - cu[seq]), heads_q=inp.q.shape[1],
-                      heads_kv=inp.k.shape[1], head_dim=64, window=inp.window, prefix=inp.prefix,
-                      seed=0, dtype="bf16")
-    sub.q, sub.k, sub.v, sub.do = (t[r].unsqueeze(0) for t in (inp.q, inp.k, inp.v, inp.do))
-    sub.sinks = inp.sinks
-    ref = run_oracle(sub, heads=heads)
-    gpu = st["gpu"]
-    g = {"o": gpu["o"][r][None], "dq": gpu["dq"][r][None], "dk": gpu["dk"][r][None],
-         "dv": gpu["dv"][r][None], "lse": gpu["lse"][:, r][None]}
-    compare(g, ref, "bf16", sub, heads=heads, what=("o", "lse", "dq", "dk", "dv"),
-            label=f"varlen seq {seq} (len {r.stop - r.start})")
-    st["ds_parts"][seq] = ref["ds"]
-    if len(st["ds_parts"]) == 8:
-        ds_ref = sum(st["ds_parts"].values())[heads]
-        ds_gpu = gpu["ds"][heads]
-        err = float(np.max(np.abs(ds_gpu - ds_ref)) / np.max(np.abs(ds_ref)))
-        log(f"  varlen ds (all sequences) norm-wise rel error {err:.3g}")
-        assert err <= 2e-2
+    r0, r1 = int(cu[seq]), int(cu[seq + 1])
+    n = r1 - r0
+    hq, hkv, d = inp.q.shape[1], inp.k.shape[1], inp.q.shape[2]
+    w, p, sc = inp.window, inp.prefix, inp.scale
+    errs = _Errs(f"varlen seq {seq} (len {n})")
+    seqt = lambda t, h: t[r0:r1, h].to(torch.float64).numpy()  # noqa: E731
+    rows = _sample_rows(n, p, seed=seq)
+    keys = _sample_keys(n, w, p)
+    full = set()
+    for kv in VARLEN_GROUPS:
+        full |= set(_group_heads(inp, kv))
+    ds_part = np.zeros(hq)
+    dk_ref = np.zeros((hkv, n, d))
+    dv_ref = np.zeros_like(dk_ref)
+    for h in range(hq):
+        kv = h // inp.group
+        q, k, v, do = seqt(inp.q, h), seqt(inp.k, kv), seqt(inp.v, kv), seqt(inp.do, h)
+        s = float(inp.sinks[h])
+        if h in full:
+            st = oracle.rows_head(q, k, v, s, w, p, sc, np.arange(n), do=do)
+            errs.add("o", gpu["o"][r0:r1, h], st["o"])
+            errs.add("lse", gpu["lse"][h, r0:r1], st["l"])
+            errs.add("dq", gpu["dq"][r0:r1, h], st["dq"])
+            ds_part[h] = -float(np.sum(np.exp(s - st["big_l"]) * st["d_row"]))
+            dkh, dvh = oracle.key_grads_head(q, k, v, s, w, p, sc, do, np.arange(n), row_stats=st)
+            dk_ref[kv] += dkh
+            dv_ref[kv] += dvh
+        else:
+            st = oracle.rows_head(q, k, v, s, w, p, sc, rows, do=do)
+            errs.add("o", gpu["o"][r0 + rows, h], st["o"])
+            errs.add("lse", gpu["lse"][h, r0 + rows], st["l"])
+            errs.add("dq", gpu["dq"][r0 + rows, h], st["dq"])
+            dkh, dvh = oracle.key_grads_head(q, k, v, s, w, p, sc, do, keys)
+            dk_ref[kv, keys] += dkh
+            dv_ref[kv, keys] += dvh
+    for kv in range(hkv):
+        sel = np.arange(n) if kv in VARLEN_GROUPS else keys
+        errs.add("dk", gpu["dk"][r0 + sel, kv], dk_ref[kv, sel])
+        errs.add("dv", gpu["dv"][r0 + sel, kv], dv_ref[kv, sel])
+    errs.check()
+    st_all["ds_parts"][seq] = ds_part
+    if len(st_all["ds_parts"]) == 8:
+        heads = sorted(full)
+        ds_ref = sum(st_all["ds_parts"].values())[heads]
+        err = float(np.max(np.abs(gpu["ds"][heads] - ds_ref)) / np.max(np.abs(ds_ref)))
+        log(f"  varlen ds (all sequences, heads {heads}) norm-wise rel error {err:.3g}")
+        assert err <= TOL["bf16"]["ds"]
 
 
 # ------------------------------------------------------------------ invariants
