@@ -79,7 +79,9 @@ typedef enum {
   SINKATTN_ERR_UNSUPPORTED = 4,  /* dtype / head_dim combination not built */
   SINKATTN_ERR_MISALIGNED = 5,   /* a tensor pointer is not 16-byte aligned */
   SINKATTN_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than required */
-  SINKATTN_ERR_HIP = 7           /* a HIP runtime call or launch failed */
+  SINKATTN_ERR_HIP = 7,          /* a HIP runtime call or launch failed */
+  SINKATTN_ERR_SCRATCH = 8       /* sinkattn_decode_noalloc: problem needs more workspace
+                                    than SINKATTN_DECODE_SCRATCH_BYTES */
 } sinkattn_status;
 
 typedef enum { SINKATTN_BF16 = 0, SINKATTN_FP32 = 1 } sinkattn_dtype;
@@ -240,6 +242,30 @@ sinkattn_status sinkattn_decode(const sinkattn_decode_problem *problem, const vo
                                 const int32_t *cache_seqlens, const float *sinks, void *o,
                                 float *lse, void *workspace, size_t workspace_bytes,
                                 void *stream);
+
+/*
+ * Decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments (minus the workspace), checks and
+ * results as sinkattn_decode.  The per-block partials go to a static device
+ * buffer of the library, SINKATTN_DECODE_SCRATCH_BYTES (24 MiB) on each GPU
+ * the library runs on, held until the process ends.  That is enough for
+ * every problem sinkattn_decode accepts (its workspace is at most
+ * 22,282,240 bytes); a problem whose sinkattn_decode_workspace_size exceeded
+ * it would return SINKATTN_ERR_SCRATCH (checked on the host, before any HIP
+ * call).  The buffer used is that of the
+ * current device; the first call on a device looks up its address
+ * (hipGetSymbolAddress), and no call allocates memory.  Every call on one GPU
+ * shares that buffer and overwrites it: calls that may overlap on one GPU
+ * (different streams without ordering between them, or different threads)
+ * race and give undefined results.  Nothing in the buffer needs to be zero
+ * on entry.
+ */
+#define SINKATTN_DECODE_SCRATCH_BYTES ((size_t)24 << 20)
+sinkattn_status sinkattn_decode_noalloc(const sinkattn_decode_problem *problem, const void *q,
+                                        const void *k_cache, const void *v_cache,
+                                        const int32_t *cache_seqlens, const float *sinks,
+                                        void *o, float *lse, void *stream);
 
 /*
  * GRPO token loss and group-normalised advantage over a packed batch of

@@ -8,7 +8,7 @@ from .binding import (BWD_ALL, BWD_DKDV, BWD_DQ, BWD_FINISH, BWD_PREPARE, WINDOW
                       DecodeProblem, GrpoProblem, Problem, SinkAttnError, load_library,
                       make_decode_problem, make_grpo_problem, make_problem, sinkattn_bwd,
                       sinkattn_bwd_phases, sinkattn_grpo_loss, sinkattn_grpo_workspace_size,
-                      sinkattn_bwd_workspace_size, sinkattn_decode,
+                      sinkattn_bwd_workspace_size, sinkattn_decode, sinkattn_decode_noalloc,
                       sinkattn_decode_workspace_size, sinkattn_fwd, sinkattn_key_tile_segments,
                       sinkattn_tile_class, sinkattn_tile_config)
 
@@ -18,5 +18,6 @@ __all__ = [
     "sinkattn_fwd", "sinkattn_bwd", "sinkattn_bwd_phases", "sinkattn_bwd_workspace_size",
     "sinkattn_tile_class", "sinkattn_key_tile_segments", "sinkattn_tile_config",
     "DecodeProblem", "make_decode_problem", "sinkattn_decode", "sinkattn_decode_workspace_size",
+    "sinkattn_decode_noalloc",
     "GrpoProblem", "make_grpo_problem", "sinkattn_grpo_loss", "sinkattn_grpo_workspace_size",
 ]

@@ -18,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsinkattn.so")
 
 WINDOW_INF = 2**31 - 1          # SINKATTN_WINDOW_INF
+# size of the library's static per-GPU scratch (sinkattn_decode_noalloc)
+SINKATTN_DECODE_SCRATCH_BYTES = 24 << 20
 
 SINKATTN_BF16 = 0
 SINKATTN_FP32 = 1
@@ -127,6 +129,8 @@ def load_library(path: str = LIB_PATH):
     lib.sinkattn_decode_workspace_size.restype = sz
     lib.sinkattn_decode.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.sinkattn_decode.restype = ctypes.c_int
+    lib.sinkattn_decode_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.sinkattn_decode_noalloc.restype = ctypes.c_int
     gp = ctypes.POINTER(GrpoProblem)
     lib.sinkattn_grpo_workspace_size.argtypes = [gp]
     lib.sinkattn_grpo_workspace_size.restype = sz
@@ -330,6 +334,31 @@ def sinkattn_decode(q, k_cache, v_cache, cache_seqlens, sinks, window: int, pref
                              _ptr(workspace), workspace.numel(), _stream())
     if st != 0:
         raise SinkAttnError(st, "sinkattn_decode", lib)
+    return out, lse
+
+
+def sinkattn_decode_noalloc(q, k_cache, v_cache, cache_seqlens, sinks, window: int, prefix: int,
+                            softmax_scale=None, out=None, lse=None,
+                            want_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """sinkattn_decode through the allocation-free entry point: the library keeps the
+    partials in its static per-GPU scratch.  Pass ``out`` (and ``lse``) to allocate
+    nothing here either."""
+    lib = load_library()
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (cache_seqlens, "cache_seqlens"), (sinks, "sinks")):
+        _dev(t, n)
+    if cache_seqlens.dtype != torch.int32:
+        raise ValueError("cache_seqlens must be int32")
+    pb = make_decode_problem(q, k_cache, window, prefix, softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((pb.batch, pb.heads_q), dtype=torch.float32, device=q.device)
+    st = lib.sinkattn_decode_noalloc(ctypes.byref(pb), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(cache_seqlens), _ptr(sinks), _ptr(out), _ptr(lse),
+                                     _stream())
+    if st != 0:
+        raise SinkAttnError(st, "sinkattn_decode_noalloc", lib)
     return out, lse
 
 

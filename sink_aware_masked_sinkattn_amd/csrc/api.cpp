@@ -53,7 +53,10 @@ hipError_t launch_decode_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                   float* lse, float* workspace, int batch, int t_max, int heads_q,
                                   int heads_kv, int window, int prefix, float scale,
                                   hipStream_t stream);
-size_t decode_workspace_bytes(int batch, int t_max, int heads_kv, int window, int prefix);
+size_t decode_workspace_bytes(int batch, int t_max, int heads_q, int heads_kv, int window,
+                              int prefix);
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** out);
 int fwd_key_tile(int window);
 int dkdv_query_tile(int window);
 bool dq_clears_dkdv_accumulators();
@@ -166,6 +169,9 @@ const char* sinkattn_status_string(sinkattn_status s) {
     case SINKATTN_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
     case SINKATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case SINKATTN_ERR_HIP: return "HIP runtime error";
+    case SINKATTN_ERR_SCRATCH:
+      return "problem needs more workspace than the static scratch of the allocation-free "
+             "entry point holds";
   }
   return "unknown status";
 }
@@ -340,34 +346,75 @@ extern "C" {
 
 size_t sinkattn_decode_workspace_size(const sinkattn_decode_problem* pb) {
   if (check_decode(pb) != SINKATTN_OK) return 0;
-  return round_up(decode_workspace_bytes(pb->batch, pb->cache_capacity, pb->heads_kv,
+  return round_up(decode_workspace_bytes(pb->batch, pb->cache_capacity, pb->heads_q, pb->heads_kv,
                                          clamp_window(pb->window, pb->cache_capacity),
                                          clamp_window(pb->prefix, pb->cache_capacity)));
 }
 
-sinkattn_status sinkattn_decode(const sinkattn_decode_problem* pb, const void* q,
-                                const void* k_cache, const void* v_cache,
-                                const int32_t* cache_seqlens, const float* sinks, void* o,
-                                float* lse, void* workspace, size_t workspace_bytes,
-                                void* stream) {
-  const sinkattn_status st = check_decode(pb);
-  if (st != SINKATTN_OK) return st;
-  if (pb->batch == 0) return SINKATTN_OK;
+}  // extern "C"
+
+namespace {
+
+// Pointer checks shared by the two decode entry points.  No HIP calls.
+sinkattn_status check_decode_pointers(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* cache_seqlens, const float* sinks,
+                                      const void* o, const float* lse) {
   if (!q || !k_cache || !v_cache || !cache_seqlens || !sinks || !o)
     return SINKATTN_ERR_NULL_POINTER;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
       !aligned16(sinks) || (lse && !aligned16(lse)) ||
       (reinterpret_cast<uintptr_t>(cache_seqlens) & 3u) != 0)
     return SINKATTN_ERR_MISALIGNED;
+  return SINKATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sinkattn_status sinkattn_decode(const sinkattn_decode_problem* pb, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* cache_seqlens, const float* sinks, void* o,
+                                float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  sinkattn_status st = check_decode(pb);
+  if (st != SINKATTN_OK) return st;
+  if (pb->batch == 0) return SINKATTN_OK;
+  st = check_decode_pointers(q, k_cache, v_cache, cache_seqlens, sinks, o, lse);
+  if (st != SINKATTN_OK) return st;
   const int window = clamp_window(pb->window, pb->cache_capacity);
   const int prefix = clamp_window(pb->prefix, pb->cache_capacity);
-  const size_t need = decode_workspace_bytes(pb->batch, pb->cache_capacity, pb->heads_kv, window,
-                                             prefix);
+  const size_t need = decode_workspace_bytes(pb->batch, pb->cache_capacity, pb->heads_q,
+                                             pb->heads_kv, window, prefix);
   if (!workspace || workspace_bytes < need) return SINKATTN_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return SINKATTN_ERR_MISALIGNED;
   return hip_status(launch_decode_bf16_d64(
       (const bf16*)q, (const bf16*)k_cache, (const bf16*)v_cache, cache_seqlens, sinks, (bf16*)o,
       lse, (float*)workspace, pb->batch, pb->cache_capacity, pb->heads_q, pb->heads_kv, window,
+      prefix, pb->softmax_scale, static_cast<hipStream_t>(stream)));
+}
+
+sinkattn_status sinkattn_decode_noalloc(const sinkattn_decode_problem* pb, const void* q,
+                                        const void* k_cache, const void* v_cache,
+                                        const int32_t* cache_seqlens, const float* sinks,
+                                        void* o, float* lse, void* stream) {
+  sinkattn_status st = check_decode(pb);
+  if (st != SINKATTN_OK) return st;
+  if (pb->batch == 0) return SINKATTN_OK;
+  st = check_decode_pointers(q, k_cache, v_cache, cache_seqlens, sinks, o, lse);
+  if (st != SINKATTN_OK) return st;
+  const int window = clamp_window(pb->window, pb->cache_capacity);
+  const int prefix = clamp_window(pb->prefix, pb->cache_capacity);
+  const size_t need = decode_workspace_bytes(pb->batch, pb->cache_capacity, pb->heads_q,
+                                             pb->heads_kv, window, prefix);
+  if (need > decode_scratch_bytes()) return SINKATTN_ERR_SCRATCH;
+  // ---- validation done; device work from here on
+  void* scratch = nullptr;
+  const hipError_t e = decode_scratch(&scratch);
+  if (e != hipSuccess) return SINKATTN_ERR_HIP;
+  return hip_status(launch_decode_bf16_d64(
+      (const bf16*)q, (const bf16*)k_cache, (const bf16*)v_cache, cache_seqlens, sinks, (bf16*)o,
+      lse, (float*)scratch, pb->batch, pb->cache_capacity, pb->heads_q, pb->heads_kv, window,
       prefix, pb->softmax_scale, static_cast<hipStream_t>(stream)));
 }
 

@@ -39,6 +39,8 @@
 //      O = acc / (r + exp(s_h - m)),  l = m + log r    (log2 units inside).
 // The decode step is bound by HBM (each visible K/V row is read once); the
 // MFMA work is small next to it.
+#include <mutex>
+
 #include "common.h"
 #include "mask_tiles.h"
 
@@ -602,19 +604,56 @@ static DecodePlan decode_plan(int batch, int t_max, int heads_kv, int window, in
 }
 
 // Stream workspace: seq_start [batch + 2] ints, then the partials of
-// STREAM_WG_MAX * WAVES + batch * heads_kv slots of up to HMAX heads (the
-// blocks number at most C / qc + S <= waves + batch * heads_kv).  The
+// STREAM_WG_MAX * WAVES + batch * heads_kv slots of the group's query heads
+// (the blocks number at most C / qc + S <= waves + batch * heads_kv).  The
 // single pass uses none; 256 bytes are still asked for, so the workspace
 // argument is required either way.
 static size_t stream_part_offset(int batch) {
   return (((size_t)batch + 2) * sizeof(int) + 255) & ~(size_t)255;
 }
 
-size_t decode_workspace_bytes(int batch, int t_max, int heads_kv, int window, int prefix) {
+size_t decode_workspace_bytes(int batch, int t_max, int heads_q, int heads_kv, int window,
+                              int prefix) {
   const DecodePlan pl = decode_plan(batch, t_max, heads_kv, window, prefix);
   if (pl.single) return 256;
   const size_t slots = (size_t)STREAM_WG_MAX * WAVES + (size_t)batch * heads_kv;
-  return stream_part_offset(batch) + slots * HMAX * PARTS * sizeof(float);
+  return stream_part_offset(batch) + slots * (size_t)(heads_q / heads_kv) * PARTS * sizeof(float);
+}
+
+// ---------------------------------------------------------------------------
+// The allocation-free decode entry point's workspace: a static array of the
+// library in device memory (one copy per GPU, held until the process ends).
+// Host code never passes the array's name to a kernel (on the host it only
+// names a stand-in); it looks up the device address once per device with
+// hipGetSymbolAddress, with that device current, and passes that address.
+// Size: the stream kernel runs only when batch * heads_kv < 1024, so its
+// workspace is at most 4352 + (4096 + 1023) slots * 16 heads * PARTS floats
+// = 22,282,240 bytes; the single pass needs none.  24 MiB so covers every
+// problem sinkattn_decode accepts; the entry point still checks the size.
+constexpr size_t DECODE_SCRATCH_BYTES = (size_t)24 << 20;
+static __device__ __align__(256) unsigned char scratch[DECODE_SCRATCH_BYTES];
+
+size_t decode_scratch_bytes() { return DECODE_SCRATCH_BYTES; }
+
+// Device address of the current device's copy of `scratch`.
+hipError_t decode_scratch(void** out) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 static int device_cus() {

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib()
-    for code in range(8):
+    for code in range(9):
         s = lib.sinkattn_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.sinkattn_status_string(99).decode() == "unknown status"
@@ -212,6 +212,50 @@ def test_decode_pointer_and_workspace_checks():
     big = _lib().sinkattn_decode_workspace_size(ctypes.byref(_dproblem(batch=8, cache_capacity=8192,
                                                                       window=2**31 - 1, prefix=0)))
     assert big >= need
+
+
+def _decode_noalloc(pb, **ptrs):
+    p = {n: ptrs.get(n, A) for n in ("q", "k", "v", "lens", "s", "o", "lse")}
+    return _lib().sinkattn_decode_noalloc(ctypes.byref(pb), p["q"], p["k"], p["v"], p["lens"],
+                                          p["s"], p["o"], p["lse"], None)
+
+
+def test_decode_noalloc_checks_before_any_device_work():
+    # every status below is returned by host checks alone (no GPU here)
+    lib = _lib()
+    assert lib.sinkattn_decode_noalloc(None, A, A, A, A, A, A, A, None) == 1
+    assert _decode_noalloc(_dproblem(batch=-1)) == 2
+    assert _decode_noalloc(_dproblem(window=-1)) == 3
+    assert _decode_noalloc(_dproblem(heads_q=32, heads_kv=1)) == 4
+    for name in ("q", "k", "v", "lens", "s", "o"):
+        assert _decode_noalloc(_dproblem(), **{name: None}) == 1, name
+    for name in ("q", "k", "v", "s", "o", "lse"):
+        assert _decode_noalloc(_dproblem(), **{name: A + 8}) == 5, name
+    assert _decode_noalloc(_dproblem(batch=0), q=None, k=None, v=None, lens=None, s=None, o=None,
+                           lse=None) == 0
+    assert "static scratch" in lib.sinkattn_status_string(8).decode()
+    # the static scratch covers every decode problem: the largest workspaces
+    # (stream kernel, batch * heads_kv just under 1024, 16 heads per kv head,
+    # long caches) stay within it
+    limit = binding.SINKATTN_DECODE_SCRATCH_BYTES
+    worst = 0
+    for hkv in (1, 2, 8, 64, 1023):
+        for batch in sorted({1, 7, max(1, 1023 // hkv), max(1, 1024 // hkv), 1024, 1025}):
+            for group in (1, 8, 16):
+                for cap, w, p in ((8192, 2**31 - 1, 0), (1 << 20, 2**31 - 1, 0),
+                                  (65536, 128, 16), (300, 2**31 - 1, 0)):
+                    pb = _dproblem(batch=batch, cache_capacity=cap, heads_q=hkv * group,
+                                   heads_kv=hkv, window=w, prefix=p)
+                    need = lib.sinkattn_decode_workspace_size(ctypes.byref(pb))
+                    worst = max(worst, need)
+                    assert 0 < need <= limit, (batch, hkv, group, cap, w, p)
+    assert worst == 22282240
+
+
+def test_header_states_the_scratch_size():
+    src = open(HEADER).read()
+    m = re.search(r"#define SINKATTN_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.SINKATTN_DECODE_SCRATCH_BYTES
 
 
 def _gproblem(**kw):
