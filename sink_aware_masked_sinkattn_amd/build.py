@@ -10,7 +10,6 @@ import concurrent.futures as cf
 import os
 import shutil
 import subprocess
-import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -39,21 +38,21 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build the HIP library)")
 
 
-def _compile(src: str, hipcc: str, extra) -> str:
+def _compile(src: str, hipcc: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc, *COMMON, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
     return obj
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
+def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, hipcc, list(extra_flags)), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, hipcc), SOURCES))
     tmp = OUT + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,4 +65,4 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra_flags=sys.argv[1:])
+    build(verbose=True)

@@ -38,15 +38,13 @@ hipError_t launch_bwd_f32(int head_dim, const float* q, const float* k, const fl
                           float* dk, float* dv, const int* cu_seqlens, int batch, int seqlen,
                           int total_tokens, int heads_q, int heads_kv, int window, int prefix,
                           float scale, bool do_dq, bool do_dkdv, hipStream_t stream);
-hipError_t launch_bwd_pre(int dtype_is_f32, int head_dim, const void* o, const void* dout,
-                          const float* lse, const float* sinks, const int* cu_seqlens,
-                          float* dsinks, float* d_ws, float* l_ws, float* dk_acc, float* dv_acc,
-                          int batch, int seqlen, int rows_total, int heads_q, int heads_kv,
+hipError_t launch_bwd_pre(int head_dim, const float* o, const float* dout, const float* lse,
+                          const float* sinks, const int* cu_seqlens, float* dsinks, float* d_ws,
+                          float* l_ws, int batch, int seqlen, int rows_total, int heads_q,
                           int lse_head_stride, hipStream_t stream);
-hipError_t launch_convert(int dtype_is_f32, const float* dk_acc, const float* dv_acc, void* dk,
-                          void* dv, long long n_kv, float scale, const float* ds_part,
-                          int ds_used, int ds_stride, int heads, float* dsinks,
-                          hipStream_t stream);
+hipError_t launch_convert(const float* dk_acc, const float* dv_acc, bf16* dk, bf16* dv,
+                          long long n_kv, float scale, const float* ds_part, int ds_used,
+                          int ds_stride, int heads, float* dsinks, hipStream_t stream);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
 hipError_t launch_decode_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                   const int* cache_seqlens, const float* sinks, bf16* o,
@@ -59,8 +57,6 @@ size_t decode_scratch_bytes();
 hipError_t decode_scratch(void** out);
 int fwd_key_tile(int window);
 int dkdv_query_tile(int window);
-bool dq_clears_dkdv_accumulators();
-hipError_t launch_zero_f32_vec(float* p, long long n, hipStream_t stream);
 hipError_t launch_grpo(const float* logp_new, const float* logp_old, const float* logp_ref,
                        const uint8_t* mask, const float* rewards, const int32_t* cu_seqlens,
                        float* loss, float* grad, float* advantages, void* workspace,
@@ -281,14 +277,9 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
   // computes the row statistics of its rows, writes them for the dK/dV
   // kernel and zeroes the dK/dV accumulators, so it runs first
   if (is_f32 && (phases & SINKATTN_BWD_PREPARE)) {
-    e = launch_bwd_pre(1, pb->head_dim, o, dout, lse, sinks, pb->cu_seqlens, dsinks, d_ws, l_ws,
-                       nullptr, nullptr, pb->batch, pb->seqlen, rows, pb->heads_q, pb->heads_kv,
-                       lse_stride, s);
-    if (e != hipSuccess) return hip_status(e);
-  }
-  if (!is_f32 && (phases & SINKATTN_BWD_PREPARE) && !dq_clears_dkdv_accumulators()) {
-    // the dK and dV accumulators fill the workspace from dk_off to its end
-    e = launch_zero_f32_vec(dk_acc, (long long)((wl.total - wl.dk_off) / sizeof(float)), s);
+    e = launch_bwd_pre(pb->head_dim, (const float*)o, (const float*)dout, lse, sinks,
+                       pb->cu_seqlens, dsinks, d_ws, l_ws, pb->batch, pb->seqlen, rows,
+                       pb->heads_q, lse_stride, s);
     if (e != hipSuccess) return hip_status(e);
   }
   if (!is_f32 && (phases & SINKATTN_BWD_DQ)) {
@@ -318,8 +309,9 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
     // the slots the dQ kernel wrote: batch * its query tiles per sequence
     const int qtile = dq_query_tile(pb->seqlen, pb->heads_q / pb->heads_kv, window, prefix);
     const int ds_used = pb->batch * ((pb->seqlen + qtile - 1) / qtile);
-    e = launch_convert(0, dk_acc, dv_acc, dk, dv, (long long)rows * pb->heads_kv * pb->head_dim,
-                       pb->softmax_scale, ds_part, ds_used, wl.ds_stride, pb->heads_q, dsinks, s);
+    e = launch_convert(dk_acc, dv_acc, (bf16*)dk, (bf16*)dv,
+                       (long long)rows * pb->heads_kv * pb->head_dim, pb->softmax_scale, ds_part,
+                       ds_used, wl.ds_stride, pb->heads_q, dsinks, s);
   }
   return hip_status(e);
 }

@@ -12,7 +12,7 @@
 // S and dP are recomputed tile by tile from Q, K, V, dO and L.
 //
 // Work decomposition.  A workgroup (4 waves) owns 128 keys of one kv head,
-// 32 per wave (by default; KB 32-key blocks per wave), whose K and V
+// 32 per wave, whose K and V
 // fragments stay in registers; query tiles are BQ rows (128).  The (query
 // tile, query head) pairs that can see those keys -- rows [k0, n) for a
 // prefix key, [k0, k1 + w] otherwise -- form the block's iteration list
@@ -40,10 +40,7 @@ namespace {
 
 constexpr int D = 64;
 constexpr int WAVES = 4;
-#ifndef SA_DKDV_KB
-#define SA_DKDV_KB 1
-#endif
-constexpr int KB = SA_DKDV_KB;         // 32-key MFMA blocks per wave
+constexpr int KB = 1;                  // 32-key MFMA blocks per wave
 constexpr int KW = 32 * KB;            // keys per wave
 constexpr int BKW = WAVES * KW;        // keys per workgroup
 // Query tiles of BQ rows (a template parameter; 128 in the launched kernel).
@@ -254,9 +251,7 @@ __device__ __forceinline__ bool dkdv_find_unit(const DkvArgs& a, int item, int l
   return false;
 }
 
-#ifndef SA_DKDV_OCC
-#define SA_DKDV_OCC 2   // waves per SIMD the register budget is set for
-#endif
+constexpr int DKDV_OCC = 2;   // waves per SIMD the register budget is set for
 template <int BQ>
 __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
   __shared__ DkvSmem<BQ> sm;
@@ -409,7 +404,7 @@ __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC, SA_DKDV_OCC))) void sinkattn_bwd_dkdv_bf16_d64(DkvArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DKDV_OCC, DKDV_OCC))) void sinkattn_bwd_dkdv_bf16_d64(DkvArgs a) {
   dkdv_body<128>(a);
 }
 }  // namespace
@@ -419,18 +414,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SA_DKDV_OCC
 // measured slower even for w = 128 (more iterations per workgroup).
 int dkdv_query_tile(int window) { (void)window; return 128; }
 
-// Iterations per work unit: about SA_DKDV_TARGET_WGS units over the whole call
+// Iterations per work unit: about DKDV_TARGET_UNITS units over the whole call
 // so the longest one is short next to the total (no long tail), but long
-// enough that the per-unit atomic flush of dK/dV stays small.  A power of two.
-#ifndef SA_DKDV_TARGET_WGS
-#define SA_DKDV_TARGET_WGS 8192
-#endif
-#ifndef SA_DKDV_MIN_CHUNK_SHIFT
-#define SA_DKDV_MIN_CHUNK_SHIFT 4
-#endif
+// enough that the per-unit atomic flush of dK/dV stays small (at least
+// 2^4 iterations).  A power of two.
+constexpr long long DKDV_TARGET_UNITS = 8192;
 int bwd_dkdv_chunk_shift(long long total_iters) {
-  int sh = SA_DKDV_MIN_CHUNK_SHIFT;
-  while (sh < 8 && ((long long)1 << sh) * SA_DKDV_TARGET_WGS < total_iters) ++sh;
+  int sh = 4;
+  while (sh < 8 && ((long long)1 << sh) * DKDV_TARGET_UNITS < total_iters) ++sh;
   return sh;
 }
 

@@ -34,16 +34,9 @@
 namespace {
 
 constexpr int D = 64;
-#ifndef SA_DQ_QB
-#define SA_DQ_QB 2      // 32-row query blocks per wave, 64-key-tile instance
-#endif
-#ifndef SA_DQ_QB_K32
-#define SA_DQ_QB_K32 1  // the same for the 32-key-tile (short window) instance
-#endif
-#ifndef SA_DQ_WAVES
-#define SA_DQ_WAVES 4
-#endif
-constexpr int WAVES = SA_DQ_WAVES;    // waves per workgroup
+constexpr int QB64 = 2;      // 32-row query blocks per wave, 64-key-tile instance
+constexpr int QB32 = 1;      // the same for the 32-key-tile (short window) instance
+constexpr int WAVES = 4;     // waves per workgroup
 constexpr int OROW = D + 8;            // padded row of the epilogue staging buffer
 // Key tiles of NKB blocks of 32 keys (64 in general, 32 for short windows).
 // LDS: two K/V tile pairs during the key loop; afterwards the same memory
@@ -57,10 +50,6 @@ struct DqTiles {
   static constexpr int SMEM_ELEMS = (4 * TILE_ELEMS > STAGE_ELEMS) ? 4 * TILE_ELEMS : STAGE_ELEMS;
   static_assert(SMEM_ELEMS >= 4 * TILE_ELEMS && SMEM_ELEMS >= STAGE_ELEMS, "LDS sizing");
 };
-
-#ifndef SA_DQ_ZERO_ACC
-#define SA_DQ_ZERO_ACC 1   // the dQ kernel clears the dK/dV accumulators
-#endif
 
 struct DqArgs {
   const bf16* q;
@@ -223,9 +212,7 @@ __device__ __forceinline__ void row_stats(const bf16x8 (&o)[4], const bf16x8 (&d
   ds = (ok && g == 0) ? -fast_exp2(sink2 - big_l2) * dot : 0.0f;
 }
 
-#ifndef SA_DQ_OCC
-#define SA_DQ_OCC 2   // waves per SIMD the register budget is set for
-#endif
+constexpr int DQ_OCC = 2;   // waves per SIMD the register budget is set for
 template <int NKB, int QB>
 __device__ __forceinline__ void dq_body(const DqArgs& a) {
   using T = DqTiles<NKB, QB>;
@@ -396,7 +383,7 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   // Zero this workgroup's share of the fp32 dK / dV accumulators (the dK/dV
   // kernel adds into them): rows of the tile congruent to h mod group, so the
   // group's query heads split the kv head's rows between them.
-  if (SA_DQ_ZERO_ACC) {
+  {
     const int part = h - kvh * a.group;
     const int n_mine = (q_last - q_start + a.group - part) / a.group;   // rows part, part+group, ...
     for (int i = tid; i < n_mine * (D / 4); i += WAVES * 64) {
@@ -408,16 +395,14 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   }
 }
 
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_DQ_OCC, SA_DQ_OCC))) void sinkattn_bwd_dq_bf16_d64(DqArgs a) {
-  dq_body<2, SA_DQ_QB>(a);
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(DQ_OCC, DQ_OCC))) void sinkattn_bwd_dq_bf16_d64(DqArgs a) {
+  dq_body<2, QB64>(a);
 }
 // short windows: 32-key tiles and (by default) 32 rows per wave at 3 waves
 // per SIMD -- a 64-row wave would span w + 64 keys of which fewer are visible
-#ifndef SA_DQ_OCC_K32
-#define SA_DQ_OCC_K32 3
-#endif
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_DQ_OCC_K32, SA_DQ_OCC_K32))) void sinkattn_bwd_dq_bf16_d64_k32(DqArgs a) {
-  dq_body<1, SA_DQ_QB_K32>(a);
+constexpr int DQ_OCC_K32 = 3;
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(DQ_OCC_K32, DQ_OCC_K32))) void sinkattn_bwd_dq_bf16_d64_k32(DqArgs a) {
+  dq_body<1, QB32>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -581,7 +566,7 @@ void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
   }
   // clear the fp32 dK / dV accumulators of the block's rows for this kv head
   // (the dK/dV kernel adds into them)
-  if (SA_DQ_ZERO_ACC) {
+  {
     const int nrows = q_last - q_start + 1;
     for (int i = tid; i < nrows * (D / 4); i += WAVES * 64) {
       const int r = q_start + i / (D / 4);
@@ -595,10 +580,6 @@ void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
 }  // namespace
 
 int fwd_key_tile(int window);
-
-// Whether the dQ kernel clears the fp32 dK/dV accumulators (else the caller
-// must before the dK/dV kernel runs).
-bool dq_clears_dkdv_accumulators() { return SA_DQ_ZERO_ACC != 0; }
 
 // Whether the resident-tile window kernel runs: GQA groups of a multiple of
 // 4 (four waves take the group's heads) and a key-tile list of at most
@@ -617,7 +598,7 @@ bool dq_window_kernel(int seqlen, int group, int window, int prefix) {
 // gradient's slots per head are batch * ceil(seqlen / rows)).
 int dq_query_tile(int seqlen, int group, int window, int prefix) {
   if (dq_window_kernel(seqlen, group, window, prefix)) return 32;
-  return fwd_key_tile(window) == 32 ? DqTiles<1, SA_DQ_QB_K32>::BQ : DqTiles<2, SA_DQ_QB>::BQ;
+  return fwd_key_tile(window) == 32 ? DqTiles<1, QB32>::BQ : DqTiles<2, QB64>::BQ;
 }
 
 hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
@@ -645,7 +626,7 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
                        dim3(WAVES * 64), 0, stream, a);
     return hipGetLastError();
   }
-  const int BQ = k32 ? DqTiles<1, SA_DQ_QB_K32>::BQ : DqTiles<2, SA_DQ_QB>::BQ;
+  const int BQ = k32 ? DqTiles<1, QB32>::BQ : DqTiles<2, QB64>::BQ;
   a.num_q_tiles = (seqlen + BQ - 1) / BQ;
   dim3 grid(heads_q, batch, a.num_q_tiles);
   if (k32)

@@ -573,13 +573,11 @@ __global__ __launch_bounds__(64) void sinkattn_decode_combine_bf16_d64(DecArgs a
 
 // Plan of one decode call.  single: every sequence's visible keys fit one
 // workgroup of the single-pass kernel, with chunks_per_wave chunks per wave
-// chosen so that about SA_DECODE_TARGET_WGS workgroups would cover a batch
+// chosen so that about DECODE_TARGET_WGS workgroups would cover a batch
 // of full caches; otherwise the stream kernel runs (then batch * heads_kv <
-// SA_DECODE_TARGET_WGS <= SEQ_WIN, so the batch's prefix sums fit its LDS).
-#ifndef SA_DECODE_TARGET_WGS
-#define SA_DECODE_TARGET_WGS 1024
-#endif
-static_assert(SA_DECODE_TARGET_WGS <= SEQ_WIN, "the stream kernel scans the batch in one window");
+// DECODE_TARGET_WGS <= SEQ_WIN, so the batch's prefix sums fit its LDS).
+constexpr int DECODE_TARGET_WGS = 1024;
+static_assert(DECODE_TARGET_WGS <= SEQ_WIN, "the stream kernel scans the batch in one window");
 struct DecodePlan {
   bool single;
   int chunks_per_wave;   // single pass
@@ -591,7 +589,7 @@ static DecodePlan decode_plan(int batch, int t_max, int heads_kv, int window, in
   const int max_chunks = sa_decode_max_chunks(t_max, window, prefix, KW);
   pl.max_chunks = max_chunks;
   const long long pairs = (long long)batch * heads_kv;
-  long long target = pairs > 0 ? (SA_DECODE_TARGET_WGS + pairs - 1) / pairs : 1;
+  long long target = pairs > 0 ? (DECODE_TARGET_WGS + pairs - 1) / pairs : 1;
   if (target < 1) target = 1;
   long long cpw = (max_chunks + WAVES * target - 1) / (WAVES * target);
   if (cpw < 1) cpw = 1;

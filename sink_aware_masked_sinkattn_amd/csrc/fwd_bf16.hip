@@ -47,13 +47,8 @@ constexpr int D = 64;
 // and V^T operand read from LDS (and the per-tile softmax bookkeeping) serves
 // 64 rows (0.619 -> 0.604 ms for a causal T=8192 layer against one block at 3
 // waves per SIMD).  The 32-key-tile kernels keep one block per wave.
-#ifndef SA_FWD_QB
-#define SA_FWD_QB 2
-#endif
-#ifndef SA_FWD_WAVES
-#define SA_FWD_WAVES 4
-#endif
-constexpr int WAVES = SA_FWD_WAVES;    // waves per workgroup
+constexpr int QB64 = 2;
+constexpr int WAVES = 4;    // waves per workgroup
 // Key tiles hold NKB blocks of 32 keys: 64-key tiles in general, 32-key
 // tiles for short windows, where a 32-row query block needs only w + 32 keys
 // and wider tiles would mostly compute masked pairs.
@@ -244,9 +239,8 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
   }
 }
 
-#ifndef SA_FWD_OCC
-#define SA_FWD_OCC 2   // waves per SIMD the 64-key kernel's register budget is set for
-#endif
+constexpr int FWD_OCC = 2;       // waves per SIMD the 64-key kernel's register budget is set for
+constexpr int FWD_OCC_K32 = 4;   // the same for the 32-key kernels
 // HW: waves along heads.  HW = 1: the workgroup's waves take consecutive
 // row blocks of one head.  HW = 4 (short windows, GQA groups of a multiple
 // of 4): they take four query heads of one kv group on the same rows, so the
@@ -393,16 +387,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   }
 }
 
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC, SA_FWD_OCC))) void sinkattn_fwd_bf16_d64(FwdArgs a) {
-  fwd_body<2, 1, SA_FWD_QB>(a);
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(FWD_OCC, FWD_OCC))) void sinkattn_fwd_bf16_d64(FwdArgs a) {
+  fwd_body<2, 1, QB64>(a);
 }
-#ifndef SA_FWD_OCC_K32
-#define SA_FWD_OCC_K32 4
-#endif
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC_K32, SA_FWD_OCC_K32))) void sinkattn_fwd_bf16_d64_k32(FwdArgs a) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(FWD_OCC_K32, FWD_OCC_K32))) void sinkattn_fwd_bf16_d64_k32(FwdArgs a) {
   fwd_body<1, 1, 1>(a);
 }
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(SA_FWD_OCC_K32, SA_FWD_OCC_K32))) void sinkattn_fwd_bf16_d64_k32h(FwdArgs a) {
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(FWD_OCC_K32, FWD_OCC_K32))) void sinkattn_fwd_bf16_d64_k32h(FwdArgs a) {
   fwd_body<1, 4, 1>(a);
 }
 
@@ -429,7 +420,7 @@ hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, cons
   // short windows with GQA groups of a multiple of 4: four heads per workgroup
   const bool heads4 = fwd_key_tile(window) == 32 && a.group % 4 == 0;
   const bool k32 = fwd_key_tile(window) == 32;
-  const int rows = heads4 ? 32 : (k32 ? WAVES * 32 : WAVES * SA_FWD_QB * 32);
+  const int rows = heads4 ? 32 : (k32 ? WAVES * 32 : WAVES * QB64 * 32);
   a.num_q_tiles = (seqlen + rows - 1) / rows;
   dim3 grid(heads4 ? heads_q / 4 : heads_q, batch, a.num_q_tiles);
   if (heads4)

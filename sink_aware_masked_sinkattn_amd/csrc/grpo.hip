@@ -29,15 +29,9 @@ namespace {
 constexpr int STATS_THREADS = 256;
 constexpr int TOK_THREADS = 256;
 constexpr int TOK_VEC = 4;                                // tokens per lane per step
-#ifndef SA_GRPO_STEPS
-#define SA_GRPO_STEPS 4
-#endif
-constexpr int TOK_STEPS = SA_GRPO_STEPS;
+constexpr int TOK_STEPS = 4;
 constexpr int TOK_CHUNK = TOK_THREADS * TOK_VEC * TOK_STEPS;   // 4096 tokens per workgroup
-#ifndef SA_GRPO_TABLE
-#define SA_GRPO_TABLE 256
-#endif
-constexpr int TABLE = SA_GRPO_TABLE;                       // rollouts staged per chunk
+constexpr int TABLE = 256;                       // rollouts staged per chunk
 
 struct GrpoArgs {
   const float* logp_new;
