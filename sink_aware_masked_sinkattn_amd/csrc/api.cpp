@@ -28,7 +28,8 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
                                   float* dv_acc, bf16* dq, const int* cu_seqlens, int batch,
                                   int seqlen, int rows_total, int heads_q, int heads_kv, int window,
                                   int prefix, float scale, hipStream_t stream);
-int dq_query_tile(int seqlen, int group, int window, int prefix);
+int dq_launch_tiles(int batch, int seqlen, int total_tokens, bool varlen, int group, int window,
+                    int prefix);
 hipError_t launch_fwd_f32(int head_dim, const float* q, const float* k, const float* v,
                           const float* sinks, float* o, float* lse, const int* cu_seqlens,
                           int batch, int seqlen, int total_tokens, int heads_q, int heads_kv,
@@ -306,9 +307,9 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
     if (e != hipSuccess) return hip_status(e);
   }
   if ((phases & SINKATTN_BWD_FINISH) && !is_f32) {
-    // the slots the dQ kernel wrote: batch * its query tiles per sequence
-    const int qtile = dq_query_tile(pb->seqlen, pb->heads_q / pb->heads_kv, window, prefix);
-    const int ds_used = pb->batch * ((pb->seqlen + qtile - 1) / qtile);
+    // the slots the dQ kernel wrote: one per workgroup of a head
+    const int ds_used = dq_launch_tiles(pb->batch, pb->seqlen, rows, dims.varlen,
+                                        pb->heads_q / pb->heads_kv, window, prefix);
     e = launch_convert(dk_acc, dv_acc, (bf16*)dk, (bf16*)dv,
                        (long long)rows * pb->heads_kv * pb->head_dim, pb->softmax_scale, ds_part,
                        ds_used, wl.ds_stride, pb->heads_q, dsinks, s);

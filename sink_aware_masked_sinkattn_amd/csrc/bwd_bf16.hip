@@ -209,7 +209,7 @@ __device__ __forceinline__ void tile_step(uint32_t qtile, const float* l2s,
 // (its query range starts lowest and ends highest).  Every wave of the
 // workgroup finds work unit `item` with the same lane-parallel count (64 key
 // blocks per step).  False if item is past the end (the grid of a packed
-// batch is sized for every sequence at the longest length).
+// batch is sized by a bound from its token count).
 template <int BQ>
 __device__ __forceinline__ bool dkdv_find_unit(const DkvArgs& a, int item, int lane, int* z_out,
                                                int* kb_out, int* chunk_out) {
@@ -451,7 +451,27 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
   long long units = 0;
   for (int kb = 0; kb < nkb; ++kb)
     units += sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW, a.chunk_shift);
-  units *= batch;
+  units *= batch;   // every sequence at the longest length
+  if (cu_seqlens) {
+    // Packed sequences of total length rows_total: a bound from the token count (the
+    // lengths stay on the device).  A block holding prefix keys (the first ceil(p / BKW))
+    // sees every later row, ceil(n / BQ) query tiles, so at most
+    // ceil(ceil(n / BQ) * group / 2^s) units; any other block sees at most BKW + w rows,
+    // no more units than the largest count among such blocks at the longest length (the
+    // same key offsets, a query range no longer).  With sum ceil(n / B) <= (N + G (B - 1)) / B
+    // over the sequences, the units of the whole launch stay within the sum below.
+    const int npb = min((prefix + BKW - 1) / BKW, nkb);
+    long long cw = 0;
+    for (int kb = npb; kb < nkb; ++kb)
+      cw = max(cw, (long long)sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW,
+                                                    a.chunk_shift));
+    const long long tiles_q = sa_packed_tiles_bound(batch, seqlen, rows_total, BQ);
+    const long long blocks = sa_packed_tiles_bound(batch, seqlen, rows_total, BKW);
+    const long long per_chunk = 1LL << a.chunk_shift;
+    const long long packed = npb * ((a.group * tiles_q + batch * (per_chunk - 1)) / per_chunk) +
+                             cw * blocks;
+    if (packed < units) units = packed;
+  }
   if (units * heads_kv > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (units == 0) return hipSuccess;
   dim3 grid((unsigned)(units * heads_kv));

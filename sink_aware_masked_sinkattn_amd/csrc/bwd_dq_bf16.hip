@@ -60,8 +60,8 @@ struct DqArgs {
   const float* lse;       // forward log-sum-exp (natural log, content keys only)
   const float* sinks;
   float* ds_part;         // [Hq, ds_stride] this launch's per-workgroup parts of ds_h:
-                          // slot z * num_q_tiles + qt of each head (the finish
-                          // kernel adds a head's slots in index order)
+                          // slot grid_y_index * grid_z + grid_z_index of each head
+                          // (the finish kernel adds a head's slots in index order)
   int ds_stride;
   float* l2_ws;           // [Hq, rows] L in log2 units (L * log2 e), written here
   float* d_ws;            // [Hq, rows] D, written here
@@ -69,7 +69,8 @@ struct DqArgs {
   float* dv_acc;
   bf16* dq;
   const int* cu_seqlens;
-  int seqlen, heads_q, heads_kv, group, window, prefix, rows_total, num_q_tiles;
+  int batch, seqlen, heads_q, heads_kv, group, window, prefix, rows_total;
+  int num_q_tiles;        // fixed length: query tiles per sequence
   int lse_head_stride;    // T (fixed length) or N (packed)
   float scale_log2;
   float scale;
@@ -222,12 +223,13 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   __shared__ __attribute__((aligned(128))) bf16 smem[T::SMEM_ELEMS];   // K0 V0 K1 V1, then output staging
 
   const int h = map_head(blockIdx.x, a.heads_q);
-  const int z = blockIdx.y;
-  const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
-  const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
+  const size_t ds_slot =
+      (size_t)h * a.ds_stride + (size_t)blockIdx.y * gridDim.z + blockIdx.z;
+  int z = 0, qt = 0;
+  const bool has_tile = launch_tile(a.cu_seqlens, a.batch, a.num_q_tiles, BQ, &z, &qt);
+  const SeqView sv = seq_view(a.cu_seqlens, has_tile ? z : 0, a.seqlen, a.heads_q);
   const int q_start = qt * BQ;
-  const size_t ds_slot = (size_t)h * a.ds_stride + (size_t)z * a.num_q_tiles + qt;
-  if (q_start >= sv.len) {   // no rows here: this workgroup's part of ds_h is 0
+  if (!has_tile || q_start >= sv.len) {   // no rows here: this workgroup's part of ds_h is 0
     if (threadIdx.x == 0) a.ds_part[ds_slot] = 0.0f;
     return;
   }
@@ -426,12 +428,12 @@ void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
   // consecutive workgroups go to consecutive XCDs: with 8 kv heads each XCD
   // keeps one kv head and its L2
   const int kvh = blockIdx.x;
-  const int z = blockIdx.y;
-  const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
-  const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
+  const size_t ds_slot = (size_t)blockIdx.y * gridDim.z + blockIdx.z;   // + h * ds_stride
+  int z = 0, qt = 0;
+  const bool has_tile = launch_tile(a.cu_seqlens, a.batch, a.num_q_tiles, 32, &z, &qt);
+  const SeqView sv = seq_view(a.cu_seqlens, has_tile ? z : 0, a.seqlen, a.heads_q);
   const int q_start = qt * 32;
-  const size_t ds_slot = (size_t)z * a.num_q_tiles + qt;   // + h * ds_stride
-  if (q_start >= sv.len) {   // no rows here: the group's parts of ds_h are 0
+  if (!has_tile || q_start >= sv.len) {   // no rows here: the group's parts of ds_h are 0
     for (int i = threadIdx.x; i < a.group; i += WAVES * 64)
       a.ds_part[(size_t)(kvh * a.group + i) * a.ds_stride + ds_slot] = 0.0f;
     return;
@@ -594,11 +596,21 @@ bool dq_window_kernel(int seqlen, int group, int window, int prefix) {
   return pre + win <= WIN_TILES;
 }
 
-// Rows per query tile of the dQ kernel the launcher picks (the sink
-// gradient's slots per head are batch * ceil(seqlen / rows)).
-int dq_query_tile(int seqlen, int group, int window, int prefix) {
+// Rows per query tile of the dQ kernel the launcher picks.
+static int dq_query_tile(int seqlen, int group, int window, int prefix) {
   if (dq_window_kernel(seqlen, group, window, prefix)) return 32;
   return fwd_key_tile(window) == 32 ? DqTiles<1, QB32>::BQ : DqTiles<2, QB64>::BQ;
+}
+
+// Workgroups per head of the dQ launch (grid y * grid z), which is the number
+// of per-workgroup sink-gradient slots per head it writes: sequences x query
+// tiles (fixed length), or the packed tiles' bound (varlen).  At most
+// batch * ceil(seqlen / 32), the workspace's slots per head.
+int dq_launch_tiles(int batch, int seqlen, int total_tokens, bool varlen, int group, int window,
+                    int prefix) {
+  const int bq = dq_query_tile(seqlen, group, window, prefix);
+  if (varlen) return sa_packed_tiles_bound(batch, seqlen, total_tokens, bq);
+  return batch * ((seqlen + bq - 1) / bq);
 }
 
 hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
@@ -613,22 +625,27 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
   a.dq = dq;
   a.lse_head_stride = cu_seqlens ? rows_total : seqlen;
   a.cu_seqlens = cu_seqlens;
-  a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
+  a.batch = batch; a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
   a.group = heads_q / heads_kv; a.window = window; a.prefix = prefix;
   a.rows_total = rows_total;
   const bool k32 = fwd_key_tile(window) == 32;
   a.scale_log2 = scale * SA_LOG2E;
   a.scale = scale;
   if (seqlen == 0 || batch == 0) return hipSuccess;
+  const int BQ = dq_query_tile(seqlen, a.group, window, prefix);
+  a.num_q_tiles = (seqlen + BQ - 1) / BQ;
+  // packed sequences: one linear index over every sequence's tiles
+  const int tiles = cu_seqlens ? sa_packed_tiles_bound(batch, seqlen, rows_total, BQ)
+                               : a.num_q_tiles;
+  if (tiles > 65535) return hipErrorInvalidConfiguration;
+  if (tiles == 0) return hipSuccess;
+  const int gy = cu_seqlens ? 1 : batch;
   if (dq_window_kernel(seqlen, a.group, window, prefix)) {
-    a.num_q_tiles = (seqlen + 31) / 32;
-    hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64_win, dim3(heads_kv, batch, a.num_q_tiles),
+    hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64_win, dim3(heads_kv, gy, tiles),
                        dim3(WAVES * 64), 0, stream, a);
     return hipGetLastError();
   }
-  const int BQ = k32 ? DqTiles<1, QB32>::BQ : DqTiles<2, QB64>::BQ;
-  a.num_q_tiles = (seqlen + BQ - 1) / BQ;
-  dim3 grid(heads_q, batch, a.num_q_tiles);
+  dim3 grid(heads_q, gy, tiles);
   if (k32)
     hipLaunchKernelGGL(sinkattn_bwd_dq_bf16_d64_k32, grid, dim3(WAVES * 64), 0, stream, a);
   else

@@ -162,6 +162,48 @@ __device__ __forceinline__ SeqView seq_view(const int* cu_seqlens, int z, int se
   return s;
 }
 
+// The (sequence, query tile) of this workgroup in a launch of a
+// query-stationary kernel with tiles of bq rows.  Fixed length: sequence =
+// grid y, tile = num_q_tiles - 1 - grid z (tiles from the last: longest rows
+// first).  Packed sequences (cu_seqlens): grid y = 1 and grid z indexes the
+// packed tiles sequence by sequence, each sequence's tiles from its last
+// down; the host sizes grid z with sa_packed_tiles_bound, and an index past
+// the last tile returns false.  The lanes of a wave scan 64 sequences at a
+// time (tile counts, prefix sum); every lane gets the same, wave-uniform result.
+__device__ __forceinline__ bool launch_tile(const int* cu_seqlens, int batch, int num_q_tiles,
+                                            int bq, int* z_out, int* qt_out) {
+  if (!cu_seqlens) {
+    *z_out = blockIdx.y;
+    *qt_out = num_q_tiles - 1 - (int)blockIdx.z;
+    return true;
+  }
+  const int lane = threadIdx.x & 63;
+  int t = blockIdx.z;
+  for (int z0 = 0; z0 < batch; z0 += 64) {
+    const int z = z0 + lane;
+    const int n = z < batch ? max(cu_seqlens[z + 1] - cu_seqlens[z], 0) : 0;
+    const int nt = (n + bq - 1) / bq;
+    int incl = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    // wave-uniform (readfirstlane), so the loop's branches are uniform too
+    const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+    if (t < total) {
+      const int L = __builtin_ctzll(__ballot(incl > t));   // first sequence past index t
+      const int before = __shfl(incl - nt, L);
+      const int ntl = __shfl(nt, L);
+      *z_out = __builtin_amdgcn_readfirstlane(z0 + L);
+      *qt_out = __builtin_amdgcn_readfirstlane(ntl - 1 - (t - before));
+      return true;
+    }
+    t -= total;
+  }
+  return false;
+}
+
 // ---------------------------------------------------------------------------
 // LDS tiles of R rows x 64 bf16 (128 B per row, no padding).  Each row's eight
 // 16-byte chunks are stored XOR-swizzled by the row index:

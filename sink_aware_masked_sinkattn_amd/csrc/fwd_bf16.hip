@@ -76,9 +76,9 @@ struct FwdArgs {
   bf16* o;
   float* lse;                // may be null
   const int* cu_seqlens;     // null for fixed length
-  int seqlen, heads_q, heads_kv, group, window, prefix;
+  int batch, seqlen, heads_q, heads_kv, group, window, prefix;
   int lse_head_stride;       // T (fixed) or N (varlen)
-  int num_q_tiles;
+  int num_q_tiles;           // fixed length: query tiles per sequence
   float scale_log2;          // softmax_scale * log2(e)
 };
 
@@ -263,8 +263,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   // h0: the workgroup's first head (uniform); the HW heads share its kv head
   const int h0 = HW == 1 ? map_head(blockIdx.x, a.heads_q) : map_head(blockIdx.x, a.heads_q / HW) * HW;
   const int h = h0 + (HW == 1 ? 0 : wave % HW);
-  const int z = blockIdx.y;
-  const int qt = a.num_q_tiles - 1 - (int)blockIdx.z;
+  int z = 0, qt = 0;
+  if (!launch_tile(a.cu_seqlens, a.batch, a.num_q_tiles, BQW, &z, &qt)) return;
   const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
   const int q_start = qt * BQW;
   if (q_start >= sv.len) return;
@@ -411,7 +411,7 @@ hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, cons
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.sinks = sinks; a.o = o; a.lse = lse;
   a.cu_seqlens = cu_seqlens;
-  a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
+  a.batch = batch; a.seqlen = seqlen; a.heads_q = heads_q; a.heads_kv = heads_kv;
   a.group = heads_q / heads_kv;
   a.window = window; a.prefix = prefix;
   a.lse_head_stride = cu_seqlens ? total_tokens : seqlen;
@@ -422,7 +422,12 @@ hipError_t launch_fwd_bf16_d64(const bf16* q, const bf16* k, const bf16* v, cons
   const bool k32 = fwd_key_tile(window) == 32;
   const int rows = heads4 ? 32 : (k32 ? WAVES * 32 : WAVES * QB64 * 32);
   a.num_q_tiles = (seqlen + rows - 1) / rows;
-  dim3 grid(heads4 ? heads_q / 4 : heads_q, batch, a.num_q_tiles);
+  // packed sequences: one linear index over every sequence's tiles
+  const int tiles = cu_seqlens ? sa_packed_tiles_bound(batch, seqlen, total_tokens, rows)
+                               : a.num_q_tiles;
+  if (tiles > 65535) return hipErrorInvalidConfiguration;
+  if (tiles == 0) return hipSuccess;
+  dim3 grid(heads4 ? heads_q / 4 : heads_q, cu_seqlens ? 1 : batch, tiles);
   if (heads4)
     hipLaunchKernelGGL(sinkattn_fwd_bf16_d64_k32h, grid, dim3(WAVES * 64), 0, stream, a);
   else if (k32)

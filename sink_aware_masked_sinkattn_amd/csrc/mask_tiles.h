@@ -64,6 +64,17 @@ SA_HD int sa_key_tile_segments(int q0, int q1, int w, int p, int bk, int* out) {
   return 2;
 }
 
+// Query tiles of bq rows over a batch of packed sequences (total_tokens rows,
+// each sequence at most seqlen): at most batch * ceil(seqlen / bq), and at
+// most floor((total_tokens + batch * (bq - 1)) / bq) since
+// sum ceil(len / bq) <= sum (len + bq - 1) / bq.  Sizes the grids of the
+// query-stationary kernels without reading the lengths on the host.
+SA_HD int sa_packed_tiles_bound(int batch, int seqlen, int total_tokens, int bq) {
+  const long long per_seq = (long long)batch * ((seqlen + bq - 1) / bq);
+  const long long by_tokens = ((long long)total_tokens + (long long)batch * (bq - 1)) / bq;
+  return (int)(per_seq < by_tokens ? per_seq : by_tokens);
+}
+
 // Query rows that key columns [k0, k1] are visible to, within a sequence of
 // n tokens: rows [k0, qmax] with qmax = n-1 if any key is a prefix key, else
 // min(n-1, k1 + w).  Returns false if no row sees them.

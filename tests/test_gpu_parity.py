@@ -66,6 +66,11 @@ def test_bf16_small(case):
     ((200, 300), 128, 16),
     ((1100, 37, 0, 1030), WINDOW_INF, 5),
     ((700, 300, 900), 50, 8),      # several dK/dV units per key block in the long sequences
+    # packed grids sized from the token count: many short sequences, prefixes over
+    # several 128-key blocks, empty and single-token sequences
+    ((5, 0, 129, 1, 300, 64, 700, 33, 128, 2), 30, 200),
+    ((1000, 999, 1, 0, 640), 128, 16),
+    ((257,) * 12, 64, 130),
 ])
 def test_bf16_varlen_small(lengths, w, p):
     inp = make_inputs(batch=0, seqlen=0, heads_q=8, heads_kv=2, head_dim=64, window=w, prefix=p,
