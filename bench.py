@@ -113,15 +113,17 @@ def kernel_source_sha(kernel: str) -> str:
     return h.hexdigest()
 
 
-def committed_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+def committed_traffic(kernel: str, workload: str, layer=None):
+    """HBM bytes of one launch of `kernel` (on layer `layer` of an attention workload, whose
+    summaries list one value per layer), from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
     sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
-    val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    key = "hbm_bytes_per_launch" + ("" if layer is None else rf"\[layer {layer}\]")
+    val = re.search(key + r":\s*([0-9.eE+]+)", txt)
     if not sha or not val or sha.group(1) != kernel_source_sha(kernel):
         return None
     return float(val.group(1))
@@ -148,6 +150,23 @@ def committed_sclk(kernel: str, workload: str):
     return best[1] if best else None
 
 
+def kernel_bytes(inp, kernel_base_name: str) -> int:
+    """Algorithmic HBM bytes of one launch of a kernel on a layer: what it must read and
+    write at least once.  Forward: Q, K, V in, O out (bf16), l out (fp32).  dQ kernel (with
+    the row statistics): Q, K, V, dO, O in, dQ out (bf16), l in, L and D out (fp32).  dK/dV
+    kernel: Q, K, V, dO in (bf16), L and D in (fp32), dK and dV out (bf16; the kernel keeps
+    them in fp32 accumulators, an implementation choice, not counted)."""
+    q, k = inp.q.numel(), inp.k.numel()
+    rows = q // inp.q.shape[-1]               # (token, query head) rows
+    if kernel_base_name == "sinkattn_fwd_bf16_d64":
+        return 2 * (q + 2 * k + q) + 4 * rows
+    if kernel_base_name == "sinkattn_bwd_dq_bf16_d64":
+        return 2 * (4 * q + 2 * k) + 12 * rows
+    if kernel_base_name == "sinkattn_bwd_dkdv_bf16_d64":
+        return 2 * (2 * q + 4 * k) + 8 * rows
+    raise KeyError(kernel_base_name)
+
+
 def compulsory_bytes(inp) -> tuple:
     """HBM bytes the forward and the backward cannot avoid: forward reads Q, K, V and writes
     O (bf16) and l (fp32); backward reads Q, K, V, dO (bf16), L and D (fp32) and writes dQ, dK,
@@ -162,7 +181,7 @@ def compulsory_bytes(inp) -> tuple:
 def cpu_baseline(layers, head_dim: int):
     """The fp64 oracle as it stands, timed on a bounded sample: the first
     four query heads of each layer (forward + backward over the full
-    sequence; about 10 s on 16 host cores)."""
+    sequence, or every packed sequence; about 10 s on 16 host cores)."""
     import numpy as np  # noqa: F401
     import torch
 
@@ -176,20 +195,22 @@ def cpu_baseline(layers, head_dim: int):
     t0 = time.perf_counter()
     for inp in layers:
         sl = slice(0, CPU_SAMPLE_HEADS)
-        q = inp.q[:, :, sl].to(torch.float64).numpy()
-        k = inp.k[:, :, sl].to(torch.float64).numpy()
-        v = inp.v[:, :, sl].to(torch.float64).numpy()
-        do = inp.do[:, :, sl].to(torch.float64).numpy()
+        q, k, v, do = (t[..., sl, :].to(torch.float64).numpy()
+                       for t in (inp.q, inp.k, inp.v, inp.do))
         s = inp.sinks[sl].to(torch.float64).numpy()
-        oracle.forward(q, k, v, s, inp.window, inp.prefix, inp.scale)
-        oracle.backward(q, k, v, s, do, inp.window, inp.prefix, inp.scale)
+        cu = inp.cu_seqlens.numpy() if inp.cu_seqlens is not None else None
+        oracle.forward(q, k, v, s, inp.window, inp.prefix, inp.scale, cu_seqlens=cu)
+        oracle.backward(q, k, v, s, do, inp.window, inp.prefix, inp.scale, cu_seqlens=cu)
+        lens = inp.lengths if inp.lengths is not None else (inp.q.shape[1],) * inp.q.shape[0]
         flops += (14 * head_dim * CPU_SAMPLE_HEADS *
-                  visible_pairs_per_head(inp.q.shape[1], inp.window, inp.prefix))
+                  sum(visible_pairs_per_head(n, inp.window, inp.prefix) for n in lens))
     dt = time.perf_counter() - t0
+    hq = layers[0].q.shape[-2]
+    what = ("every packed sequence" if layers[0].lengths is not None
+            else f"T={layers[0].q.shape[1]}")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{CPU_SAMPLE_HEADS} of 64 query heads per layer (both layers, T=8192), "
-                      "fwd+bwd in fp64; "
-                      f"{dt:.1f} s",
+            "sample": f"{CPU_SAMPLE_HEADS} of {hq} query heads per layer ({len(layers)} "
+                      f"layer(s), {what}), fwd+bwd in fp64; {dt:.1f} s",
             "seconds": round(dt, 3)}
 
 
@@ -350,6 +371,7 @@ def run_decode(args) -> int:
                    "parallelism": "single GPU"},
         "per_layer": per_layer,
         "roofline": roofline,
+        "roofline_per_launch": launches,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -467,6 +489,7 @@ def run_grpo(args) -> int:
                    "kl_mode": wl.kl_mode, "eps_clip": wl.eps_clip, "parallelism": "single GPU"},
         "tokens_per_s": round(inp.logp_new.numel() / (ms_per_step * 1e-3), 1),
         "roofline": roofline,
+        "roofline_per_launch": launches,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -601,32 +624,46 @@ def main(argv=None):
     total_flops = sum(14 * d * r["pairs"] for r in runs)
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the one with the largest total time per step; each
-    # layer launches the tile variant the library picks for its window
-    kern_time, kern_flops, kern_launches = {}, {}, {}
-    for p, r in zip(per_layer, runs):
+    # Roofline per launch: every kernel of every layer against the bound its own
+    # arithmetic intensity sets (useful FLOP over algorithmic bytes, against the
+    # ridge peak_flops / peak_bytes): MFMA above the ridge, HBM below.  The
+    # headline roofline is the launch with the largest time per step.
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    launches = []
+    for li, (p, r) in enumerate(zip(per_layer, runs)):
         p["kernels"] = r["kernels"]
         for ph, name in r["kernels"].items():
             base = kernel_base(name)
-            kern_time[name] = kern_time.get(name, 0.0) + p[ph]
-            kern_flops[name] = kern_flops.get(name, 0) + KERNEL_FLOP_PER_PAIR[base] * d * p["pairs"]
-            kern_launches[name] = kern_launches.get(name, 0) + 1
-    dom = max(kern_time, key=kern_time.get)
-    launches = kern_launches[dom]
-    avg_ms = kern_time[dom] / launches
-    achieved = kern_flops[dom] / launches / (avg_ms * 1e-3) / 1e12
-    traffic = committed_traffic(dom, args.workload)
-    # the peak scales with the clock: 2516.6 TFLOP/s assumes 2.4 GHz, the measured shader
-    # clock under this load is lower (SQ counters of the committed counter summary)
-    sclk = committed_sclk(dom, args.workload)
-    peak_at_sclk = PEAK_BF16_TFLOPS * sclk / NOMINAL_SCLK_GHZ if sclk else None
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic, "kernel": dom, "avg_launch_ms": round(avg_ms, 4),
-                "algorithmic_flop_per_launch": kern_flops[dom] / launches,
-                "sclk_ghz_measured": sclk,
-                "frac_at_measured_sclk": round(achieved / peak_at_sclk, 4) if sclk else None,
-                "sclk_source": f"profiles/sq_counters_{args.workload}.md" if sclk else None}
+            t_s = p[ph] * 1e-3
+            flop = KERNEL_FLOP_PER_PAIR[base] * d * p["pairs"]
+            nbytes = kernel_bytes(r["inp"], base)
+            if flop / nbytes >= ridge:
+                rl = {"bound": "mfma", "achieved": round(flop / t_s / 1e12, 2),
+                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+            else:
+                rl = {"bound": "hbm", "achieved": round(nbytes / t_s / 1e9, 1),
+                      "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+            rl["frac"] = round(rl["achieved"] / rl["peak"], 4)
+            rl.update({"kernel": name, "layer": li, "avg_launch_ms": round(p[ph], 4),
+                       "algorithmic_flop_per_launch": flop,
+                       "algorithmic_bytes_per_launch": nbytes})
+            launches.append(rl)
+    dom = max(launches, key=lambda x: x["avg_launch_ms"])
+    traffic = committed_traffic(dom["kernel"], args.workload, dom["layer"])
+    roofline = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roofline.update({"traffic": traffic, "kernel": dom["kernel"], "layer": dom["layer"],
+                     "avg_launch_ms": dom["avg_launch_ms"],
+                     "algorithmic_flop_per_launch": dom["algorithmic_flop_per_launch"],
+                     "algorithmic_bytes_per_launch": dom["algorithmic_bytes_per_launch"]})
+    # diagnostic only: the 2516.6 TFLOP/s peak assumes 2.4 GHz; the committed SQ counter
+    # summary measures the shader clock under this load, which lowers the attainable peak
+    sclk = committed_sclk(dom["kernel"], args.workload)
+    diagnostics = None
+    if sclk:
+        diagnostics = {"sclk_ghz_measured": sclk,
+                       "sclk_source": f"profiles/sq_counters_{args.workload}.md",
+                       "step_frac_of_peak_at_measured_sclk":
+                           round(value / (PEAK_BF16_TFLOPS * sclk / NOMINAL_SCLK_GHZ), 4)}
 
     # the full-causal layer alone (the target configuration)
     causal = [p for p in per_layer if p["window"] >= 8192 and p["prefix"] == 0]
@@ -660,15 +697,16 @@ def main(argv=None):
                               for (w, p) in wl.layers],
                    "parallelism": "single GPU"},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "frac_of_peak_at_measured_sclk": round(value / peak_at_sclk, 4) if sclk else None,
         "useful_flop_per_step": total_flops,
         "full_causal_layer": causal_info,
         "per_layer_ms": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in p.items()}
                          for p in per_layer],
         "roofline": roofline,
+        "roofline_per_launch": launches,
         "cpu_baseline": cpu,
         "peak_mem_bytes": int(peak_mem - base_alloc),
         "peak_mem_including_inputs_bytes": int(peak_mem - base_alloc + inputs_bytes),
+        "diagnostics": diagnostics,
     }
     print(json.dumps(out), flush=True)
     return 0

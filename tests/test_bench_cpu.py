@@ -71,6 +71,18 @@ def test_decode_visible_count():
                 assert bench.decode_visible(n, w, p) == brute(n, w, p)
 
 
+def test_kernel_bytes_of_the_long_context_layers():
+    from workloads import workload_inputs
+    inp = workload_inputs("long_8192")[0]
+    q = 8192 * 64 * 64
+    k = 8192 * 8 * 64
+    rows = 8192 * 64
+    assert bench.kernel_bytes(inp, "sinkattn_fwd_bf16_d64") == 2 * (2 * q + 2 * k) + 4 * rows
+    assert bench.kernel_bytes(inp, "sinkattn_bwd_dq_bf16_d64") == 2 * (4 * q + 2 * k) + 12 * rows
+    # dK/dV: Q, dO, K, V in, dK, dV out (bf16), L and D in: 171.97 MB
+    assert bench.kernel_bytes(inp, "sinkattn_bwd_dkdv_bf16_d64") == 171966464
+
+
 def test_compulsory_bytes_target_layer():
     # T=8192, Hq=64, Hkv=8, d=64: Q, K, V in and O out in bf16 plus l in fp32 is 153.1 MB for
     # the forward; the backward reads Q, K, V, dO and L, D and writes dQ, dK, dV
@@ -120,8 +132,15 @@ def test_committed_traffic_summaries_parse():
         key = re.search(r"^kernel:\s*(\S+)", txt, re.M).group(1)
         assert key in bench.KERNEL_SOURCES, path
         workload = os.path.basename(path)[len(key) + 1:-len("_traffic.md")]
-        val = float(re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt).group(1))
-        assert val > 0
-        got = bench.committed_traffic(key, workload)
         sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt).group(1)
-        assert (got == val) == (sha == bench.kernel_source_sha(key)), path
+        per_layer = re.findall(r"hbm_bytes_per_launch\[layer (\d+)\]:\s*([0-9.eE+]+)", txt)
+        if per_layer:   # attention workloads: one value per layer
+            for layer, val in per_layer:
+                assert float(val) > 0
+                got = bench.committed_traffic(key, workload, int(layer))
+                assert (got == float(val)) == (sha == bench.kernel_source_sha(key)), path
+        else:           # one library call per step (decode, GRPO)
+            val = float(re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt).group(1))
+            assert val > 0
+            got = bench.committed_traffic(key, workload)
+            assert (got == val) == (sha == bench.kernel_source_sha(key)), path
