@@ -12,9 +12,18 @@ extreme masks) use max(2e-2, max|ref| / 64) on O, dQ, dK, dV: a bf16 result
 of magnitude M carries up to M * 2^-8 from its final rounding alone, and the
 probabilities and dS enter the MFMA as bf16 with the same relative error, so
 the bound allows at least four half-ulps of the largest magnitude.
+Extra fp32 cases (the 1e-5 of the fp32 configuration is stated for its small
+shape) use max(1e-5, max|ref| * 2^-18) on O, dQ, dK, dV: a prefix key's dK,
+dV sums hundreds of terms, and an fp32 sum of n terms of magnitude M in
+another order differs by up to about n * 2^-24 * M; 2^-18 allows 64 of those
+terms' roundings of the largest magnitude.
 The ds reading is norm-wise because ds_h is a sum of terms of both signs:
 a head whose sum lands near zero by chance would make a per-head relative
-error meaningless while the absolute error is at rounding level.
+error meaningless while the absolute error is at rounding level.  Extra bf16
+cases with few heads and extreme sinks can draw every head's sum far below
+its terms; there ds also passes head by head within 2^-8 of the magnitude sum
+sum_i |exp(s_h - L_i) D_i|: D is formed from the stored bf16 O, whose RNE
+rounding moves each term by up to 2^-9 of its size.
 """
 from __future__ import annotations
 
@@ -70,6 +79,32 @@ def run_oracle(inp, heads=None, want_grad=True):
     return out
 
 
+def ds_magnitude(inp):
+    """sum_i |exp(s_h - L_i) D_i| per query head: the size of the terms of ds_h, from
+    the oracle's row statistics of every row of every sequence."""
+    q, k, v, do = (t.to(torch.float64).numpy() for t in (inp.q, inp.k, inp.v, inp.do))
+    s = inp.sinks.to(torch.float64).numpy()
+    hq = q.shape[-2]
+    if inp.cu_seqlens is not None:
+        cu = inp.cu_seqlens.numpy()
+        seqs = [(slice(int(cu[z]), int(cu[z + 1])), None) for z in range(len(cu) - 1)]
+    else:
+        seqs = [(slice(None), b) for b in range(q.shape[0])]
+    mag = np.zeros(hq)
+    for rows, b in seqs:
+        for h in range(hq):
+            kv = h // inp.group
+            pick = (lambda t, i: t[rows, i]) if b is None else (lambda t, i: t[b, :, i])
+            qh, kh, vh, dh = pick(q, h), pick(k, kv), pick(v, kv), pick(do, h)
+            n = qh.shape[0]
+            if n == 0:
+                continue
+            st = oracle.rows_head(qh, kh, vh, s[h], inp.window, inp.prefix, inp.scale,
+                                  np.arange(n), do=dh)
+            mag[h] += float(np.sum(np.abs(np.exp(s[h] - st["big_l"]) * st["d_row"])))
+    return mag
+
+
 def head_slices(inp, heads):
     """Index tuples selecting `heads` (query side) and their kv heads."""
     varlen = inp.cu_seqlens is not None
@@ -103,13 +138,21 @@ def compare(gpu, ref, dtype, inp, heads=None, what=("o", "lse", "dq", "dk", "dv"
         assert np.all(np.isfinite(g)), f"{label} {n}: non-finite GPU values"
         if n == "ds" and dtype == "bf16":
             err = float(np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-30))
+            if scaled and err > tol["ds"]:
+                mag = ds_magnitude(inp)[hsel]
+                per_head = float(np.max(np.abs(g - r) / np.maximum(mag, 1e-30)))
+                log(f"  {label} ds: norm-wise {err:.3g}; per head against the magnitude "
+                    f"sums {per_head:.3g} (bound 2^-8 = {2.0 ** -8:.3g})")
+                err = 0.0 if per_head <= 2.0 ** -8 else err
         else:
             err = float(np.max(np.abs(g - r))) if g.size else 0.0
         errs[n] = err
-        if scaled and dtype == "bf16" and n in ("o", "dq", "dk", "dv"):
+        if scaled and n in ("o", "dq", "dk", "dv"):
             tol = dict(tol)
-            tol[n] = max(tol[n], float(np.max(np.abs(r))) / 64 if r.size else 0.0)
-    log(f"  {label} errors: " + ", ".join(f"{n}={e:.3g}" for n, e in errs.items()))
+            rel = 1.0 / 64 if dtype == "bf16" else 2.0 ** -18
+            tol[n] = max(tol[n], float(np.max(np.abs(r))) * rel if r.size else 0.0)
+    log(f"  {label} errors: " + ", ".join(f"{n}={e:.3g}" for n, e in errs.items()) +
+        (f" (largest |ref| of dv {float(np.max(np.abs(ref['dv']))):.3g})" if "dv" in ref else ""))
     for n, e in errs.items():
         assert e <= tol[n], f"{label} {n}: error {e:.3g} > tolerance {tol[n]}"
     return errs

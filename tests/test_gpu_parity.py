@@ -96,6 +96,38 @@ def test_fp32_small(d, case):
     compare(run_gpu(inp), run_oracle(inp), "fp32", inp, label=f"fp32 d{d} {case}")
 
 
+# Mask-edge sweep (the windows and prefixes around every tile size the kernels
+# use: 32- and 64-key tiles, 32-row window dQ blocks, 64-row fp32 row blocks,
+# 128-row dK/dV tiles), ragged lengths packed into one call, and the sink
+# logits -inf, -10, 0, +10 on the four query heads.
+SWEEP_SINKS = (float("-inf"), -10.0, 0.0, 10.0)
+SWEEP_W = (0, 31, 32, 33, 63, 64, 65, 127, 128, 129, WINDOW_INF)
+SWEEP_P = (0, 1, 32, 64, 128, 100000)
+
+
+@pytest.mark.parametrize("w", SWEEP_W, ids=lambda w: f"w{w}")
+@pytest.mark.parametrize("p", SWEEP_P, ids=lambda p: f"p{p}")
+def test_fp32_mask_edge_sweep(w, p):
+    lengths = (1, 63, 65, 129, 130)
+    inp = make_inputs(batch=0, seqlen=0, heads_q=4, heads_kv=2, head_dim=32, window=w, prefix=p,
+                      seed=w % 997 + p % 991, std=1.0, dtype="fp32", lengths=lengths,
+                      sink_values=SWEEP_SINKS)
+    compare(run_gpu(inp), run_oracle(inp), "fp32", inp, label=f"fp32 sweep w={w} p={p}",
+            scaled=True)
+
+
+@pytest.mark.parametrize("w", SWEEP_W + (1023, 1024, 1025), ids=lambda w: f"w{w}")
+@pytest.mark.parametrize("p", SWEEP_P, ids=lambda p: f"p{p}")
+def test_bf16_mask_edge_sweep(w, p):
+    # the longest sequence (1090) puts windows >= 1024 on the 64-key kernels
+    lengths = (1, 31, 33, 127, 129, 257, 1090)
+    inp = make_inputs(batch=0, seqlen=0, heads_q=4, heads_kv=1, head_dim=64, window=w, prefix=p,
+                      seed=w % 997 + 7 * (p % 991), std=1.0, dtype="bf16", lengths=lengths,
+                      sink_values=SWEEP_SINKS)
+    compare(run_gpu(inp), run_oracle(inp), "bf16", inp, label=f"bf16 sweep w={w} p={p}",
+            scaled=True)
+
+
 def test_fp32_varlen():
     inp = make_inputs(batch=0, seqlen=0, heads_q=2, heads_kv=1, head_dim=32, window=9, prefix=3,
                       seed=3, std=1.0, dtype="fp32", lengths=(17, 0, 64, 1))
@@ -373,7 +405,7 @@ def test_gqa_equals_mha_with_repeated_kv():
 def test_memory_grows_linearly():
     """Peak device memory of fwd+bwd (workspace included) is O(T)."""
     peaks = {}
-    for t in (2048, 4096, 8192):
+    for t in (2048, 4096, 8192, 16384):
         inp = make_inputs(batch=1, seqlen=t, heads_q=64, heads_kv=8, head_dim=64,
                           window=WINDOW_INF, prefix=0, seed=1, std=0.5, dtype="bf16")
         dev = torch.device("cuda:0")
@@ -392,6 +424,7 @@ def test_memory_grows_linearly():
     # doubling T must not more than double (plus slack) the extra memory
     assert peaks[4096] <= 2.1 * peaks[2048]
     assert peaks[8192] <= 2.1 * peaks[4096]
+    assert peaks[16384] <= 2.1 * peaks[8192]
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 64), ("fp32", 32)])
