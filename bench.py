@@ -355,6 +355,11 @@ def run_decode(args) -> int:
                           f"(one sinkattn_decode call, layer {dom})",
                 "avg_launch_ms": per_layer[dom]["ms"],
                 "algorithmic_bytes_per_launch": runs[dom]["bytes"]}
+    # every layer's call against HBM (a decode call reads each visible K/V row once)
+    launches = [{"bound": "hbm", "achieved": p["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(p["gbs"] / PEAK_HBM_GBS, 4), "kernel": "one sinkattn_decode call",
+                 "layer": li, "avg_launch_ms": p["ms"], "algorithmic_bytes_per_launch": p["bytes"]}
+                for li, p in enumerate(per_layer)]
     if args.copy_probe:
         copy_probe(dev)
     cpu = None if args.no_cpu_baseline else decode_cpu_baseline(layers)
@@ -475,6 +480,7 @@ def run_grpo(args) -> int:
                 "avg_launch_ms": round(avg_ms, 5), "median_call_ms":
                     round(statistics.median(per_call), 5),
                 "algorithmic_bytes_per_launch": nbytes}
+    launches = [dict(roofline)]   # one call, three kernels: reported together
     if args.copy_probe:
         copy_probe(dev)
     cpu = None if args.no_cpu_baseline else grpo_cpu_baseline(inp)

@@ -144,3 +144,33 @@ def test_committed_traffic_summaries_parse():
             assert val > 0
             got = bench.committed_traffic(key, workload)
             assert (got == val) == (sha == bench.kernel_source_sha(key)), path
+
+
+def test_scripts_reference_only_defined_names():
+    # a name a function reads from module scope must exist there (or be a
+    # builtin): the GPU-only branches of these scripts never run on the CPU, so
+    # a stray name would otherwise surface only on the GPU machine
+    import builtins
+    import os
+    import symtable
+    scripts = ["bench.py", "__graft_entry__.py", "workloads.py", "tests/parity_util.py",
+               "sink_aware_masked_sinkattn_amd/binding.py", "sink_aware_masked_sinkattn_amd/build.py"]
+    for rel in scripts:
+        path = os.path.join(bench.ROOT, rel)
+        if not os.path.exists(path):
+            continue
+        top = symtable.symtable(open(path).read(), rel, "exec")
+        defined = set(dir(builtins)) | {s.get_name() for s in top.get_symbols()
+                                        if s.is_assigned() or s.is_imported() or s.is_namespace()}
+        missing = []
+
+        def walk(t):
+            for s in t.get_symbols():
+                if s.is_global() and s.is_referenced() and s.get_name() not in defined:
+                    missing.append((t.get_name(), s.get_name()))
+            for c in t.get_children():
+                walk(c)
+
+        for c in top.get_children():
+            walk(c)
+        assert not missing, (rel, missing)
