@@ -141,6 +141,53 @@ __device__ __forceinline__ void mask_query_lane(f32x16& st, int base, int pb, in
   }
 }
 
+// The same for the 32 x 32 block of rows [qs, qs + 31] (lane: row qs + l32)
+// and keys [ks, ks + 31] (element i: key ks + 4g + c_i), in the cheapest
+// exact form the block's geometry allows (dq = qs - ks, uniform branches):
+//  * the window bound cannot bind (every key a prefix key, or no prefix key
+//    and dq + 31 <= w): visible iff k <= q, i.e. c_i <= base;
+//  * no key past its row (dq >= 31) and no prefix key: visible iff
+//    q - k <= w, i.e. c_i >= base - w;
+//  * prefix keys mixed in, but every row past the window of the block's
+//    other keys (dq > w + 31): visible iff k < p, i.e. c_i < p - kr;
+//  * otherwise the general predicate above.
+// Each of the first three is one compare against a constant and one select
+// per element.
+__device__ __forceinline__ void mask_query_block(f32x16& st, int qs, int ks, int lane, int window,
+                                                 int prefix) {
+  // the form is chosen from wave-uniform values only, so the branches are scalar
+  const int dq = __builtin_amdgcn_readfirstlane(qs - ks);
+  const int ku = __builtin_amdgcn_readfirstlane(ks);
+  const int kr = ku + 4 * (lane >> 5);
+  const int base = sa_opaque(__builtin_amdgcn_readfirstlane(qs) + (lane & 31) - kr);
+  const bool all_prefix = ku + 31 < prefix;
+  const bool no_prefix = ku >= prefix;
+  int form;   // 0: c_i <= base, 1: c_i >= base - w, 2: c_i < p - kr, 3: general
+  if (all_prefix || (no_prefix && dq <= window - 31)) form = 0;
+  else if (no_prefix && dq >= 31) form = 1;
+  else if (!no_prefix && dq - 31 > window) form = 2;
+  else form = 3;
+  if (form == 3) {
+    mask_query_lane<true>(st, base, sa_opaque(prefix - kr), window);
+    return;
+  }
+  const bool upper = form != 1;
+  const int th = sa_opaque(form == 0 ? base : form == 1 ? base - window : prefix - kr - 1);
+  if (upper) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 8 * (i >> 2) + (i & 3);
+      st[i] = c <= th ? st[i] : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 8 * (i >> 2) + (i & 3);
+      st[i] = c >= th ? st[i] : -INFINITY;
+    }
+  }
+}
+
 // Where a sequence lives in the packed/batched tensors.
 struct SeqView {
   int row_base;  // first token row of the sequence in [B*T] or [N]

@@ -175,9 +175,16 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int kr = k0 + kb * 32 + 4 * g;
-        const int base = sa_opaque(qw0 + qb * 32 + l32 - kr);
-        mask_query_lane<true>(st[kb][qb], base, sa_opaque(prefix - kr), window);
+        if constexpr (NKB == 1) {
+          // window layers: most partial tiles take a one-sided form
+          mask_query_block(st[kb][qb], qw0 + qb * 32, k0 + kb * 32, lane, window, prefix);
+        } else {
+          // 64-key tiles (long windows, causal): few partial tiles; the general
+          // predicate keeps the kernel within its registers
+          const int kr = k0 + kb * 32 + 4 * g;
+          const int base = sa_opaque(qw0 + qb * 32 + l32 - kr);
+          mask_query_lane<true>(st[kb][qb], base, sa_opaque(prefix - kr), window);
+        }
       }
   }
   // ---- online softmax in the log2 domain, lazily rescaled
