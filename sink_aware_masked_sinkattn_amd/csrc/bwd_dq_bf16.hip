@@ -82,7 +82,9 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
 }
 
 // One key tile (NKB blocks of 32 keys) against this wave's QB blocks of 32
-// query rows.  MASK: apply the element predicate (partial tiles only).
+// query rows.  MF: the mask -- 0 none (full tiles), SA_MASK_GENERAL the
+// element predicate, SA_MASK_UPPER / SA_MASK_LOWER the one-sided forms of
+// mask_form with the per-lane threshold thr (32-key tiles, one row block).
 //
 // Issue order, per (key block, query block): S^T chain; dP^T chain with a
 // quarter of the P' work after each MFMA; the first half of dS, then its two
@@ -91,12 +93,14 @@ __device__ __forceinline__ int map_head(int x, int heads_q) {
 // that to the other waves of its SIMD.  The next key block's operands are
 // read behind the last query block's MFMAs.  sched_barrier fences hold each
 // part in place.
-template <int NKB, int QB, bool MASK>
+template <int NKB, int QB, int MF>
 __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB][4],
                                           const bf16x8 (&df)[QB][4], const float (&l2)[QB],
                                           const float (&dd)[QB], f32x16 (&acc)[QB][2], int qw0,
                                           int k0, int window, int prefix, float scale_log2,
-                                          int lane) {
+                                          int lane, int thr = 0) {
+  static_assert(MF == 0 || MF == SA_MASK_GENERAL || (NKB == 1 && QB == 1),
+                "one-sided masks: 32-key tiles, one row block");
   const int l32 = lane & 31;
   const int g = lane >> 5;
   const int grp = lane >> 4;
@@ -157,9 +161,13 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * j + e;
           float p = fast_exp2(fmaf(st[i], scale_log2, -l2[qb]));
-          if (MASK) {
+          if (MF == SA_MASK_GENERAL) {
             const int c = 8 * j + e;
             p = sa_vis(base - c, c < pb ? SA_LIM_PREFIX : window) ? p : 0.0f;
+          } else if (MF == SA_MASK_UPPER) {
+            p = 8 * j + e <= thr ? p : 0.0f;
+          } else if (MF == SA_MASK_LOWER) {
+            p = 8 * j + e >= thr ? p : 0.0f;
           }
           pp[i] = sa_pin(p);
         }
@@ -183,6 +191,27 @@ __device__ __forceinline__ void tile_step(uint32_t ktile, const bf16x8 (&qf)[QB]
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// A partial 32-key tile of one 32-row block in the cheapest exact form of
+// its mask (mask_form).
+__device__ __forceinline__ void partial_step(uint32_t ktile, const bf16x8 (&qf)[1][4],
+                                             const bf16x8 (&df)[1][4], const float (&l2)[1],
+                                             const float (&dd)[1], f32x16 (&acc)[1][2], int qw0,
+                                             int k0, int window, int prefix, float scale_log2,
+                                             int lane) {
+  int thr;
+  const int form = mask_form(qw0, k0, lane, window, prefix, &thr);
+  thr = sa_opaque(thr);
+  if (form == SA_MASK_UPPER)
+    tile_step<1, 1, SA_MASK_UPPER>(ktile, qf, df, l2, dd, acc, qw0, k0, window, prefix, scale_log2,
+                                   lane, thr);
+  else if (form == SA_MASK_LOWER)
+    tile_step<1, 1, SA_MASK_LOWER>(ktile, qf, df, l2, dd, acc, qw0, k0, window, prefix, scale_log2,
+                                   lane, thr);
+  else
+    tile_step<1, 1, SA_MASK_GENERAL>(ktile, qf, df, l2, dd, acc, qw0, k0, window, prefix,
+                                     scale_log2, lane);
 }
 
 // The backward's row statistics for one query row, from this lane's half
@@ -322,9 +351,14 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
                                 : SA_TILE_SKIP;
     const uint32_t ktile = lds_addr(smem + (2 * buf) * TILE_ELEMS);   // V tile follows
     if (cls == SA_TILE_FULL) {
-      tile_step<NKB, QB, false>(ktile, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      tile_step<NKB, QB, 0>(ktile, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
     } else if (cls == SA_TILE_PARTIAL) {
-      tile_step<NKB, QB, true>(ktile, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      if constexpr (NKB == 1 && QB == 1) {
+        partial_step(ktile, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix, a.scale_log2, lane);
+      } else {
+        tile_step<NKB, QB, SA_MASK_GENERAL>(ktile, qf, df, l2, dd, acc, qw0, k0, a.window, a.prefix,
+                                            a.scale_log2, lane);
+      }
     }
     wait_all_mem();
     __syncthreads();
@@ -521,11 +555,11 @@ void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
       const int cls = sa_tile_class(q_start, q_last, k0, k0 + 31, a.window, a.prefix);
       const uint32_t ktile = lds_addr(sm.kv[t][0]);   // V tile follows
       if (cls == SA_TILE_FULL)
-        tile_step<1, 1, false>(ktile, qf, df, l2, dd, acc, q_start, k0, a.window, a.prefix,
-                               a.scale_log2, lane);
+        tile_step<1, 1, 0>(ktile, qf, df, l2, dd, acc, q_start, k0, a.window, a.prefix,
+                           a.scale_log2, lane);
       else if (cls == SA_TILE_PARTIAL)
-        tile_step<1, 1, true>(ktile, qf, df, l2, dd, acc, q_start, k0, a.window, a.prefix,
-                              a.scale_log2, lane);
+        partial_step(ktile, qf, df, l2, dd, acc, q_start, k0, a.window, a.prefix, a.scale_log2,
+                     lane);
     }
 
     // dQ = scale * acc through this wave's staging rows (runs of 4 head dims

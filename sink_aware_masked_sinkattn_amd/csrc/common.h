@@ -141,39 +141,57 @@ __device__ __forceinline__ void mask_query_lane(f32x16& st, int base, int pb, in
   }
 }
 
-// The same for the 32 x 32 block of rows [qs, qs + 31] (lane: row qs + l32)
-// and keys [ks, ks + 31] (element i: key ks + 4g + c_i), in the cheapest
-// exact form the block's geometry allows (dq = qs - ks, uniform branches):
+// The cheapest exact form of the mask of the 32 x 32 block of rows
+// [qs, qs + 31] (lane: row qs + l32) and keys [ks, ks + 31] (element i: key
+// ks + 4g + c_i, c_i = 8*(i/4) + i%4), chosen from wave-uniform values
+// (dq = qs - ks), with base = qs + l32 - kr, kr = ks + 4g:
 //  * the window bound cannot bind (every key a prefix key, or no prefix key
-//    and dq + 31 <= w): visible iff k <= q, i.e. c_i <= base;
+//    and dq + 31 <= w): visible iff k <= q, i.e. c_i <= base   (UPPER);
 //  * no key past its row (dq >= 31) and no prefix key: visible iff
-//    q - k <= w, i.e. c_i >= base - w;
+//    q - k <= w, i.e. c_i >= base - w                          (LOWER);
 //  * prefix keys mixed in, but every row past the window of the block's
-//    other keys (dq > w + 31): visible iff k < p, i.e. c_i < p - kr;
-//  * otherwise the general predicate above.
-// Each of the first three is one compare against a constant and one select
-// per element.
-__device__ __forceinline__ void mask_query_block(f32x16& st, int qs, int ks, int lane, int window,
-                                                 int prefix) {
-  // the form is chosen from wave-uniform values only, so the branches are scalar
+//    other keys (dq > w + 31): visible iff k < p, i.e. c_i <= p - kr - 1
+//                                                              (UPPER);
+//  * otherwise the general predicate of mask_query_lane        (GENERAL).
+// UPPER and LOWER cost one compare against a constant and one select per
+// element.  *thr: the per-lane threshold of UPPER / LOWER.
+enum { SA_MASK_UPPER = 1, SA_MASK_LOWER = 2, SA_MASK_GENERAL = 3 };
+__device__ __forceinline__ int mask_form(int qs, int ks, int lane, int window, int prefix,
+                                         int* thr) {
   const int dq = __builtin_amdgcn_readfirstlane(qs - ks);
   const int ku = __builtin_amdgcn_readfirstlane(ks);
   const int kr = ku + 4 * (lane >> 5);
-  const int base = sa_opaque(__builtin_amdgcn_readfirstlane(qs) + (lane & 31) - kr);
+  const int base = __builtin_amdgcn_readfirstlane(qs) + (lane & 31) - kr;
   const bool all_prefix = ku + 31 < prefix;
   const bool no_prefix = ku >= prefix;
-  int form;   // 0: c_i <= base, 1: c_i >= base - w, 2: c_i < p - kr, 3: general
-  if (all_prefix || (no_prefix && dq <= window - 31)) form = 0;
-  else if (no_prefix && dq >= 31) form = 1;
-  else if (!no_prefix && dq - 31 > window) form = 2;
-  else form = 3;
-  if (form == 3) {
-    mask_query_lane<true>(st, base, sa_opaque(prefix - kr), window);
+  if (all_prefix || (no_prefix && dq <= window - 31)) {
+    *thr = base;
+    return SA_MASK_UPPER;
+  }
+  if (no_prefix && dq >= 31) {
+    *thr = base - window;
+    return SA_MASK_LOWER;
+  }
+  if (!no_prefix && dq - 31 > window) {
+    *thr = prefix - kr - 1;
+    return SA_MASK_UPPER;
+  }
+  *thr = 0;
+  return SA_MASK_GENERAL;
+}
+
+// Mask the block's 16 elements of this lane to -inf in that form.
+__device__ __forceinline__ void mask_query_block(f32x16& st, int qs, int ks, int lane, int window,
+                                                 int prefix) {
+  int thr;
+  const int form = mask_form(qs, ks, lane, window, prefix, &thr);
+  if (form == SA_MASK_GENERAL) {
+    const int kr = ks + 4 * (lane >> 5);
+    mask_query_lane<true>(st, sa_opaque(qs + (lane & 31) - kr), sa_opaque(prefix - kr), window);
     return;
   }
-  const bool upper = form != 1;
-  const int th = sa_opaque(form == 0 ? base : form == 1 ? base - window : prefix - kr - 1);
-  if (upper) {
+  const int th = sa_opaque(thr);
+  if (form == SA_MASK_UPPER) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int c = 8 * (i >> 2) + (i & 3);
