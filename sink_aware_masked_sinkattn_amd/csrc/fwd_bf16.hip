@@ -33,7 +33,8 @@
 //     MFMA against a 0/1 selector also forms the row sums from fp16 copies);
 //   * each wave classifies every key tile against its own rows: skipped
 //     tiles cost nothing, full tiles run mask-free, partial tiles apply the
-//     element predicate;
+//     element predicate (with 32-key tiles, in a one-sided form -- one
+//     compare per element -- when the tile's geometry allows, mask_form);
 //   * grid z runs from the last query tile to the first (longest rows start
 //     first); grid x maps the heads so that one kv-group's query heads share
 //     an XCD and its L2 (consecutive workgroups go to consecutive XCDs).
