@@ -178,10 +178,11 @@ def compulsory_bytes(inp) -> tuple:
     return fwd, bwd
 
 
-def cpu_baseline(layers, head_dim: int):
-    """The fp64 oracle as it stands, timed on a bounded sample: the first
-    four query heads of each layer (forward + backward over the full
-    sequence, or every packed sequence; about 10 s on 16 host cores)."""
+def cpu_baseline(layers, head_dim: int, min_seconds: float = 10.0):
+    """The fp64 oracle as it stands, timed on a bounded sample: query heads of
+    every layer in groups of CPU_SAMPLE_HEADS (each with its own kv head, forward
+    + backward over the full sequence, or every packed sequence), group after
+    group until at least `min_seconds` have passed (10-30 s on 16 host cores)."""
     import numpy as np  # noqa: F401
     import torch
 
@@ -191,25 +192,30 @@ def cpu_baseline(layers, head_dim: int):
         cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else 1
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    flops = 0.0
-    t0 = time.perf_counter()
-    for inp in layers:
-        sl = slice(0, CPU_SAMPLE_HEADS)
-        q, k, v, do = (t[..., sl, :].to(torch.float64).numpy()
-                       for t in (inp.q, inp.k, inp.v, inp.do))
-        s = inp.sinks[sl].to(torch.float64).numpy()
-        cu = inp.cu_seqlens.numpy() if inp.cu_seqlens is not None else None
-        oracle.forward(q, k, v, s, inp.window, inp.prefix, inp.scale, cu_seqlens=cu)
-        oracle.backward(q, k, v, s, do, inp.window, inp.prefix, inp.scale, cu_seqlens=cu)
-        lens = inp.lengths if inp.lengths is not None else (inp.q.shape[1],) * inp.q.shape[0]
-        flops += (14 * head_dim * CPU_SAMPLE_HEADS *
-                  sum(visible_pairs_per_head(n, inp.window, inp.prefix) for n in lens))
-    dt = time.perf_counter() - t0
     hq = layers[0].q.shape[-2]
+    group = hq // layers[0].k.shape[-2]
+    flops = 0.0
+    heads_done = 0
+    t0 = time.perf_counter()
+    while heads_done < hq and (heads_done == 0 or time.perf_counter() - t0 < min_seconds):
+        heads = list(range(heads_done, min(hq, heads_done + CPU_SAMPLE_HEADS)))
+        kvh = [h // group for h in heads]
+        for inp in layers:
+            q, do = (t[..., heads, :].to(torch.float64).numpy() for t in (inp.q, inp.do))
+            k, v = (t[..., kvh, :].to(torch.float64).numpy() for t in (inp.k, inp.v))
+            s = inp.sinks[heads].to(torch.float64).numpy()
+            cu = inp.cu_seqlens.numpy() if inp.cu_seqlens is not None else None
+            oracle.forward(q, k, v, s, inp.window, inp.prefix, inp.scale, cu_seqlens=cu)
+            oracle.backward(q, k, v, s, do, inp.window, inp.prefix, inp.scale, cu_seqlens=cu)
+            lens = inp.lengths if inp.lengths is not None else (inp.q.shape[1],) * inp.q.shape[0]
+            flops += (14 * head_dim * len(heads) *
+                      sum(visible_pairs_per_head(n, inp.window, inp.prefix) for n in lens))
+        heads_done += len(heads)
+    dt = time.perf_counter() - t0
     what = ("every packed sequence" if layers[0].lengths is not None
             else f"T={layers[0].q.shape[1]}")
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{CPU_SAMPLE_HEADS} of {hq} query heads per layer ({len(layers)} "
+            "sample": f"{heads_done} of {hq} query heads per layer ({len(layers)} "
                       f"layer(s), {what}), fwd+bwd in fp64; {dt:.1f} s",
             "seconds": round(dt, 3)}
 
