@@ -145,13 +145,17 @@ sinkattn_status sinkattn_bwd(const sinkattn_problem *problem, const void *q,
  *   PREPARE: fp32: clears dsinks and runs the row pass; bf16: nothing
  *            (except clearing dsinks for an empty problem);
  *   DQ:      dQ, written to dq (bf16: also the row statistics, each
- *            workgroup's part of dsinks into the workspace, and clearing the
- *            fp32 dK/dV workspace accumulators);
+ *            workgroup's part of dsinks into the workspace, clearing the
+ *            fp32 dK/dV workspace accumulators, and, for short windows with
+ *            0 < prefix <= 16, the prefix keys' part of dK, dV from the rows
+ *            past the first key block's window, per workgroup into the
+ *            workspace);
  *   DKDV:    dK, dV from the recomputed probabilities exp(S - L) (bf16: into
  *            the fp32 workspace accumulators; fp32: into dk, dv);
- *   FINISH:  bf16: scales and converts the dK/dV accumulators into dk, dv,
- *            and writes dsinks as the sum of DQ's parts, added in a fixed
- *            order (so dsinks is the same on every call); fp32: nothing.
+ *   FINISH:  bf16: adds DQ's prefix-key parts into the dK/dV accumulators,
+ *            scales and converts them into dk, dv, and writes dsinks as the
+ *            sum of DQ's parts; every sum is taken in a fixed order (so dk,
+ *            dv and dsinks are the same on every call); fp32: nothing.
  * sinkattn_bwd(...) == sinkattn_bwd_phases(SINKATTN_BWD_ALL, ...).
  */
 enum {

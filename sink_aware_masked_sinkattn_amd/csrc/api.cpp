@@ -20,14 +20,21 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                     const bf16* dout, const float* l_ws, const float* d_ws,
                                     float* dk_acc, float* dv_acc, const int* cu_seqlens,
                                     int batch, int seqlen, int rows_total, int heads_q,
-                                    int heads_kv, int window, int prefix, float scale,
+                                    int heads_kv, int window, int prefix, float scale, bool fold,
                                     hipStream_t stream);
 hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
                                   const bf16* o, const float* lse, const float* sinks,
                                   float* ds_part, int ds_stride, float* l_ws, float* d_ws, float* dk_acc,
                                   float* dv_acc, bf16* dq, const int* cu_seqlens, int batch,
                                   int seqlen, int rows_total, int heads_q, int heads_kv, int window,
-                                  int prefix, float scale, hipStream_t stream);
+                                  int prefix, float scale, long long fold_row, float* fold_part,
+                                  hipStream_t stream);
+bool dq_prefix_fold(int seqlen, int group, int window, int prefix);
+hipError_t launch_prefix_fold_add(const float* fold_part, float* dk_acc, float* dv_acc,
+                                  const int* cu_seqlens, int batch, int seqlen, int heads_kv,
+                                  int prefix, int ds_stride, long long fold_row,
+                                  hipStream_t stream);
+long long dkdv_prefix_fold_row(int window);
 int dq_launch_tiles(int batch, int seqlen, int total_tokens, bool varlen, int group, int window,
                     int prefix);
 hipError_t launch_fwd_f32(int head_dim, const float* q, const float* k, const float* v,
@@ -108,9 +115,14 @@ sinkattn_status check_problem(const sinkattn_problem* pb, Dims* dims) {
 }
 
 struct Workspace {
-  size_t d_off, l_off, dk_off, dv_off, ds_off, total;
+  size_t d_off, l_off, dk_off, dv_off, ds_off, fold_off, total;
   int ds_stride;   // slots per head for the parts of ds_h (bf16)
+  bool fold;       // the window dQ kernel takes the prefix keys' rows past the fold row
 };
+
+// window and prefix as the kernels see them: clamped to the longest sequence
+int clamped_window(const sinkattn_problem* pb) { return pb->window > pb->seqlen ? pb->seqlen : pb->window; }
+int clamped_prefix(const sinkattn_problem* pb) { return pb->prefix > pb->seqlen ? pb->seqlen : pb->prefix; }
 
 Workspace workspace_layout(const sinkattn_problem* pb, const Dims& dims) {
   Workspace w;
@@ -123,12 +135,18 @@ Workspace workspace_layout(const sinkattn_problem* pb, const Dims& dims) {
   const long long blocks32 = (long long)pb->batch * ((pb->seqlen + 31) / 32);
   w.ds_stride = accum ? (int)blocks32 : 0;
   const size_t ds = accum ? round_up((size_t)blocks32 * pb->heads_q * sizeof(float)) : 0;
+  // prefix fold: per (kv head, slot) the block's dK and dV rows of the prefix keys
+  const int prefix = clamped_prefix(pb);
+  w.fold = accum && dq_prefix_fold(pb->seqlen, pb->heads_q / pb->heads_kv, clamped_window(pb), prefix);
+  const size_t fold = w.fold ? round_up((size_t)blocks32 * pb->heads_kv * 2 * prefix *
+                                        pb->head_dim * sizeof(float)) : 0;
   w.d_off = 0;
   w.l_off = stat;
   w.dk_off = 2 * stat;
   w.dv_off = w.dk_off + kvacc;
   w.ds_off = w.dv_off + kvacc;
-  w.total = w.ds_off + ds;
+  w.fold_off = w.ds_off + ds;
+  w.total = w.fold_off + fold;
   return w;
 }
 
@@ -270,8 +288,9 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
   float* dk_acc = is_f32 ? nullptr : (float*)(ws + wl.dk_off);
   float* dv_acc = is_f32 ? nullptr : (float*)(ws + wl.dv_off);
   float* ds_part = is_f32 ? nullptr : (float*)(ws + wl.ds_off);
-  const int window = pb->window > pb->seqlen ? pb->seqlen : pb->window;
-  const int prefix = pb->prefix > pb->seqlen ? pb->seqlen : pb->prefix;
+  const int window = clamped_window(pb);
+  const int prefix = clamped_prefix(pb);
+  float* fold_part = wl.fold ? (float*)(ws + wl.fold_off) : nullptr;
   const int rows = (int)dims.rows;
   const int lse_stride = dims.varlen ? rows : pb->seqlen;
   // fp32: the row pass (D, L, dsinks) is its own kernel; bf16: the dQ kernel
@@ -287,7 +306,8 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
     e = launch_bwd_dq_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
                                (const bf16*)o, lse, sinks, ds_part, wl.ds_stride, l_ws, d_ws, dk_acc, dv_acc,
                                (bf16*)dq, pb->cu_seqlens, pb->batch, pb->seqlen, rows,
-                               pb->heads_q, pb->heads_kv, window, prefix, pb->softmax_scale, s);
+                               pb->heads_q, pb->heads_kv, window, prefix, pb->softmax_scale,
+                               dkdv_prefix_fold_row(window), fold_part, s);
     if (e != hipSuccess) return hip_status(e);
   }
   if (is_f32 && (phases & (SINKATTN_BWD_DKDV | SINKATTN_BWD_DQ))) {
@@ -303,13 +323,19 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
     e = launch_bwd_dkdv_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v,
                                  (const bf16*)dout, l_ws, d_ws, dk_acc, dv_acc, pb->cu_seqlens,
                                  pb->batch, pb->seqlen, rows, pb->heads_q, pb->heads_kv, window,
-                                 prefix, pb->softmax_scale, s);
+                                 prefix, pb->softmax_scale, wl.fold, s);
     if (e != hipSuccess) return hip_status(e);
   }
   if ((phases & SINKATTN_BWD_FINISH) && !is_f32) {
     // the slots the dQ kernel wrote: one per workgroup of a head
     const int ds_used = dq_launch_tiles(pb->batch, pb->seqlen, rows, dims.varlen,
                                         pb->heads_q / pb->heads_kv, window, prefix);
+    if (wl.fold) {
+      e = launch_prefix_fold_add(fold_part, dk_acc, dv_acc, pb->cu_seqlens, pb->batch,
+                                 pb->seqlen, pb->heads_kv, prefix, wl.ds_stride,
+                                 dkdv_prefix_fold_row(window), s);
+      if (e != hipSuccess) return hip_status(e);
+    }
     e = launch_convert(dk_acc, dv_acc, (bf16*)dk, (bf16*)dv,
                        (long long)rows * pb->heads_kv * pb->head_dim, pb->softmax_scale, ds_part,
                        ds_used, wl.ds_stride, pb->heads_q, dsinks, s);

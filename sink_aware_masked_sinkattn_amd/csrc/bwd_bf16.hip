@@ -58,6 +58,8 @@ struct DkvArgs {
   int seqlen, heads_q, heads_kv, group, window, prefix, rows_total;
   int batch;
   int chunk_shift;        // iterations per work unit: 2^chunk_shift
+  int fold;               // 1: the window dQ kernel adds the prefix keys' part of rows past
+                          // the fold row (sa_dkdv_query_range stops the blocks there)
   float scale_log2;
 };
 
@@ -218,18 +220,19 @@ __device__ __forceinline__ bool dkdv_find_unit(const DkvArgs& a, int item, int l
     const int nkb = (len + BKW - 1) / BKW;
     if (nkb == 0) continue;
     const int cmax = sa_dkdv_block_chunks(0, len, a.window, a.prefix, a.group, BQ, BKW,
-                                          a.chunk_shift);
+                                          a.chunk_shift, a.fold);
     // chunk counts of this lane's key blocks are recomputed per level when
     // the sequence has more than 64 blocks, kept in a register otherwise
     const int own = lane < nkb ? sa_dkdv_block_chunks(lane, len, a.window, a.prefix, a.group, BQ,
-                                                      BKW, a.chunk_shift)
+                                                      BKW, a.chunk_shift, a.fold)
                                : 0;
     for (int c = cmax - 1; c >= 0; --c) {
       for (int kb0 = 0; kb0 < nkb; kb0 += 64) {
         const int kb = kb0 + lane;
         const int ch = kb0 == 0 ? own
                                 : (kb < nkb ? sa_dkdv_block_chunks(kb, len, a.window, a.prefix,
-                                                                   a.group, BQ, BKW, a.chunk_shift)
+                                                                   a.group, BQ, BKW, a.chunk_shift,
+                                                                   a.fold)
                                             : 0);
         const bool has = ch > c;
         const unsigned long long m = __ballot(has);
@@ -265,9 +268,9 @@ __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
   const SeqView sv = seq_view(a.cu_seqlens, z, a.seqlen, a.heads_q);
   const int k_start = kblk * BKW;
   if (k_start >= sv.len) return;
-  const int k_last = min(k_start + BKW - 1, sv.len - 1);
   int q_lo, q_hi;
-  if (!sa_query_range(k_start, k_last, sv.len, a.window, a.prefix, &q_lo, &q_hi)) return;
+  if (!sa_dkdv_query_range(kblk, sv.len, a.window, a.prefix, BQ, BKW, a.fold, &q_lo, &q_hi))
+    return;
   const int qt_begin = q_lo / BQ;
   const int n_qt = q_hi / BQ - qt_begin + 1;
   const int n_iter_all = n_qt * a.group;
@@ -365,7 +368,7 @@ __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
                        q0, kw0, a.window, a.prefix, a.scale_log2, lane);
     } else if (cls == SA_TILE_PARTIAL) {
       tile_step<BQ, true>(lds_addr(sm.qt[buf]), sm.l2[buf], sm.dd[buf], kf, vf, dk_acc, dv_acc,
-                      q0, kw0, a.window, a.prefix, a.scale_log2, lane);
+                       q0, kw0, a.window, a.prefix, a.scale_log2, lane);
     }
     if (it + 1 < it_end) store_stats(buf ^ 1);
     wait_all_mem();
@@ -414,6 +417,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DKDV_OCC, D
 // measured slower even for w = 128 (more iterations per workgroup).
 int dkdv_query_tile(int window) { (void)window; return 128; }
 
+// First row past which the dK/dV kernel's first key block sees only its
+// prefix keys (the rows it stops at when the window dQ kernel folds them).
+long long dkdv_prefix_fold_row(int window) {
+  return sa_prefix_fold_row(0, window, BKW, dkdv_query_tile(window));
+}
+
 // Iterations per work unit: about DKDV_TARGET_UNITS units over the whole call
 // so the longest one is short next to the total (no long tail), but long
 // enough that the per-unit atomic flush of dK/dV stays small (at least
@@ -429,7 +438,7 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                     const bf16* dout, const float* l_ws, const float* d_ws,
                                     float* dk_acc, float* dv_acc, const int* cu_seqlens,
                                     int batch, int seqlen, int rows_total, int heads_q,
-                                    int heads_kv, int window, int prefix, float scale,
+                                    int heads_kv, int window, int prefix, float scale, bool fold,
                                     hipStream_t stream) {
   DkvArgs a;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.l2_ws = l_ws; a.d_ws = d_ws;
@@ -439,6 +448,7 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
   a.rows_total = rows_total;
   a.scale_log2 = scale * SA_LOG2E;
   a.batch = batch;
+  a.fold = fold ? 1 : 0;
   const int nkb = (seqlen + BKW - 1) / BKW;
   if (nkb == 0 || batch == 0) return hipSuccess;
   const int BQ = dkdv_query_tile(window);
@@ -446,25 +456,27 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
   // the longest length, so this bounds every sequence)
   long long iters = 0;
   for (int kb = 0; kb < nkb; ++kb)
-    iters += (long long)sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW, 0);
+    iters += (long long)sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW, 0, fold);
   a.chunk_shift = bwd_dkdv_chunk_shift(iters * batch * heads_kv);
   long long units = 0;
   for (int kb = 0; kb < nkb; ++kb)
-    units += sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW, a.chunk_shift);
+    units += sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW, a.chunk_shift,
+                                  fold);
   units *= batch;   // every sequence at the longest length
   if (cu_seqlens) {
     // Packed sequences of total length rows_total: a bound from the token count (the
     // lengths stay on the device).  A block holding prefix keys (the first ceil(p / BKW))
     // sees every later row, ceil(n / BQ) query tiles, so at most
-    // ceil(ceil(n / BQ) * group / 2^s) units; any other block sees at most BKW + w rows,
+    // ceil(ceil(n / BQ) * group / 2^s) units (with the fold its range stops at the fold
+    // row and it counts with the others); any other block sees at most BKW + w rows,
     // no more units than the largest count among such blocks at the longest length (the
     // same key offsets, a query range no longer).  With sum ceil(n / B) <= (N + G (B - 1)) / B
     // over the sequences, the units of the whole launch stay within the sum below.
-    const int npb = min((prefix + BKW - 1) / BKW, nkb);
+    const int npb = fold ? 0 : min((prefix + BKW - 1) / BKW, nkb);
     long long cw = 0;
     for (int kb = npb; kb < nkb; ++kb)
       cw = max(cw, (long long)sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW,
-                                                    a.chunk_shift));
+                                                    a.chunk_shift, fold));
     const long long tiles_q = sa_packed_tiles_bound(batch, seqlen, rows_total, BQ);
     const long long blocks = sa_packed_tiles_bound(batch, seqlen, rows_total, BKW);
     const long long per_chunk = 1LL << a.chunk_shift;

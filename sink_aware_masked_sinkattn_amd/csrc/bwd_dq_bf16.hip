@@ -72,6 +72,12 @@ struct DqArgs {
   int batch, seqlen, heads_q, heads_kv, group, window, prefix, rows_total;
   int num_q_tiles;        // fixed length: query tiles per sequence
   int lse_head_stride;    // T (fixed length) or N (packed)
+  // prefix fold (window kernel): rows at or past fold_row add the prefix keys'
+  // dK/dV part of their block into fold_part[(kv head * ds_stride + slot) *
+  // 2 * prefix * D]: dK (unscaled) then dV, prefix keys x head dims
+  int fold;
+  long long fold_row;
+  float* fold_part;
   float scale_log2;
   float scale;
 };
@@ -456,6 +462,182 @@ struct __attribute__((aligned(128))) DqWinSmem {
   bf16 stage[WAVES][32 * OROW];     // each wave's dQ rows, for row-contiguous stores
 };
 
+// The prefix fold: the prefix keys' (keys 0 .. p-1, p <= 16, all in the
+// resident tile 0) part of dK and dV from this block's rows, when they lie at
+// or past the fold row -- rows that see no other key of the dK/dV kernel's
+// first key block, whose work stops before them; they see exactly the keys
+// k < p.  Each wave takes its heads two at a time, with the heads' Q and dO
+// rows copied into the block's LDS (the key tiles are no longer needed once
+// the K, V operands of keys 0..15 are in registers) and their L and -D read
+// back from the workspace this wave wrote them to, and runs for each head a
+// 32-row x 16-key step on v_mfma_f32_16x16x32_bf16 (fold_step16).  The four
+// waves' sums are added in wave order and the block's part goes to its slot;
+// the finish phase adds a sequence's slots in order into the fp32 dK/dV
+// accumulators.  Blocks before the fold row write nothing (the finish phase
+// reads only the slots past it).
+//
+// LDS during the fold (the whole DqWinSmem, 66 KB): wave w's two Q / dO
+// tiles at 16 KB * w (+ 8 KB for the second head; dO 4 KB after its Q),
+// the heads' L and -D rows in the last 2 KB.
+constexpr int FOLD_WAVE_BYTES = 2 * 2 * 32 * D * 2;
+constexpr int FOLD_STAT_OFF = WAVES * FOLD_WAVE_BYTES;
+constexpr int FOLD_KEYS = 16;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One head's part of the prefix keys' dK (unscaled dS^T Q) and dV (P'^T dO)
+// from the block's 32 rows, keys 0..15, on the 16x16x32 MFMA (lane l: G =
+// l/16, i = l%16; A: row i, k 8G..8G+7; B: column i, k 8G..8G+7; C: column i,
+// rows 4G..4G+3):
+//   S = Q K^T and dP = dO V^T, per 16-row half h: rows on m, keys on n, the
+//     head dim on k (two k-steps of 32); dP starts from -D of its rows;
+//   P' = exp2(S scale log2 e - L) for keys < p (0 otherwise), dS = P' (dP - D);
+//   dV += P'^T dO and dK += dS^T Q with keys on m, d on n (four blocks of 16)
+//     and the rows on k in the order 4G..4G+3, 16+4G..16+4G+3: P' and dS in
+//     the C layout of S are then already the A operand, and the B operand
+//     (dO, Q) is two transpose reads of four rows each.
+// kb16 / vb16: B operands of S / dP (K and V rows of keys 0..15, k-step ks).
+__device__ __forceinline__ void fold_step16(uint32_t qtile, uint32_t dtile, const float* l2s,
+                                            const float* dds, const bf16x8 (&kb16)[2],
+                                            const bf16x8 (&vb16)[2], f32x4 (&dk)[4],
+                                            f32x4 (&dv)[4], int prefix, float scale_log2,
+                                            int lane) {
+  const int G = lane >> 4, i16 = lane & 15;
+  f32x4 pq[2], dq4[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = 16 * h + i16;   // A row of this lane
+    f32x4 sacc = f32x4{};
+    f32x4 dacc = *(const f32x4*)(dds + 16 * h + 4 * G);   // -D of rows 16h + 4G + j
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c8 = 4 * ks + G;   // 16-byte chunk of the head dim
+      const bf16x8 qa = lds_read8(qtile + (uint32_t)(r * 128 + ((c8 ^ tile_swz(r)) << 4)));
+      const bf16x8 da = lds_read8(dtile + (uint32_t)(r * 128 + ((c8 ^ tile_swz(r)) << 4)));
+      sacc = mfma16(qa, kb16[ks], sacc);
+      dacc = mfma16(da, vb16[ks], dacc);
+    }
+    const f32x4 l4 = *(const f32x4*)(l2s + 16 * h + 4 * G);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float p = fast_exp2(fmaf(sacc[j], scale_log2, -l4[j]));
+      p = i16 < prefix ? p : 0.0f;   // key i16 (rows past the fold see only k < p)
+      pq[h][j] = p;
+      dq4[h][j] = p * dacc[j];
+    }
+  }
+  const bf16x8 pa = to_bf16x8(pq[0][0], pq[0][1], pq[0][2], pq[0][3], pq[1][0], pq[1][1], pq[1][2],
+                              pq[1][3]);
+  const bf16x8 sa = to_bf16x8(dq4[0][0], dq4[0][1], dq4[0][2], dq4[0][3], dq4[1][0], dq4[1][1],
+                              dq4[1][2], dq4[1][3]);
+  // B: rows 4G..4G+3 then 16+4G..16+4G+3 of column 16 nb + i16: lane L of the
+  // 16-lane group points at row r0 + L/4, column c0 + 4 (L%4)
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    bf16x4 lo[2], hi[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int rr = 16 * half + 4 * G + (i16 >> 2);
+      const int cc = 16 * nb + 4 * (i16 & 3);
+      const uint32_t off = (uint32_t)(2 * tile_off(rr, cc));
+      lo[half] = lds_read_tr4_at(dtile + off);
+      hi[half] = lds_read_tr4_at(qtile + off);
+    }
+    dv[nb] = mfma16(pa, cat8(lo[0], lo[1]), dv[nb]);
+    dk[nb] = mfma16(sa, cat8(hi[0], hi[1]), dk[nb]);
+  }
+}
+
+__device__ __forceinline__ void prefix_fold(const DqArgs& a, DqWinSmem& sm, const SeqView& sv,
+                                            int kvh, size_t slot, int q_start, int wave,
+                                            int lane) {
+  static_assert(FOLD_STAT_OFF + WAVES * 2 * 2 * 32 * (int)sizeof(float) <= (int)sizeof(DqWinSmem),
+                "the fold's tiles and row statistics fit in the window kernel's LDS");
+  static_assert(WAVES * 2 * FOLD_KEYS * D * (int)sizeof(float) <= FOLD_STAT_OFF,
+                "the waves' sums fit in their tile areas");
+  const int np = a.prefix;   // 1 .. FOLD_KEYS
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int G = lane >> 4, i16 = lane & 15;
+  // B operands of S and dP: K and V rows of keys 0..15 (column i16), head dim
+  // 32 ks + 8G .. +7
+  bf16x8 kb16[2], vb16[2];
+  {
+    const uint32_t kt = lds_addr(sm.kv[0][0]), vt = lds_addr(sm.kv[0][1]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c8 = 4 * ks + G;
+      const uint32_t off = (uint32_t)(i16 * 128 + ((c8 ^ tile_swz(i16)) << 4));
+      kb16[ks] = lds_read8(kt + off);
+      vb16[ks] = lds_read8(vt + off);
+    }
+  }
+  wait_all_mem();
+  __syncthreads();   // every wave is done with the key tiles and its staging rows
+  f32x4 pdk[4], pdv[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) pdk[nb] = pdv[nb] = f32x4{};
+  char* lds = (char*)&sm;
+  bf16* qt0 = (bf16*)(lds + wave * FOLD_WAVE_BYTES);   // Q, then dO 32 * D after
+  float* st0 = (float*)(lds + FOLD_STAT_OFF) + wave * 2 * 64;   // per head: L[32], -D[32]
+  const int q_row_stride = a.heads_q * D;
+  const TileLane tl = tile_lane(lane, q_row_stride * 2);
+  const int n_valid = sv.len - q_start;
+  for (int hi = wave; hi < a.group; hi += 2 * WAVES) {
+    const int nh = hi + WAVES < a.group ? 2 : 1;
+    for (int j = 0; j < nh; ++j) {
+      const int h = kvh * a.group + hi + j * WAVES;
+      const size_t off = ((size_t)sv.row_base + q_start) * q_row_stride + (size_t)h * D;
+      bf16* qt = qt0 + j * 2 * 32 * D;
+      tile_load_lds_lane<32, 1>(qt, a.q + off, q_row_stride * 2, n_valid, 0, tl);
+      tile_load_lds_lane<32, 1>(qt + 32 * D, a.dout + off, q_row_stride * 2, n_valid, 0, tl);
+    }
+    // lanes 0..31: the first head's rows, 32..63: the second's
+    {
+      const int h = kvh * a.group + hi + g * WAVES;
+      const bool ok = g < nh && q_start + l32 < sv.len;
+      const size_t wi = (size_t)h * a.rows_total + sv.row_base + q_start + l32;
+      const float l2v = ok ? a.l2_ws[wi] : INFINITY;
+      const float ddv = ok ? -a.d_ws[wi] : 0.0f;
+      st0[g * 64 + l32] = l2v;
+      st0[g * 64 + 32 + l32] = ddv;
+    }
+    wait_all_mem();
+    __builtin_amdgcn_wave_barrier();
+    for (int j = 0; j < nh; ++j) {
+      const uint32_t qt = lds_addr(qt0 + j * 2 * 32 * D);
+      fold_step16(qt, qt + 32 * D * 2, st0 + j * 64, st0 + j * 64 + 32, kb16, vb16, pdk, pdv,
+                  np, a.scale_log2, lane);
+    }
+    wait_all_mem();   // the tiles' reads are done before the next round's copies
+    __builtin_amdgcn_wave_barrier();
+  }
+  // each wave's sums of keys < p into its own tile area ([dK | dV][key][d]),
+  // then all threads add the four in wave order.  C layout: key 4G + j,
+  // head dim 16 nb + i16.
+  float* mine = (float*)qt0;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = 4 * G + j;
+      if (key < np) {
+        mine[key * D + 16 * nb + i16] = pdk[nb][j];
+        mine[(np + key) * D + 16 * nb + i16] = pdv[nb][j];
+      }
+    }
+  __syncthreads();
+  float* out = a.fold_part + ((size_t)kvh * a.ds_stride + slot) * (2 * np * D);
+  for (int i = threadIdx.x; i < 2 * np * D; i += WAVES * 64) {
+    float t = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) t += ((const float*)(lds + w * FOLD_WAVE_BYTES))[i];
+    out[i] = t;
+  }
+}
+
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
   __shared__ DqWinSmem sm;
@@ -611,6 +793,88 @@ void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
       *(float4*)(a.dv_acc + e) = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
+  if (a.fold && q_start >= a.fold_row) prefix_fold(a, sm, sv, kvh, ds_slot, q_start, wave, lane);
+}
+
+// Finish phase of the prefix fold: for sequence z (grid x), kv head (grid y)
+// and 64 of the 2 p D values of the prefix keys' dK and dV (grid z, lane =
+// value), add the parts the window dQ kernel's blocks past the fold row wrote
+// to their slots into the fp32 dK/dV accumulators.  The slots of a sequence
+// are consecutive (z * num_q_tiles .. for fixed length, the sequence's run of
+// the packed tile index) and run from its last 32-row block down, so its
+// blocks past the fold row are its first slots.  Wave w adds slots w, w + 16,
+// ... in order, then the 16 wave sums are added in wave order.
+constexpr int FOLD_ADD_WAVES = 16;
+__global__ __launch_bounds__(FOLD_ADD_WAVES * 64) void sinkattn_prefix_fold_add(
+    const float* fold_part, float* dk_acc, float* dv_acc, const int* cu_seqlens, int seqlen,
+    int heads_kv, int prefix, int ds_stride, int num_q_tiles, int fold_tiles) {
+  const int z = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  __shared__ int s_first;
+  __shared__ float red[FOLD_ADD_WAVES][64];
+  int first, count, row_base, len;
+  if (!cu_seqlens) {
+    first = z * num_q_tiles;
+    count = num_q_tiles;
+    row_base = z * seqlen;
+    len = seqlen;
+  } else {
+    // the 32-row tiles of the sequences before z, counted 64 at a time by wave 0
+    if (wave == 0) {
+      int before = 0;
+      for (int z0 = 0; z0 < z; z0 += 64) {
+        const int zz = z0 + lane;
+        const int n = zz < z ? max(cu_seqlens[zz + 1] - cu_seqlens[zz], 0) : 0;
+        int t = (n + 31) / 32;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+        before += t;
+      }
+      if (lane == 0) s_first = before;
+    }
+    __syncthreads();
+    first = s_first;
+    row_base = cu_seqlens[z];
+    len = max(cu_seqlens[z + 1] - row_base, 0);
+    count = (len + 31) / 32;
+  }
+  const int used = count - fold_tiles;   // slots past the fold row
+  if (used <= 0) return;                 // block-uniform
+  const int per = 2 * prefix * D;        // floats per slot
+  const int e = blockIdx.z * 64 + lane;
+  const float* src = fold_part + ((size_t)kvh * ds_stride + first) * per + e;
+  float t = 0.0f;
+  if (e < per) {
+    // eight slots' loads in flight at a time; added in slot order
+    constexpr int U = 8;
+    for (int c0 = wave; c0 < used; c0 += U * FOLD_ADD_WAVES) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * FOLD_ADD_WAVES;
+        v[u] = src[(size_t)min(c, used - 1) * per];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (c0 + u * FOLD_ADD_WAVES < used) t += v[u];
+    }
+  }
+  red[wave][lane] = t;
+  __syncthreads();
+  if (wave == 0 && e < per) {
+    float u = 0.0f;
+#pragma unroll
+    for (int w = 0; w < FOLD_ADD_WAVES; ++w) u += red[w][lane];
+    const int part = e / (prefix * D);           // 0: dK, 1: dV
+    const int rem = e - part * prefix * D;       // key * D + d
+    const int key = rem / D, d = rem - key * D;
+    if (key < len) {
+      float* dst = (part == 0 ? dk_acc : dv_acc) + ((size_t)(row_base + key) * heads_kv + kvh) * D + d;
+      *dst += u;
+    }
+  }
 }
 
 }  // namespace
@@ -630,6 +894,13 @@ bool dq_window_kernel(int seqlen, int group, int window, int prefix) {
   return pre + win <= WIN_TILES;
 }
 
+// Whether the window dQ kernel takes the prefix keys' dK/dV part of the rows
+// past the fold row (see prefix_fold): it runs, and every prefix key lies in
+// its first resident tile.
+bool dq_prefix_fold(int seqlen, int group, int window, int prefix) {
+  return dq_window_kernel(seqlen, group, window, prefix) && prefix > 0 && prefix <= FOLD_KEYS;
+}
+
 // Rows per query tile of the dQ kernel the launcher picks.
 static int dq_query_tile(int seqlen, int group, int window, int prefix) {
   if (dq_window_kernel(seqlen, group, window, prefix)) return 32;
@@ -640,6 +911,22 @@ static int dq_query_tile(int seqlen, int group, int window, int prefix) {
 // of per-workgroup sink-gradient slots per head it writes: sequences x query
 // tiles (fixed length), or the packed tiles' bound (varlen).  At most
 // batch * ceil(seqlen / 32), the workspace's slots per head.
+hipError_t launch_prefix_fold_add(const float* fold_part, float* dk_acc, float* dv_acc,
+                                  const int* cu_seqlens, int batch, int seqlen, int heads_kv,
+                                  int prefix, int ds_stride, long long fold_row,
+                                  hipStream_t stream) {
+  if (batch == 0 || seqlen == 0) return hipSuccess;
+  if (prefix <= 0 || prefix > 32 || fold_row % 32 != 0) return hipErrorInvalidValue;
+  const int chunks = (2 * prefix * D + 63) / 64;
+  const long long fold_tiles = fold_row / 32;
+  const int num_q_tiles = (seqlen + 31) / 32;
+  if (fold_tiles >= num_q_tiles) return hipSuccess;   // no row past the fold row
+  hipLaunchKernelGGL(sinkattn_prefix_fold_add, dim3(batch, heads_kv, chunks),
+                     dim3(FOLD_ADD_WAVES * 64), 0, stream, fold_part, dk_acc, dv_acc, cu_seqlens,
+                     seqlen, heads_kv, prefix, ds_stride, num_q_tiles, (int)fold_tiles);
+  return hipGetLastError();
+}
+
 int dq_launch_tiles(int batch, int seqlen, int total_tokens, bool varlen, int group, int window,
                     int prefix) {
   const int bq = dq_query_tile(seqlen, group, window, prefix);
@@ -652,7 +939,8 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
                                   float* ds_part, int ds_stride, float* l_ws, float* d_ws, float* dk_acc,
                                   float* dv_acc, bf16* dq, const int* cu_seqlens, int batch,
                                   int seqlen, int rows_total, int heads_q, int heads_kv, int window,
-                                  int prefix, float scale, hipStream_t stream) {
+                                  int prefix, float scale, long long fold_row, float* fold_part,
+                                  hipStream_t stream) {
   DqArgs a;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.o = o; a.lse = lse; a.sinks = sinks;
   a.ds_part = ds_part; a.ds_stride = ds_stride; a.l2_ws = l_ws; a.d_ws = d_ws; a.dk_acc = dk_acc; a.dv_acc = dv_acc;
@@ -665,7 +953,11 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
   const bool k32 = fwd_key_tile(window) == 32;
   a.scale_log2 = scale * SA_LOG2E;
   a.scale = scale;
+  a.fold = fold_part != nullptr;
+  a.fold_row = fold_row;
+  a.fold_part = fold_part;
   if (seqlen == 0 || batch == 0) return hipSuccess;
+  if (a.fold && !dq_prefix_fold(seqlen, a.group, window, prefix)) return hipErrorInvalidValue;
   const int BQ = dq_query_tile(seqlen, a.group, window, prefix);
   a.num_q_tiles = (seqlen + BQ - 1) / BQ;
   // packed sequences: one linear index over every sequence's tiles

@@ -87,17 +87,42 @@ SA_HD bool sa_query_range(int k0, int k1, int n, int w, int p, int* qlo, int* qh
   return *qlo <= *qhi;
 }
 
+// The prefix fold.  When it is on (prefix keys all in the first 32-key tile,
+// resident-tile window dQ kernel), the rows of a key block holding prefix
+// keys that lie past the first query tile boundary after the block's
+// window, i.e. rows >= sa_prefix_fold_row(kb, w, bkw, bq), see only the
+// block's prefix keys; the window dQ kernel adds their part of the prefix
+// keys' dK and dV (it holds those rows and the prefix tile anyway), and the
+// dK/dV kernel's work for the block stops before them.
+SA_HD long long sa_prefix_fold_row(int kb, int w, int bkw, int bq) {
+  const long long last = (long long)kb * bkw + bkw - 1 + (long long)w;   // last row of the window
+  return (last / bq + 1) * bq;
+}
+
+// Query rows [lo, hi] of the dK/dV kernel's work for key block kb of a
+// sequence of n tokens (false if none): the rows that see it, cut at the fold
+// row for blocks holding prefix keys when the fold is on.
+SA_HD bool sa_dkdv_query_range(int kb, int n, int w, int p, int bq, int bkw, bool fold, int* lo,
+                               int* hi) {
+  const int k0 = kb * bkw;
+  if (!sa_query_range(k0, sa_min(k0 + bkw - 1, n - 1), n, w, p, lo, hi)) return false;
+  if (fold && k0 < p) {
+    const long long cut = sa_prefix_fold_row(kb, w, bkw, bq) - 1;
+    if (cut < *hi) *hi = (int)cut;
+  }
+  return true;
+}
+
 // Work units of the dK/dV backward: key block kb (keys [kb*bkw, kb*bkw+bkw))
 // of a sequence of n tokens is paired with every (query tile of bq rows,
-// query head of the group) that can see it; those iterations are cut into
+// query head of the group) in its query range; those iterations are cut into
 // chunks of 2^chunk_shift.  Returns the number of chunks (0 if no row sees
 // the block).  Host and kernel use this same count to size and walk the flat
 // work list.
 SA_HD int sa_dkdv_block_chunks(int kb, int n, int w, int p, int group, int bq, int bkw,
-                               int chunk_shift) {
-  const int k0 = kb * bkw;
+                               int chunk_shift, bool fold) {
   int lo, hi;
-  if (!sa_query_range(k0, sa_min(k0 + bkw - 1, n - 1), n, w, p, &lo, &hi)) return 0;
+  if (!sa_dkdv_query_range(kb, n, w, p, bq, bkw, fold, &lo, &hi)) return 0;
   const int n_iter = (hi / bq - lo / bq + 1) * group;
   return (n_iter + (1 << chunk_shift) - 1) >> chunk_shift;
 }
