@@ -60,6 +60,7 @@ struct DkvArgs {
   int chunk_shift;        // iterations per work unit: 2^chunk_shift
   int fold;               // 1: the window dQ kernel adds the prefix keys' part of rows past
                           // the fold row (sa_dkdv_query_range stops the blocks there)
+  int heads_outer;        // iteration order: query heads outermost (short windows)
   float scale_log2;
 };
 
@@ -129,6 +130,16 @@ __device__ __forceinline__ void tile_step(uint32_t qtile, const float* l2s,
   for (int qb = 0; qb < BQ / 32; ++qb) {
     // this lane's C rows are queries qb*32 + 8*(i/4) + 4g + i%4, its column
     // is key k: q - k = base + 8*(i/4) + i%4
+    if constexpr (MASK) {
+      // a 32-row block that sees none of this wave's keys (the far side of
+      // the diagonal or of the window edge) is skipped
+      const int ku = __builtin_amdgcn_readfirstlane(kw0);
+      const int qu = __builtin_amdgcn_readfirstlane(q0 + qb * 32);
+      if (sa_tile_class(qu, qu + 31, ku, ku + 31, window, prefix) == SA_TILE_SKIP) {
+        if (qb + 1 < BQ / 32) read_rows(qb + 1);
+        continue;
+      }
+    }
     const int base = sa_opaque(q0 + qb * 32 + 4 * g - k);
     __builtin_amdgcn_sched_barrier(0);
     // L and -D of the block's rows first: LDS reads complete in issue order, so
@@ -321,9 +332,15 @@ __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
   // in step and their Q/dO tiles stay in the XCD's L2.
   const int qt_last = qt_begin + n_qt - 1;
   auto tile_of = [&](int it, int* h, int* q0) {
-    const int ti = it / a.group;
-    *h = h_begin + (it - ti * a.group);
-    *q0 = (qt_last - ti) * BQ;
+    if (a.heads_outer) {
+      const int hi = it / n_qt;
+      *h = h_begin + hi;
+      *q0 = (qt_last - (it - hi * n_qt)) * BQ;
+    } else {
+      const int ti = it / a.group;
+      *h = h_begin + (it - ti * a.group);
+      *q0 = (qt_last - ti) * BQ;
+    }
   };
   const TileLane tl = tile_lane(lane, q_row_stride * 2);
   auto load_tile = [&](int it, int buf) {
@@ -452,6 +469,7 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
   const int nkb = (seqlen + BKW - 1) / BKW;
   if (nkb == 0 || batch == 0) return hipSuccess;
   const int BQ = dkdv_query_tile(window);
+  a.heads_outer = window <= 2 * BQ ? 1 : 0;
   // iterations of one sequence of seqlen tokens (for a packed batch seqlen is
   // the longest length, so this bounds every sequence)
   long long iters = 0;
