@@ -146,7 +146,8 @@ sinkattn_status sinkattn_bwd(const sinkattn_problem *problem, const void *q,
  *            (except clearing dsinks for an empty problem);
  *   DQ:      dQ, written to dq (bf16: also the row statistics, each
  *            workgroup's part of dsinks into the workspace, clearing the
- *            fp32 dK/dV workspace accumulators, and, for short windows with
+ *            fp32 dK/dV workspace accumulators where DKDV adds into them
+ *            rather than storing whole rows, and, for short windows with
  *            0 < prefix <= 16, the prefix keys' part of dK, dV from the rows
  *            past the first key block's window, per workgroup into the
  *            workspace);

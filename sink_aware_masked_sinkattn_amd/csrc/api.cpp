@@ -28,7 +28,9 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
                                   float* dv_acc, bf16* dq, const int* cu_seqlens, int batch,
                                   int seqlen, int rows_total, int heads_q, int heads_kv, int window,
                                   int prefix, float scale, long long fold_row, float* fold_part,
-                                  hipStream_t stream);
+                                  bool clear_acc, hipStream_t stream);
+bool dkdv_accumulates(int batch, int seqlen, int heads_q, int heads_kv, int window, int prefix,
+                      bool fold);
 bool dq_prefix_fold(int seqlen, int group, int window, int prefix);
 hipError_t launch_prefix_fold_add(const float* fold_part, float* dk_acc, float* dv_acc,
                                   const int* cu_seqlens, int batch, int seqlen, int heads_kv,
@@ -307,7 +309,10 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
                                (const bf16*)o, lse, sinks, ds_part, wl.ds_stride, l_ws, d_ws, dk_acc, dv_acc,
                                (bf16*)dq, pb->cu_seqlens, pb->batch, pb->seqlen, rows,
                                pb->heads_q, pb->heads_kv, window, prefix, pb->softmax_scale,
-                               dkdv_prefix_fold_row(window), fold_part, s);
+                               dkdv_prefix_fold_row(window), fold_part,
+                               dkdv_accumulates(pb->batch, pb->seqlen, pb->heads_q, pb->heads_kv,
+                                                window, prefix, wl.fold),
+                               s);
     if (e != hipSuccess) return hip_status(e);
   }
   if (is_f32 && (phases & (SINKATTN_BWD_DKDV | SINKATTN_BWD_DQ))) {

@@ -451,6 +451,37 @@ int bwd_dkdv_chunk_shift(long long total_iters) {
   return sh;
 }
 
+// Iterations per work unit for a launch: from the total over every block of
+// every sequence at the longest length.  *max_chunks: the most units any key
+// block is cut into (a bound for every packed sequence too: a shorter
+// sequence's block sees no more query tiles).
+static int dkdv_plan(int batch, int seqlen, int group, int heads_kv, int window, int prefix,
+                     bool fold, int* max_chunks) {
+  const int nkb = (seqlen + BKW - 1) / BKW;
+  const int BQ = dkdv_query_tile(window);
+  long long iters = 0;
+  for (int kb = 0; kb < nkb; ++kb)
+    iters += (long long)sa_dkdv_block_chunks(kb, seqlen, window, prefix, group, BQ, BKW, 0, fold);
+  const int shift = bwd_dkdv_chunk_shift(iters * batch * heads_kv);
+  int mc = 0;
+  for (int kb = 0; kb < nkb; ++kb)
+    mc = max(mc, sa_dkdv_block_chunks(kb, seqlen, window, prefix, group, BQ, BKW, shift, fold));
+  *max_chunks = mc;
+  return shift;
+}
+
+// Whether the dK/dV launch for this problem adds into its fp32 accumulators
+// (some key block is cut into several work units, whose parts are added with
+// atomics) and so needs them cleared first; with one unit per block every
+// key's row is stored whole.
+bool dkdv_accumulates(int batch, int seqlen, int heads_q, int heads_kv, int window, int prefix,
+                      bool fold) {
+  if (seqlen == 0 || batch == 0 || heads_kv == 0) return false;
+  int mc;
+  dkdv_plan(batch, seqlen, heads_q / heads_kv, heads_kv, window, prefix, fold, &mc);
+  return mc > 1;
+}
+
 hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                     const bf16* dout, const float* l_ws, const float* d_ws,
                                     float* dk_acc, float* dv_acc, const int* cu_seqlens,
@@ -470,12 +501,8 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
   if (nkb == 0 || batch == 0) return hipSuccess;
   const int BQ = dkdv_query_tile(window);
   a.heads_outer = window <= 2 * BQ ? 1 : 0;
-  // iterations of one sequence of seqlen tokens (for a packed batch seqlen is
-  // the longest length, so this bounds every sequence)
-  long long iters = 0;
-  for (int kb = 0; kb < nkb; ++kb)
-    iters += (long long)sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW, 0, fold);
-  a.chunk_shift = bwd_dkdv_chunk_shift(iters * batch * heads_kv);
+  int max_chunks;   // > 1: the dQ kernel cleared the accumulators these units add into
+  a.chunk_shift = dkdv_plan(batch, seqlen, a.group, heads_kv, window, prefix, fold, &max_chunks);
   long long units = 0;
   for (int kb = 0; kb < nkb; ++kb)
     units += sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW, a.chunk_shift,

@@ -65,8 +65,9 @@ struct DqArgs {
   int ds_stride;
   float* l2_ws;           // [Hq, rows] L in log2 units (L * log2 e), written here
   float* d_ws;            // [Hq, rows] D, written here
-  float* dk_acc;          // [rows, Hkv, D] fp32 dK / dV accumulators, zeroed here
-  float* dv_acc;
+  float* dk_acc;          // [rows, Hkv, D] fp32 dK / dV accumulators, zeroed here when
+  float* dv_acc;          // clear_acc (the dK/dV kernel adds into them)
+  int clear_acc;          // 0: the dK/dV kernel stores every key's row (one work unit per block)
   bf16* dq;
   const int* cu_seqlens;
   int batch, seqlen, heads_q, heads_kv, group, window, prefix, rows_total;
@@ -425,7 +426,7 @@ __device__ __forceinline__ void dq_body(const DqArgs& a) {
   // Zero this workgroup's share of the fp32 dK / dV accumulators (the dK/dV
   // kernel adds into them): rows of the tile congruent to h mod group, so the
   // group's query heads split the kv head's rows between them.
-  {
+  if (a.clear_acc) {
     const int part = h - kvh * a.group;
     const int n_mine = (q_last - q_start + a.group - part) / a.group;   // rows part, part+group, ...
     for (int i = tid; i < n_mine * (D / 4); i += WAVES * 64) {
@@ -784,7 +785,7 @@ void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
   }
   // clear the fp32 dK / dV accumulators of the block's rows for this kv head
   // (the dK/dV kernel adds into them)
-  {
+  if (a.clear_acc) {
     const int nrows = q_last - q_start + 1;
     for (int i = tid; i < nrows * (D / 4); i += WAVES * 64) {
       const int r = q_start + i / (D / 4);
@@ -940,7 +941,7 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
                                   float* dv_acc, bf16* dq, const int* cu_seqlens, int batch,
                                   int seqlen, int rows_total, int heads_q, int heads_kv, int window,
                                   int prefix, float scale, long long fold_row, float* fold_part,
-                                  hipStream_t stream) {
+                                  bool clear_acc, hipStream_t stream) {
   DqArgs a;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.o = o; a.lse = lse; a.sinks = sinks;
   a.ds_part = ds_part; a.ds_stride = ds_stride; a.l2_ws = l_ws; a.d_ws = d_ws; a.dk_acc = dk_acc; a.dv_acc = dv_acc;
@@ -956,6 +957,7 @@ hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, c
   a.fold = fold_part != nullptr;
   a.fold_row = fold_row;
   a.fold_part = fold_part;
+  a.clear_acc = clear_acc ? 1 : 0;
   if (seqlen == 0 || batch == 0) return hipSuccess;
   if (a.fold && !dq_prefix_fold(seqlen, a.group, window, prefix)) return hipErrorInvalidValue;
   const int BQ = dq_query_tile(seqlen, a.group, window, prefix);
