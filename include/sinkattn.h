@@ -151,12 +151,16 @@ sinkattn_status sinkattn_bwd(const sinkattn_problem *problem, const void *q,
  *            0 < prefix <= 16, the prefix keys' part of dK, dV from the rows
  *            past the first key block's window, per workgroup into the
  *            workspace);
- *   DKDV:    dK, dV from the recomputed probabilities exp(S - L) (bf16: into
- *            the fp32 workspace accumulators; fp32: into dk, dv);
+ *   DKDV:    dK, dV from the recomputed probabilities exp(S - L) (bf16:
+ *            into the fp32 workspace accumulators where a key block is
+ *            split over several work units, else straight into dk, dv --
+ *            with the prefix fold, the prefix keys' rows into the
+ *            accumulators; fp32: into dk, dv);
  *   FINISH:  bf16: adds DQ's prefix-key parts into the dK/dV accumulators,
- *            scales and converts them into dk, dv, and writes dsinks as the
- *            sum of DQ's parts; every sum is taken in a fixed order (so dk,
- *            dv and dsinks are the same on every call); fp32: nothing.
+ *            scales and converts what DKDV left there into dk, dv, and
+ *            writes dsinks as the sum of DQ's parts; every sum is taken in a
+ *            fixed order (so dk, dv and dsinks are the same on every call);
+ *            fp32: nothing.
  * sinkattn_bwd(...) == sinkattn_bwd_phases(SINKATTN_BWD_ALL, ...).
  */
 enum {

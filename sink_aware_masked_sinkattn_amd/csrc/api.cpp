@@ -21,7 +21,7 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                     float* dk_acc, float* dv_acc, const int* cu_seqlens,
                                     int batch, int seqlen, int rows_total, int heads_q,
                                     int heads_kv, int window, int prefix, float scale, bool fold,
-                                    hipStream_t stream);
+                                    bf16* dk, bf16* dv, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16_d64(const bf16* q, const bf16* k, const bf16* v, const bf16* dout,
                                   const bf16* o, const float* lse, const float* sinks,
                                   float* ds_part, int ds_stride, float* l_ws, float* d_ws, float* dk_acc,
@@ -33,9 +33,9 @@ bool dkdv_accumulates(int batch, int seqlen, int heads_q, int heads_kv, int wind
                       bool fold);
 bool dq_prefix_fold(int seqlen, int group, int window, int prefix);
 hipError_t launch_prefix_fold_add(const float* fold_part, float* dk_acc, float* dv_acc,
-                                  const int* cu_seqlens, int batch, int seqlen, int heads_kv,
-                                  int prefix, int ds_stride, long long fold_row,
-                                  hipStream_t stream);
+                                  bf16* dk, bf16* dv, float scale, const int* cu_seqlens,
+                                  int batch, int seqlen, int heads_kv, int prefix, int ds_stride,
+                                  long long fold_row, hipStream_t stream);
 long long dkdv_prefix_fold_row(int window);
 int dq_launch_tiles(int batch, int seqlen, int total_tokens, bool varlen, int group, int window,
                     int prefix);
@@ -293,6 +293,10 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
   const int window = clamped_window(pb);
   const int prefix = clamped_prefix(pb);
   float* fold_part = wl.fold ? (float*)(ws + wl.fold_off) : nullptr;
+  // bf16: whether the dK/dV kernel adds into its accumulators (cleared by the
+  // dQ kernel, converted by the finish pass) or writes dk, dv itself
+  const bool dkdv_acc = !is_f32 && dkdv_accumulates(pb->batch, pb->seqlen, pb->heads_q,
+                                                    pb->heads_kv, window, prefix, wl.fold);
   const int rows = (int)dims.rows;
   const int lse_stride = dims.varlen ? rows : pb->seqlen;
   // fp32: the row pass (D, L, dsinks) is its own kernel; bf16: the dQ kernel
@@ -309,10 +313,7 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
                                (const bf16*)o, lse, sinks, ds_part, wl.ds_stride, l_ws, d_ws, dk_acc, dv_acc,
                                (bf16*)dq, pb->cu_seqlens, pb->batch, pb->seqlen, rows,
                                pb->heads_q, pb->heads_kv, window, prefix, pb->softmax_scale,
-                               dkdv_prefix_fold_row(window), fold_part,
-                               dkdv_accumulates(pb->batch, pb->seqlen, pb->heads_q, pb->heads_kv,
-                                                window, prefix, wl.fold),
-                               s);
+                               dkdv_prefix_fold_row(window), fold_part, dkdv_acc, s);
     if (e != hipSuccess) return hip_status(e);
   }
   if (is_f32 && (phases & (SINKATTN_BWD_DKDV | SINKATTN_BWD_DQ))) {
@@ -328,22 +329,25 @@ static sinkattn_status bwd_phases(unsigned phases, const sinkattn_problem* pb, c
     e = launch_bwd_dkdv_bf16_d64((const bf16*)q, (const bf16*)k, (const bf16*)v,
                                  (const bf16*)dout, l_ws, d_ws, dk_acc, dv_acc, pb->cu_seqlens,
                                  pb->batch, pb->seqlen, rows, pb->heads_q, pb->heads_kv, window,
-                                 prefix, pb->softmax_scale, wl.fold, s);
+                                 prefix, pb->softmax_scale, wl.fold, (bf16*)dk, (bf16*)dv, s);
     if (e != hipSuccess) return hip_status(e);
   }
   if ((phases & SINKATTN_BWD_FINISH) && !is_f32) {
     // the slots the dQ kernel wrote: one per workgroup of a head
     const int ds_used = dq_launch_tiles(pb->batch, pb->seqlen, rows, dims.varlen,
                                         pb->heads_q / pb->heads_kv, window, prefix);
+    // dkdv_acc false: the dK/dV kernel wrote dk, dv itself (the fold's rows
+    // excepted), and only ds_h is left to the convert pass
     if (wl.fold) {
-      e = launch_prefix_fold_add(fold_part, dk_acc, dv_acc, pb->cu_seqlens, pb->batch,
-                                 pb->seqlen, pb->heads_kv, prefix, wl.ds_stride,
-                                 dkdv_prefix_fold_row(window), s);
+      e = launch_prefix_fold_add(fold_part, dk_acc, dv_acc, dkdv_acc ? nullptr : (bf16*)dk,
+                                 dkdv_acc ? nullptr : (bf16*)dv, pb->softmax_scale,
+                                 pb->cu_seqlens, pb->batch, pb->seqlen, pb->heads_kv, prefix,
+                                 wl.ds_stride, dkdv_prefix_fold_row(window), s);
       if (e != hipSuccess) return hip_status(e);
     }
     e = launch_convert(dk_acc, dv_acc, (bf16*)dk, (bf16*)dv,
-                       (long long)rows * pb->heads_kv * pb->head_dim, pb->softmax_scale, ds_part,
-                       ds_used, wl.ds_stride, pb->heads_q, dsinks, s);
+                       dkdv_acc ? (long long)rows * pb->heads_kv * pb->head_dim : 0,
+                       pb->softmax_scale, ds_part, ds_used, wl.ds_stride, pb->heads_q, dsinks, s);
   }
   return hip_status(e);
 }

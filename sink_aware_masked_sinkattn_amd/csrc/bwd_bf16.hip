@@ -54,6 +54,12 @@ struct DkvArgs {
   const float* d_ws;      // [Hq, rows] D
   float* dk_acc;          // [rows, Hkv, D] sum dS^T Q (unscaled)
   float* dv_acc;          // [rows, Hkv, D] sum P'^T dO
+  bf16* dk_out;           // [rows, Hkv, D] dK, dV: written here when direct
+  bf16* dv_out;
+  int direct;             // 1: every key block is one work unit, so each key's row is final
+                          // here and goes out as bf16 (dK scaled) -- except, with the fold,
+                          // the prefix keys' rows, which go to the accumulators
+  float scale;
   const int* cu_seqlens;
   int seqlen, heads_q, heads_kv, group, window, prefix, rows_total;
   int batch;
@@ -400,7 +406,31 @@ __device__ __forceinline__ void dkdv_body(const DkvArgs& a) {
 #pragma unroll
     for (int db = 0; db < 2; ++db) asm volatile("" : "+v"(dk_acc[kb][db]), "+v"(dv_acc[kb][db]));
   // ---- C rows are keys kw0 + kb*32 + 8*(i/4) + 4g + i%4, column d = db*32 + l32
-  if (wave_active) {
+  if (wave_active && a.direct) {
+    // every unit covers its whole block: the rows are final (but for the
+    // prefix keys the fold completes)
+    const int acc_below = a.fold ? a.prefix : 0;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const size_t e0 = ((size_t)sv.row_base * a.heads_kv + kvh) * D + db * 32 + l32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kw0 + kb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+          const size_t e = e0 + (size_t)key * kv_row_stride;
+          if (key < sv.len) {
+            if (key < acc_below) {
+              a.dk_acc[e] = dk_acc[kb][db][i];
+              a.dv_acc[e] = dv_acc[kb][db][i];
+            } else {
+              a.dk_out[e] = (bf16)(dk_acc[kb][db][i] * a.scale);
+              a.dv_out[e] = (bf16)dv_acc[kb][db][i];
+            }
+          }
+        }
+      }
+  } else if (wave_active) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -472,8 +502,9 @@ static int dkdv_plan(int batch, int seqlen, int group, int heads_kv, int window,
 
 // Whether the dK/dV launch for this problem adds into its fp32 accumulators
 // (some key block is cut into several work units, whose parts are added with
-// atomics) and so needs them cleared first; with one unit per block every
-// key's row is stored whole.
+// atomics) and so needs them cleared first and converted after; with one
+// unit per block every key's row is final in the kernel and goes out as bf16
+// directly (with the prefix fold, the prefix keys' rows excepted).
 bool dkdv_accumulates(int batch, int seqlen, int heads_q, int heads_kv, int window, int prefix,
                       bool fold) {
   if (seqlen == 0 || batch == 0 || heads_kv == 0) return false;
@@ -487,7 +518,7 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
                                     float* dk_acc, float* dv_acc, const int* cu_seqlens,
                                     int batch, int seqlen, int rows_total, int heads_q,
                                     int heads_kv, int window, int prefix, float scale, bool fold,
-                                    hipStream_t stream) {
+                                    bf16* dk, bf16* dv, hipStream_t stream) {
   DkvArgs a;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.l2_ws = l_ws; a.d_ws = d_ws;
   a.dk_acc = dk_acc; a.dv_acc = dv_acc; a.cu_seqlens = cu_seqlens;
@@ -503,6 +534,9 @@ hipError_t launch_bwd_dkdv_bf16_d64(const bf16* q, const bf16* k, const bf16* v,
   a.heads_outer = window <= 2 * BQ ? 1 : 0;
   int max_chunks;   // > 1: the dQ kernel cleared the accumulators these units add into
   a.chunk_shift = dkdv_plan(batch, seqlen, a.group, heads_kv, window, prefix, fold, &max_chunks);
+  a.direct = max_chunks <= 1 ? 1 : 0;
+  a.dk_out = dk; a.dv_out = dv;
+  a.scale = scale;
   long long units = 0;
   for (int kb = 0; kb < nkb; ++kb)
     units += sa_dkdv_block_chunks(kb, seqlen, window, prefix, a.group, BQ, BKW, a.chunk_shift,

@@ -797,87 +797,6 @@ void sinkattn_bwd_dq_bf16_d64_win(DqArgs a) {
   if (a.fold && q_start >= a.fold_row) prefix_fold(a, sm, sv, kvh, ds_slot, q_start, wave, lane);
 }
 
-// Finish phase of the prefix fold: for sequence z (grid x), kv head (grid y)
-// and 64 of the 2 p D values of the prefix keys' dK and dV (grid z, lane =
-// value), add the parts the window dQ kernel's blocks past the fold row wrote
-// to their slots into the fp32 dK/dV accumulators.  The slots of a sequence
-// are consecutive (z * num_q_tiles .. for fixed length, the sequence's run of
-// the packed tile index) and run from its last 32-row block down, so its
-// blocks past the fold row are its first slots.  Wave w adds slots w, w + 16,
-// ... in order, then the 16 wave sums are added in wave order.
-constexpr int FOLD_ADD_WAVES = 16;
-__global__ __launch_bounds__(FOLD_ADD_WAVES * 64) void sinkattn_prefix_fold_add(
-    const float* fold_part, float* dk_acc, float* dv_acc, const int* cu_seqlens, int seqlen,
-    int heads_kv, int prefix, int ds_stride, int num_q_tiles, int fold_tiles) {
-  const int z = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  __shared__ int s_first;
-  __shared__ float red[FOLD_ADD_WAVES][64];
-  int first, count, row_base, len;
-  if (!cu_seqlens) {
-    first = z * num_q_tiles;
-    count = num_q_tiles;
-    row_base = z * seqlen;
-    len = seqlen;
-  } else {
-    // the 32-row tiles of the sequences before z, counted 64 at a time by wave 0
-    if (wave == 0) {
-      int before = 0;
-      for (int z0 = 0; z0 < z; z0 += 64) {
-        const int zz = z0 + lane;
-        const int n = zz < z ? max(cu_seqlens[zz + 1] - cu_seqlens[zz], 0) : 0;
-        int t = (n + 31) / 32;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
-        before += t;
-      }
-      if (lane == 0) s_first = before;
-    }
-    __syncthreads();
-    first = s_first;
-    row_base = cu_seqlens[z];
-    len = max(cu_seqlens[z + 1] - row_base, 0);
-    count = (len + 31) / 32;
-  }
-  const int used = count - fold_tiles;   // slots past the fold row
-  if (used <= 0) return;                 // block-uniform
-  const int per = 2 * prefix * D;        // floats per slot
-  const int e = blockIdx.z * 64 + lane;
-  const float* src = fold_part + ((size_t)kvh * ds_stride + first) * per + e;
-  float t = 0.0f;
-  if (e < per) {
-    // eight slots' loads in flight at a time; added in slot order
-    constexpr int U = 8;
-    for (int c0 = wave; c0 < used; c0 += U * FOLD_ADD_WAVES) {
-      float v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = c0 + u * FOLD_ADD_WAVES;
-        v[u] = src[(size_t)min(c, used - 1) * per];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (c0 + u * FOLD_ADD_WAVES < used) t += v[u];
-    }
-  }
-  red[wave][lane] = t;
-  __syncthreads();
-  if (wave == 0 && e < per) {
-    float u = 0.0f;
-#pragma unroll
-    for (int w = 0; w < FOLD_ADD_WAVES; ++w) u += red[w][lane];
-    const int part = e / (prefix * D);           // 0: dK, 1: dV
-    const int rem = e - part * prefix * D;       // key * D + d
-    const int key = rem / D, d = rem - key * D;
-    if (key < len) {
-      float* dst = (part == 0 ? dk_acc : dv_acc) + ((size_t)(row_base + key) * heads_kv + kvh) * D + d;
-      *dst += u;
-    }
-  }
-}
-
 }  // namespace
 
 int fwd_key_tile(int window);
@@ -912,22 +831,6 @@ static int dq_query_tile(int seqlen, int group, int window, int prefix) {
 // of per-workgroup sink-gradient slots per head it writes: sequences x query
 // tiles (fixed length), or the packed tiles' bound (varlen).  At most
 // batch * ceil(seqlen / 32), the workspace's slots per head.
-hipError_t launch_prefix_fold_add(const float* fold_part, float* dk_acc, float* dv_acc,
-                                  const int* cu_seqlens, int batch, int seqlen, int heads_kv,
-                                  int prefix, int ds_stride, long long fold_row,
-                                  hipStream_t stream) {
-  if (batch == 0 || seqlen == 0) return hipSuccess;
-  if (prefix <= 0 || prefix > 32 || fold_row % 32 != 0) return hipErrorInvalidValue;
-  const int chunks = (2 * prefix * D + 63) / 64;
-  const long long fold_tiles = fold_row / 32;
-  const int num_q_tiles = (seqlen + 31) / 32;
-  if (fold_tiles >= num_q_tiles) return hipSuccess;   // no row past the fold row
-  hipLaunchKernelGGL(sinkattn_prefix_fold_add, dim3(batch, heads_kv, chunks),
-                     dim3(FOLD_ADD_WAVES * 64), 0, stream, fold_part, dk_acc, dv_acc, cu_seqlens,
-                     seqlen, heads_kv, prefix, ds_stride, num_q_tiles, (int)fold_tiles);
-  return hipGetLastError();
-}
-
 int dq_launch_tiles(int batch, int seqlen, int total_tokens, bool varlen, int group, int window,
                     int prefix) {
   const int bq = dq_query_tile(seqlen, group, window, prefix);
