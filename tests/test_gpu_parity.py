@@ -39,6 +39,10 @@ SMALL = [
     (1, 640, 8, 1, 100, 4, 0.5),
     (2, 700, 16, 2, 64, 16, 0.5),
     (1, 900, 8, 2, 40, 32, 0.5),
+    # the prefix fold with key blocks split over two dK/dV work units (GQA
+    # group of 16: the accumulating path), and p just past the fold's limit
+    (1, 700, 16, 1, 128, 8, 0.5),
+    (1, 600, 8, 2, 128, 17, 0.5),
     # windows >= 1024 after clamping run the wide-tile kernels (64-key forward /
     # dQ tiles, 128-row dK/dV tiles); shorter ones the narrow-tile kernels
     (1, 1100, 4, 2, WINDOW_INF, 0, 0.5),
@@ -71,6 +75,8 @@ def test_bf16_small(case):
     ((5, 0, 129, 1, 300, 64, 700, 33, 128, 2), 30, 200),
     ((1000, 999, 1, 0, 640), 128, 16),
     ((257,) * 12, 64, 130),
+    # the prefix fold with sequences shorter than the prefix and than the fold row
+    ((1, 5, 15, 16, 17, 0, 300, 40), 128, 16),
 ])
 def test_bf16_varlen_small(lengths, w, p):
     inp = make_inputs(batch=0, seqlen=0, heads_q=8, heads_kv=2, head_dim=64, window=w, prefix=p,
@@ -455,11 +461,14 @@ def test_bwd_phases_equal_single_call(dtype, d):
 def test_repeat_calls_bitwise_equal(case):
     # o, lse, dq and the sink gradient involve no atomics: the sink gradient
     # is added from per-workgroup parts in a fixed order, so two calls on the
-    # same inputs agree bit for bit (dK/dV of key blocks split over several
-    # work units are added with float atomics and may differ in the last bit)
+    # same inputs agree bit for bit.  dK/dV of key blocks split over several
+    # work units are added with float atomics and may differ in the last bit;
+    # in the short-window case every key block is one unit (stored whole, the
+    # prefix fold's parts added in a fixed order), so dK and dV agree too.
     b, t, hq, hkv, w, p = case
     inp = make_inputs(batch=b, seqlen=t, heads_q=hq, heads_kv=hkv, head_dim=64, window=w,
                       prefix=p, seed=t + hq, std=0.5, dtype="bf16")
     first, second = run_gpu(inp), run_gpu(inp)
-    for name in ("o", "lse", "dq", "ds"):
+    names = ("o", "lse", "dq", "ds") + (("dk", "dv") if w == 128 else ())
+    for name in names:
         np.testing.assert_array_equal(first[name], second[name], err_msg=f"{case} {name}")
