@@ -175,29 +175,52 @@ __global__ __launch_bounds__(256) void sinkattn_convert(const float* dk_acc, con
 }
 
 // Finish phase of the prefix fold: for sequence z (grid x), kv head (grid y)
-// and 64 of the 2 p D values of the prefix keys' dK and dV (grid z, lane =
-// value), add the parts the window dQ kernel's blocks past the fold row wrote
-// to their slots onto the fp32 accumulators.  The slots of a sequence are
-// consecutive (z * num_q_tiles .. for fixed length, the sequence's run of the
-// packed tile index) and run from its last 32-row block down, so its blocks
-// past the fold row are its first slots.  Wave w adds slots w, w + 16, ...
-// in order (all its loads in flight at once), then the 16 wave sums are
-// added in wave order.  dk_out != nullptr: the dK/dV kernel stored every
-// other row as bf16, and these rows go out here the same way (dK scaled);
-// otherwise the sums are added into the accumulators for the convert pass.
+// and 64 VEC of the 2 p D values of the prefix keys' dK and dV (grid z; lane
+// = VEC consecutive values), add the parts the window dQ kernel's blocks past
+// the fold row wrote to their slots onto the fp32 accumulators.  The slots of
+// a sequence are consecutive (z * num_q_tiles .. for fixed length, the
+// sequence's run of the packed tile index) and run from its last 32-row
+// block down, so its blocks past the fold row are its first slots.  Wave w
+// adds slots w, w + 16, ... in order (all its loads in flight at once), then
+// the 16 wave sums are added in wave order.  dk_out != nullptr: the dK/dV
+// kernel stored every other row as bf16, and these rows go out here the
+// same way (dK scaled); otherwise the sums are added into the accumulators
+// for the convert pass.
 constexpr int FOLD_D = 64;
 constexpr int FOLD_ADD_WAVES = 16;
 constexpr int FOLD_ADD_LOADS = 16;   // slots per wave in flight
+template <int VEC>
+struct FoldVec;
+template <>
+struct FoldVec<1> {
+  typedef float T;
+  static __device__ T zero() { return 0.0f; }
+  static __device__ void add(T& a, const T& b) { a += b; }
+  static __device__ void store_bf16(bf16* p, const T& x, float sc) { *p = (bf16)(x * sc); }
+};
+template <>
+struct FoldVec<4> {
+  typedef float4 T;
+  static __device__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+  static __device__ void add(T& a, const T& b) { a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w; }
+  static __device__ void store_bf16(bf16* p, const T& x, float sc) {
+    *(bf16x4*)p = to_bf16x4(x.x * sc, x.y * sc, x.z * sc, x.w * sc);
+  }
+};
+
+template <int VEC>
 __global__ __launch_bounds__(FOLD_ADD_WAVES * 64) void sinkattn_prefix_fold_add(
     const float* fold_part, float* dk_acc, float* dv_acc, bf16* dk_out, bf16* dv_out,
     float scale, const int* cu_seqlens, int seqlen, int heads_kv, int prefix, int ds_stride,
     int num_q_tiles, int fold_tiles) {
+  using V = FoldVec<VEC>;
+  typedef typename V::T T;
   const int z = blockIdx.x;
   const int kvh = blockIdx.y;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   __shared__ int s_first;
-  __shared__ float red[FOLD_ADD_WAVES][64];
+  __shared__ T red[FOLD_ADD_WAVES][64];
   int first, count, row_base, len;
   if (!cu_seqlens) {
     first = z * num_q_tiles;
@@ -226,42 +249,39 @@ __global__ __launch_bounds__(FOLD_ADD_WAVES * 64) void sinkattn_prefix_fold_add(
   }
   const int used = count - fold_tiles;   // slots past the fold row
   if (used <= 0 && !dk_out) return;      // block-uniform
-  const int per = 2 * prefix * FOLD_D;   // floats per slot
-  const int e = blockIdx.z * 64 + lane;
+  const int per = 2 * prefix * FOLD_D;   // floats per slot (a multiple of 4)
+  const int e = (blockIdx.z * 64 + lane) * VEC;
   const float* src = fold_part + ((size_t)kvh * ds_stride + first) * per + e;
-  float t = 0.0f;
+  T t = V::zero();
   if (e < per) {
     for (int c0 = wave; c0 < used; c0 += FOLD_ADD_LOADS * FOLD_ADD_WAVES) {
-      float v[FOLD_ADD_LOADS];
+      T v[FOLD_ADD_LOADS];
 #pragma unroll
       for (int u = 0; u < FOLD_ADD_LOADS; ++u) {
         const int c = c0 + u * FOLD_ADD_WAVES;
-        v[u] = src[(size_t)min(c, used - 1) * per];
+        v[u] = *(const T*)(src + (size_t)min(c, used - 1) * per);
       }
 #pragma unroll
       for (int u = 0; u < FOLD_ADD_LOADS; ++u)
-        if (c0 + u * FOLD_ADD_WAVES < used) t += v[u];
+        if (c0 + u * FOLD_ADD_WAVES < used) V::add(t, v[u]);
     }
   }
   red[wave][lane] = t;
   __syncthreads();
   if (wave == 0 && e < per) {
-    float u = 0.0f;
+    T u = V::zero();
 #pragma unroll
-    for (int w = 0; w < FOLD_ADD_WAVES; ++w) u += red[w][lane];
+    for (int w = 0; w < FOLD_ADD_WAVES; ++w) V::add(u, red[w][lane]);
     const int part = e / (prefix * FOLD_D);      // 0: dK, 1: dV
     const int rem = e - part * prefix * FOLD_D;  // key * D + d
     const int key = rem / FOLD_D, d = rem - key * FOLD_D;
     if (key < len) {
       const size_t i = ((size_t)(row_base + key) * heads_kv + kvh) * FOLD_D + d;
-      float* acc = part == 0 ? dk_acc : dv_acc;
-      if (dk_out) {
-        const float x = acc[i] + u;
-        if (part == 0) dk_out[i] = (bf16)(x * scale);
-        else dv_out[i] = (bf16)x;
-      } else {
-        acc[i] += u;
-      }
+      T* acc = (T*)((part == 0 ? dk_acc : dv_acc) + i);
+      T x = *acc;
+      V::add(x, u);
+      if (dk_out) V::store_bf16((part == 0 ? dk_out : dv_out) + i, x, part == 0 ? scale : 1.0f);
+      else *acc = x;
     }
   }
 }
@@ -277,15 +297,22 @@ hipError_t launch_prefix_fold_add(const float* fold_part, float* dk_acc, float* 
                                   long long fold_row, hipStream_t stream) {
   if (batch == 0 || seqlen == 0) return hipSuccess;
   if (prefix <= 0 || prefix > 32 || fold_row % 32 != 0) return hipErrorInvalidValue;
-  const int chunks = (2 * prefix * FOLD_D + 63) / 64;
   const long long fold_tiles = fold_row / 32;
   const int num_q_tiles = (seqlen + 31) / 32;
   // no row past the fold row: nothing to add (but rows to convert when direct)
   if (fold_tiles >= num_q_tiles && !dk) return hipSuccess;
   const int ft = (int)(fold_tiles < num_q_tiles ? fold_tiles : num_q_tiles);
-  hipLaunchKernelGGL(sinkattn_prefix_fold_add, dim3(batch, heads_kv, chunks),
-                     dim3(FOLD_ADD_WAVES * 64), 0, stream, fold_part, dk_acc, dv_acc, dk, dv,
-                     scale, cu_seqlens, seqlen, heads_kv, prefix, ds_stride, num_q_tiles, ft);
+  // four values per lane when that still leaves a workgroup per CU or more
+  const int per = 2 * prefix * FOLD_D;
+  if ((long long)batch * heads_kv * ((per + 255) / 256) >= 256) {
+    hipLaunchKernelGGL(sinkattn_prefix_fold_add<4>, dim3(batch, heads_kv, (per + 255) / 256),
+                       dim3(FOLD_ADD_WAVES * 64), 0, stream, fold_part, dk_acc, dv_acc, dk, dv,
+                       scale, cu_seqlens, seqlen, heads_kv, prefix, ds_stride, num_q_tiles, ft);
+  } else {
+    hipLaunchKernelGGL(sinkattn_prefix_fold_add<1>, dim3(batch, heads_kv, (per + 63) / 64),
+                       dim3(FOLD_ADD_WAVES * 64), 0, stream, fold_part, dk_acc, dv_acc, dk, dv,
+                       scale, cu_seqlens, seqlen, heads_kv, prefix, ds_stride, num_q_tiles, ft);
+  }
   return hipGetLastError();
 }
 
