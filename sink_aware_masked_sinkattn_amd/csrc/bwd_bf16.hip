@@ -16,14 +16,19 @@
 // fragments stay in registers; query tiles are BQ rows (128).  The (query
 // tile, query head) pairs that can see those keys -- rows [k0, n) for a
 // prefix key, [k0, k1 + w] otherwise -- form the block's iteration list
-// (tiles from the last down, heads innermost), cut into work units of
-// 2^chunk_shift iterations.  The grid is the exact list of work units (one
-// workgroup each, the extra units of the longest key blocks first), so
-// prefix keys (seen by every later row) and early causal keys do not leave a
-// few workgroups running long after the rest, and no workgroup is launched
-// without work.  A key
-// block covered by one unit stores its fp32 result; a key block cut into
-// several units adds them with one float atomic per element, once per unit.
+// (tiles from the last down, heads innermost; heads outermost for windows of
+// at most two tiles, so neighbouring blocks read a shared tile one iteration
+// apart), cut into work units of 2^chunk_shift iterations.  The grid is the
+// exact list of work units (one workgroup each, the extra units of the
+// longest key blocks first), so prefix keys (seen by every later row) and
+// early causal keys do not leave a few workgroups running long after the
+// rest, and no workgroup is launched without work.  When every key block of
+// the launch is one unit, each writes its rows as bf16 (dK scaled) directly;
+// otherwise a key block covered by one unit stores its fp32 result and a key
+// block cut into several units adds them with one float atomic per element,
+// once per unit, for the finish phase to convert.  With the prefix fold, the
+// first block's query range stops at the fold row: the window dQ kernel
+// takes the prefix keys' part of the rows past it.
 //
 // Per iteration, per wave and 32-row query block, on MFMA 32x32x16 with one
 // key per lane (C layout):
@@ -31,6 +36,8 @@
 //   P' and dS computed in registers are already the A operand (keys on m,
 //   queries on k) of dV += P'^T dO and dK += dS^T Q, whose B operands
 //   (queries on k) are transpose reads of the row-major dO and Q tiles.
+//   In a partial tile a wave skips the 32-row blocks that see none of its
+//   keys.
 // Query tiles (Q, dO, L, D) are double-buffered: registers -> LDS.  Rows
 // past the end of a sequence get L = +inf, so P' = dS = 0 there.
 #include "common.h"

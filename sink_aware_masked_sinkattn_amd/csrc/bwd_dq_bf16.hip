@@ -24,10 +24,13 @@
 //
 // Short windows with GQA groups of a multiple of 4 run a variant that keeps
 // a 32-row block's key tiles resident in LDS for all the group's heads
-// (sinkattn_bwd_dq_bf16_d64_win, below).  Every kernel here also writes the
-// backward's row statistics (D, L) for the dK/dV kernel and its parts of the
-// sink gradient ds_h into per-workgroup slots (no atomics; the finish kernel
-// adds them in a fixed order).
+// (sinkattn_bwd_dq_bf16_d64_win, below), which for 0 < p <= 16 also computes
+// the prefix keys' dK/dV part of its rows past the fold row (the prefix
+// fold).  Every kernel here also writes the backward's row statistics (D, L)
+// for the dK/dV kernel and its parts of the sink gradient ds_h into
+// per-workgroup slots (no atomics; the finish kernel adds them in a fixed
+// order), and clears its rows of the fp32 dK/dV accumulators when the dK/dV
+// launch adds into them.
 #include "common.h"
 #include "mask_tiles.h"
 
