@@ -4,8 +4,9 @@ GPU): every visible (row, key) pair of the mask M[q,k] = 1[k<=q] AND
 block kb, its query range from sa_dkdv_query_range) or, with the prefix fold
 on, by the window dQ kernel (rows at or past the fold row of the first key
 block, keys k < p).  The work-unit count of each block follows from its range.
-The schedule header is compiled with the host compiler; the mask predicate
-here is written out independently of it."""
+And the window dQ kernel's key-tile lists fit the tiles it keeps in LDS.  The
+schedule header is compiled with the host compiler; the mask predicate here
+is written out independently of it."""
 import os
 import shutil
 import subprocess
@@ -77,22 +78,69 @@ int main() {
 """
 
 
+# The resident-tile window dQ kernel holds a 32-row block's whole key-tile
+# list in LDS (6 tiles of 32 keys).  The library runs it when
+# ceil(min(p, T) / 32) + ceil(w / 32) + 1 <= 6 (w, p already clamped to the
+# longest length T); then no block of any sequence of length <= T may list
+# more than 6 tiles.
+WIN_SOURCE = r"""
+#include <cstdio>
+#include "mask_tiles.h"
+
+int main() {
+  const int BK = 32, WIN_TILES = 6;
+  long long checked = 0;
+  for (int T = 1; T <= 700; T += (T < 80 ? 1 : 7))
+    for (int w0 = 0; w0 <= 200; ++w0)
+      for (int p0 = 0; p0 <= 200; p0 += (p0 < 70 ? 1 : 13)) {
+        const int w = w0 < T ? w0 : T, p = p0 < T ? p0 : T;
+        const int pre = (p + BK - 1) / BK, win = (w + BK - 1) / BK + 1;
+        if (pre + win > WIN_TILES) continue;
+        for (int len = 1; len <= T; len += (len < 70 ? 1 : 11))
+          for (int q0 = 0; q0 < len; q0 += BK) {
+            const int q1 = q0 + BK - 1 < len - 1 ? q0 + BK - 1 : len - 1;
+            int seg[4];
+            const int ns = sa_key_tile_segments(q0, q1, w, p, BK, seg);
+            const int nt = (seg[1] - seg[0]) + (ns > 1 ? seg[3] - seg[2] : 0);
+            if (nt > WIN_TILES) {
+              printf("T=%d w=%d p=%d len=%d q0=%d: %d tiles\n", T, w, p, len, q0, nt);
+              return 1;
+            }
+            ++checked;
+          }
+      }
+  printf("ok %lld\n", checked);
+  return 0;
+}
+"""
+
+
+def _build(cxx, d, name, source):
+    src = os.path.join(d, name + ".cpp")
+    exe = os.path.join(d, name)
+    with open(src, "w") as f:
+        f.write(source)
+    subprocess.run([cxx, "-std=c++17", "-O2", "-I", CSRC, src, "-o", exe], check=True)
+    return exe
+
+
 @pytest.fixture(scope="module")
 def cover_binary():
     cxx = shutil.which("g++") or shutil.which("c++")
     if cxx is None:
         pytest.skip("no host C++ compiler")
     d = tempfile.mkdtemp(prefix="dkdv_cover_")
-    src = os.path.join(d, "cover.cpp")
-    exe = os.path.join(d, "cover")
-    with open(src, "w") as f:
-        f.write(SOURCE)
-    subprocess.run([cxx, "-std=c++17", "-O2", "-I", CSRC, src, "-o", exe], check=True)
-    yield exe
+    yield {"cover": _build(cxx, d, "cover", SOURCE), "win": _build(cxx, d, "win", WIN_SOURCE)}
     shutil.rmtree(d, ignore_errors=True)
 
 
 def test_dkdv_ranges_and_fold_cover_every_visible_pair_once(cover_binary):
-    r = subprocess.run([cover_binary], capture_output=True, text=True, timeout=300)
+    r = subprocess.run([cover_binary["cover"]], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.startswith("ok")
+
+
+def test_window_dq_tile_lists_fit_its_resident_tiles(cover_binary):
+    r = subprocess.run([cover_binary["win"]], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.startswith("ok")
