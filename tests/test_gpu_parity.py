@@ -85,6 +85,20 @@ def test_bf16_varlen_small(lengths, w, p):
     compare(run_gpu(inp), run_oracle(inp), "bf16", inp, label=f"varlen{lengths}", scaled=True)
 
 
+@pytest.mark.parametrize("lengths,hq,hkv,w,p", [
+    # GQA group of 16 packed: the window dQ kernel takes four heads per wave
+    # and the prefix fold runs with key blocks split over two dK/dV units
+    ((700, 300, 129, 0, 520), 16, 1, 128, 8),
+    # group of 12: the last round of each wave takes one head
+    ((400, 33, 260), 12, 1, 96, 16),
+])
+def test_bf16_varlen_wide_groups(lengths, hq, hkv, w, p):
+    inp = make_inputs(batch=0, seqlen=0, heads_q=hq, heads_kv=hkv, head_dim=64, window=w, prefix=p,
+                      seed=sum(lengths) + hq, std=0.5, dtype="bf16", lengths=lengths)
+    log(f"varlen {lengths} Hq={hq} Hkv={hkv} w={w} p={p}")
+    compare(run_gpu(inp), run_oracle(inp), "bf16", inp, label=f"varlen{lengths}/{hq}", scaled=True)
+
+
 @pytest.mark.parametrize("sinks", [(float("-inf"), -10.0, 0.0, 10.0)])
 def test_bf16_sink_extremes(sinks):
     inp = make_inputs(batch=1, seqlen=200, heads_q=4, heads_kv=2, head_dim=64, window=30,
