@@ -43,6 +43,8 @@ SMALL = [
     # group of 16: the accumulating path), and p just past the fold's limit
     (1, 700, 16, 1, 128, 8, 0.5),
     (1, 600, 8, 2, 128, 17, 0.5),
+    # many sequences of one length (grid y), window dQ kernel and fold
+    (64, 300, 8, 2, 64, 4, 0.5),
     # windows >= 1024 after clamping run the wide-tile kernels (64-key forward /
     # dQ tiles, 128-row dK/dV tiles); shorter ones the narrow-tile kernels
     (1, 1100, 4, 2, WINDOW_INF, 0, 0.5),
@@ -77,6 +79,9 @@ def test_bf16_small(case):
     ((257,) * 12, 64, 130),
     # the prefix fold with sequences shorter than the prefix and than the fold row
     ((1, 5, 15, 16, 17, 0, 300, 40), 128, 16),
+    # 150 packed sequences: the per-sequence scans of the work lists and the
+    # fold's sum walk more than two 64-sequence steps
+    (tuple((37 * i) % 97 + (260 if i % 10 == 0 else 0) for i in range(150)), 64, 8),
 ])
 def test_bf16_varlen_small(lengths, w, p):
     inp = make_inputs(batch=0, seqlen=0, heads_q=8, heads_kv=2, head_dim=64, window=w, prefix=p,
