@@ -11,8 +11,9 @@ and workspace are preallocated.
 Printed: one JSON line with useful (unmasked) TFLOP/s of the whole step
 (4d FLOP per visible (q, k) pair forward, 10d backward), the fraction of
 the bf16 dense MFMA peak, the roofline of the dominant kernel (timed live
-with HIP events on the library's stream), peak device memory, and the fp64
-oracle timed on a bounded sample on the host cores.
+with HIP events on the library's stream, on every EVENT_STRIDE-th timed
+step), peak device memory, and the fp64 oracle timed on a bounded sample on
+the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --workload decode_grpo_32   (rollout decode: its own JSON line,
